@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for deformable aggregation (ctypes over ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of the benchmark.  The product library never imports,
+links or calls anything here, and this package imports nothing from it.
+
+The arithmetic lives in ``oracle.c``; its header states the definition it
+follows (the Sparse4D deformable_aggregation walkthrough, mhpn.cn/news/1081857,
+sections 3.1, 3.2, 4.1 and 5.1) and the readings taken where the page is
+silent.  This file only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+__all__ = ["build", "forward", "backward", "backward_anchors", "grad_feat_rows"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, i32p, vp = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+        prob = [i64] * 8 + [vp, ctypes.c_int, vp, vp, vp, vp]
+        lib.oracle_forward.argtypes = prob + [vp, i64, vp]
+        lib.oracle_backward.argtypes = prob + [vp, vp, vp, vp]
+        lib.oracle_backward_anchors.argtypes = prob + [vp, vp, i64, vp, vp]
+        lib.oracle_grad_feat_rows.argtypes = prob + [vp, vp, i64, vp]
+        for f in (lib.oracle_forward, lib.oracle_backward, lib.oracle_backward_anchors,
+                  lib.oracle_grad_feat_rows):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _problem(feat, spatial_shape, scale_start_index, loc, weights):
+    """Validate dtypes/contiguity and derive the sizes; returns (args, keepalive, dims)."""
+    spatial_shape = np.ascontiguousarray(spatial_shape, dtype=np.int32)
+    scale_start_index = np.ascontiguousarray(scale_start_index, dtype=np.int32)
+    K, S = scale_start_index.shape
+    if feat.dtype == np.uint16:
+        is_bf16 = 1
+    elif feat.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("feat must be float32 or uint16 bf16 bit patterns")
+    feat = np.ascontiguousarray(feat)
+    loc = np.ascontiguousarray(loc, dtype=np.float32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    bs, num_feat, C = feat.shape
+    A, P = loc.shape[1], loc.shape[2]
+    G = weights.shape[-1]
+    if loc.shape != (bs, A, P, K, 2) or weights.shape != (bs, A, P, K, S, G):
+        raise ValueError("inconsistent shapes")
+    dims = dict(bs=bs, num_feat=num_feat, C=C, A=A, P=P, K=K, S=S, G=G)
+    args = [bs, num_feat, C, A, P, K, S, G, _ptr(feat), is_bf16, _ptr(spatial_shape),
+            _ptr(scale_start_index), _ptr(loc), _ptr(weights)]
+    return args, (feat, spatial_shape, scale_start_index, loc, weights), dims
+
+
+def forward(feat, spatial_shape, scale_start_index, loc, weights,
+            anchor_ids: Optional[Sequence[int]] = None) -> np.ndarray:
+    """out [bs, A, C] (or [len(anchor_ids), C] for flat ids b*A + a), fp64."""
+    args, keep, d = _problem(feat, spatial_shape, scale_start_index, loc, weights)
+    if anchor_ids is None:
+        out = np.empty((d["bs"], d["A"], d["C"]), dtype=np.float64)
+        rc = _load().oracle_forward(*args, None, 0, _ptr(out))
+    else:
+        ids = np.ascontiguousarray(anchor_ids, dtype=np.int64)
+        out = np.empty((ids.size, d["C"]), dtype=np.float64)
+        rc = _load().oracle_forward(*args, _ptr(ids), ids.size, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_forward rejected the problem (rc={rc})")
+    return out
+
+
+def backward(feat, spatial_shape, scale_start_index, loc, weights, grad_out,
+             need_feat: bool = True) -> Tuple[Optional[np.ndarray], np.ndarray, np.ndarray]:
+    """(grad_feat [bs,num_feat,C] or None, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
+    args, keep, d = _problem(feat, spatial_shape, scale_start_index, loc, weights)
+    grad_out = np.ascontiguousarray(grad_out, dtype=np.float32)
+    if grad_out.shape != (d["bs"], d["A"], d["C"]):
+        raise ValueError("grad_out shape")
+    gf = np.empty((d["bs"], d["num_feat"], d["C"]), dtype=np.float64) if need_feat else None
+    gl = np.empty((d["bs"], d["A"], d["P"], d["K"], 2), dtype=np.float64)
+    gw = np.empty((d["bs"], d["A"], d["P"], d["K"], d["S"], d["G"]), dtype=np.float64)
+    rc = _load().oracle_backward(*args, _ptr(grad_out), _ptr(gf), _ptr(gl), _ptr(gw))
+    if rc:
+        raise ValueError(f"oracle_backward rejected the problem (rc={rc})")
+    return gf, gl, gw
+
+
+def backward_anchors(feat, spatial_shape, scale_start_index, loc, weights, grad_out,
+                     anchor_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """grad_loc [n,P,K,2] and grad_weights [n,P,K,S,G] of flat anchors b*A + a."""
+    args, keep, d = _problem(feat, spatial_shape, scale_start_index, loc, weights)
+    grad_out = np.ascontiguousarray(grad_out, dtype=np.float32)
+    ids = np.ascontiguousarray(anchor_ids, dtype=np.int64)
+    gl = np.empty((ids.size, d["P"], d["K"], 2), dtype=np.float64)
+    gw = np.empty((ids.size, d["P"], d["K"], d["S"], d["G"]), dtype=np.float64)
+    rc = _load().oracle_backward_anchors(*args, _ptr(grad_out), _ptr(ids), ids.size,
+                                         _ptr(gl), _ptr(gw))
+    if rc:
+        raise ValueError(f"oracle_backward_anchors rejected the problem (rc={rc})")
+    return gl, gw
+
+
+def grad_feat_rows(feat, spatial_shape, scale_start_index, loc, weights, grad_out,
+                   rows: Sequence[int]) -> np.ndarray:
+    """grad_feat of distinct flat rows b*num_feat + r: [n, C] fp64."""
+    args, keep, d = _problem(feat, spatial_shape, scale_start_index, loc, weights)
+    grad_out = np.ascontiguousarray(grad_out, dtype=np.float32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, d["C"]), dtype=np.float64)
+    rc = _load().oracle_grad_feat_rows(*args, _ptr(grad_out), _ptr(rows), rows.size, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_grad_feat_rows rejected the problem (rc={rc})")
+    return out
+
+
+def run_inputs(inp: Dict[str, np.ndarray], backward_too: bool = True):
+    """Convenience: forward (and backward) of a ``make_inputs`` dict."""
+    keys = ("feat", "spatial_shape", "scale_start_index", "loc", "weights")
+    out = forward(*(inp[k] for k in keys))
+    if not backward_too:
+        return out
+    return (out,) + backward(*(inp[k] for k in keys), inp["grad_out"])
