@@ -1,0 +1,169 @@
+#!/usr/bin/env python3
+"""Benchmark of deformable aggregation on one MI355X.
+
+One step = one pass of the whole hot path on one batch: da_forward then
+da_backward (which zero-fills grad_feat and scatters into it) on the
+nuScenes-shaped workload (bs=1, 6 cameras, 4 scales 64x176 / 32x88 / 16x44 /
+8x22, C=256, G=8, 900 anchors, 13 keypoints), inputs resident in HBM.
+
+Prints ONE JSON line.  value = bilinear sample-channels per second over
+forward + backward (bs*A*P*K*S*C per step / step time).  The roofline
+entries use the algorithmic bytes of each direction (feature rows of the
+four corners, locations, weights, outputs; backward also the feature-gradient
+atomic payload) over the HIP-event time of that call.  cpu_baseline is the
+plain fp64 C oracle, single-threaded, on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def algorithmic_bytes(wl):
+    """Bytes each direction must move ("Byte accounting")."""
+    n_s = wl.num_samples
+    n_pk = wl.bs * wl.anchors * wl.pts * wl.num_cams
+    e = wl.feat_elem_bytes
+    C, G = wl.C, wl.groups
+    b_fwd = 4 * C * e * n_s + 8 * n_pk + 4 * G * n_s + 4 * wl.bs * wl.anchors * C
+    b_bwd = (4 * wl.bs * wl.anchors * C + 4 * C * e * n_s + 16 * C * n_s + 16 * n_pk
+             + 8 * G * n_s)
+    return b_fwd, b_bwd
+
+
+def cpu_baseline(wl, inp, min_seconds=10.0):
+    """Time the fp64 oracle (forward + backward) on the host; single-threaded C."""
+    import oracle
+    args = [inp[k] for k in ("feat", "spatial_shape", "scale_start_index", "loc", "weights")]
+    oracle.forward(*args, anchor_ids=[0])          # load / build outside the timed region
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args)
+        oracle.backward(*args, inp["grad_out"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return dict(value=wl.sample_channels * reps / el, unit="sample-channels/s", cores=1,
+                kind="oracle",
+                sample=f"full {wl.name} workload, forward + backward, {reps} passes in {el:.1f} s "
+                       f"(fp64 C loop, one thread)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="nuscenes_bwd",
+                    help="workload name (nuscenes_bwd is the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the op would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import view_deformable_feature_amd as vdf
+    from view_deformable_feature_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if inp["feat"].dtype == np.uint16:
+        feat = torch.from_numpy(inp["feat"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        feat = torch.from_numpy(inp["feat"]).to(dev)
+    loc = torch.from_numpy(inp["loc"]).to(dev)
+    w = torch.from_numpy(inp["weights"]).to(dev)
+    go = torch.from_numpy(inp["grad_out"]).to(dev)
+    shape, start = inp["spatial_shape"], inp["scale_start_index"]
+    out = torch.empty((wl.bs, wl.anchors, wl.C), device=dev, dtype=torch.float32)
+    gf = torch.empty(tuple(feat.shape), device=dev, dtype=torch.float32)
+    gl = torch.empty(tuple(loc.shape), device=dev, dtype=torch.float32)
+    gw = torch.empty(tuple(w.shape), device=dev, dtype=torch.float32)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        vdf.da_forward(feat, shape, start, loc, w, out=out)
+        if ev is not None:
+            ev[1].record()
+        vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                        grad_weights=gw)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_fwd = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_bwd = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_step = wall / args.steps
+    b_fwd, b_bwd = algorithmic_bytes(wl)
+    sc = wl.sample_channels
+    fwd_s, bwd_s = float(t_fwd.mean()), float(t_bwd.mean())
+    dominant = "backward" if bwd_s >= fwd_s else "forward"
+
+    def roof(bytes_, secs, kernel):
+        a = bytes_ / secs / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                "algorithmic_bytes": int(bytes_), "avg_launch_us": round(secs * 1e6, 2)}
+
+    rec = {
+        "metric": "bilinear sample-channels/s, forward + backward (1 GPU)",
+        "value": sc / t_step,
+        "unit": "sample-channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.feat_dtype == "f32" else "bf16-features/f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: bs={wl.bs}, {wl.num_cams} cameras, scales "
+                               + "/".join(f"{h}x{w_}" for h, w_ in wl.levels)
+                               + f", C={wl.C}, groups={wl.groups}, anchors={wl.anchors}, "
+                                 f"points={wl.pts}",
+                   "sample_channels_per_step": sc},
+        "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
+        "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
+        "roofline": roof(b_bwd, bwd_s, "da_backward (zero fill + scatter kernel)")
+        if dominant == "backward" else roof(b_fwd, fwd_s, "da_forward_kernel"),
+        "roofline_forward": roof(b_fwd, fwd_s, "da_forward_kernel"),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

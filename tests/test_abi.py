@@ -1,0 +1,187 @@
+"""The C-ABI library loads, exports what include/deformagg.h declares, and
+rejects malformed calls on the host before any HIP call (no GPU needed).
+
+Pointers passed here are fake, suitably aligned addresses: every call in
+this file fails a host-side check, so nothing is dereferenced or launched.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+from view_deformable_feature_amd import _lib
+from view_deformable_feature_amd.build import LIB_PATH, build, is_stale
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if is_stale():
+        build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.declared_functions()
+    assert set(names) >= {"da_forward", "da_backward", "da_backward_accumulate",
+                          "da_status_string", "da_last_error", "da_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in deformagg.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.da_version() == 100
+    for code in range(4):
+        assert lib.da_status_string(code)
+    assert b"unknown" in lib.da_status_string(99)
+
+
+FAKE = 0x10000000          # 256-byte aligned fake device address
+HOST_SHAPE = np.array([[[16, 16]]], np.int32)
+HOST_START = np.array([[0]], np.int32)
+
+
+def _prob(**kw):
+    d = dict(bs=1, num_feat=256, num_embeds=32, num_anchors=8, num_pts=4, num_cams=1,
+             num_scale=1, num_groups=1, feat_dtype=0, reserved=0)
+    d.update(kw)
+    return _lib.DAProblem(**d)
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _fwd(lib, prob, feat=FAKE, shape=HOST_SHAPE, start=HOST_START, loc=FAKE, w=FAKE, out=FAKE):
+    vp = ctypes.c_void_p
+    return lib.da_forward(ctypes.byref(prob) if prob is not None else None, vp(feat),
+                          _i32p(shape) if shape is not None else None,
+                          _i32p(start) if start is not None else None,
+                          vp(loc), vp(w), vp(out), None)
+
+
+def _bwd(lib, prob, name="da_backward", feat=FAKE, loc=FAKE, w=FAKE, go=FAKE, gf=FAKE, gl=FAKE,
+         gw=FAKE, shape=HOST_SHAPE, start=HOST_START):
+    vp = ctypes.c_void_p
+    return getattr(lib, name)(ctypes.byref(prob), vp(feat), _i32p(shape), _i32p(start), vp(loc),
+                              vp(w), vp(go), vp(gf), vp(gl), vp(gw), None)
+
+
+def _msg(lib):
+    return lib.da_last_error().decode()
+
+
+@pytest.mark.parametrize("kw, code, needle", [
+    (dict(num_embeds=30, num_groups=4), 1, "multiple of num_groups"),
+    (dict(num_cams=0), 1, ">= 1"),
+    (dict(num_scale=0), 1, ">= 1"),
+    (dict(num_groups=0), 1, ">= 1"),
+    (dict(num_feat=0), 1, ">= 1"),
+    (dict(bs=-1), 1, ">= 0"),
+    (dict(num_anchors=-2), 1, ">= 0"),
+    (dict(num_pts=-1), 1, ">= 0"),
+    (dict(feat_dtype=7), 1, "feat_dtype"),
+    (dict(reserved=1), 1, "reserved"),
+    (dict(num_feat=255), 1, "inside num_feat"),
+    (dict(num_cams=9, num_scale=8), 1, "DA_MAX_LEVELS"),
+])
+def test_forward_rejects_malformed_problem(lib, kw, code, needle):
+    prob = _prob(**kw)
+    shape, start = HOST_SHAPE, HOST_START
+    if prob.num_cams * prob.num_scale > 1 and prob.num_cams * prob.num_scale <= 64:
+        shape = np.tile(HOST_SHAPE, (prob.num_cams, prob.num_scale, 1))
+        start = np.zeros((prob.num_cams, prob.num_scale), np.int32)
+    elif prob.num_cams * prob.num_scale > 64:
+        shape = np.ones((prob.num_cams, prob.num_scale, 2), np.int32)
+        start = np.zeros((prob.num_cams, prob.num_scale), np.int32)
+    assert _fwd(lib, prob, shape=shape, start=start) == code
+    assert needle in _msg(lib)
+
+
+@pytest.mark.parametrize("H, W, st, needle", [
+    (0, 16, 0, "outside [1"),
+    (16, 0, 0, "outside [1"),
+    (40000, 1, 0, "outside [1"),
+    (16, 16, -1, "inside num_feat"),
+    (16, 16, 1, "inside num_feat"),
+])
+def test_rejects_bad_level_table(lib, H, W, st, needle):
+    shape = np.array([[[H, W]]], np.int32)
+    start = np.array([[st]], np.int32)
+    assert _fwd(lib, _prob(num_feat=40000 if H == 40000 else 256), shape=shape, start=start) == 1
+    assert needle in _msg(lib)
+    assert _bwd(lib, _prob(num_feat=40000 if H == 40000 else 256), shape=shape, start=start) == 1
+
+
+def test_rejects_null_pointers(lib):
+    p = _prob()
+    assert lib.da_forward(None, None, None, None, None, None, None, None) == 1
+    assert "problem is NULL" in _msg(lib)
+    assert _fwd(lib, p, shape=None) == 1
+    assert _fwd(lib, p, feat=0) == 1 and "mc_ms_feat" in _msg(lib)
+    assert _fwd(lib, p, loc=0) == 1 and "sampling_location" in _msg(lib)
+    assert _fwd(lib, p, w=0) == 1
+    assert _fwd(lib, p, out=0) == 1 and "out is NULL" in _msg(lib)
+    for kw, needle in ((dict(go=0), "grad_out"), (dict(gf=0), "grad_feat"),
+                       (dict(gl=0), "grad_loc"), (dict(gw=0), "grad_loc / grad_weights")):
+        for name in ("da_backward", "da_backward_accumulate"):
+            assert _bwd(lib, p, name, **kw) == 1
+            assert needle in _msg(lib)
+
+
+def test_rejects_misaligned_pointers(lib):
+    p = _prob()
+    assert _fwd(lib, p, feat=FAKE + 2) == 1 and "element aligned" in _msg(lib)
+    assert _fwd(lib, p, loc=FAKE + 4) == 1 and "8-byte" in _msg(lib)
+    assert _fwd(lib, p, w=FAKE + 1) == 1
+    assert _fwd(lib, p, out=FAKE + 2) == 1
+    assert _bwd(lib, p, gl=FAKE + 4) == 1 and "grad_loc" in _msg(lib)
+    assert _bwd(lib, p, gf=FAKE + 1) == 1
+    # bf16 features need 2-byte alignment only
+    pb = _prob(feat_dtype=1)
+    assert _fwd(lib, pb, feat=FAKE + 1) == 1
+
+
+def test_rejects_unsupported_sizes(lib):
+    # a batch image beyond the 32-bit buffer range
+    n = (1 << 32) // (256 * 4)
+    shape = np.array([[[n // 8, 8]]], np.int32)
+    p = _prob(num_feat=n, num_embeds=256, num_groups=8)
+    assert _fwd(lib, p, shape=np.array([[[16, 16]]], np.int32)) == 2
+    assert "4 GiB" in _msg(lib)
+    # backward: too many channels per lane (C / pow2-part-of-group-width > 16)
+    p = _prob(num_embeds=192, num_groups=8)
+    assert _bwd(lib, p) == 2 and "exceeds 16" in _msg(lib)
+    # too many channels
+    p = _prob(num_embeds=(1 << 20) + 8, num_groups=1)
+    assert _fwd(lib, p) == 2
+    # LDS: one (point, camera) pair with a huge S * G does not fit
+    p = _prob(num_embeds=4096, num_groups=4096, num_scale=64)
+    shape = np.tile(HOST_SHAPE, (1, 64, 1))
+    start = np.zeros((1, 64), np.int32)
+    assert _fwd(lib, p, shape=shape, start=start) == 2 and "LDS" in _msg(lib)
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    assert _fwd(lib, _prob(num_embeds=30, num_groups=4)) == 1
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.da_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "multiple" in _msg(lib)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import view_deformable_feature_amd as vdf
+    wl_shape = np.array([[[4, 4]]], np.int32)
+    feat = torch.zeros(1, 16, 4)
+    loc = torch.zeros(1, 1, 1, 1, 2)
+    w = torch.zeros(1, 1, 1, 1, 1, 1)
+    with pytest.raises(ValueError, match="no CPU path"):
+        vdf.da_forward(feat, wl_shape, np.zeros((1, 1), np.int32), loc, w)

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and medium workloads are compared on every output element; the
+full-size large workloads on sampled anchors / feature rows that the oracle
+computes one by one, plus identities that hold at any size.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (KEYS, TOL_BF16, TOL_BWD, TOL_FWD, assert_close, gpu_backward,
+                         gpu_forward, say, to_device)
+from view_deformable_feature_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _args(inp):
+    return [inp[k] for k in KEYS]
+
+
+def _full_check(inp, tol_f, tol_b, label):
+    say(f"[parity] {label}: upload")
+    dev = to_device(inp)
+    say(f"[parity] {label}: forward")
+    out = gpu_forward(dev).cpu().numpy()
+    say(f"[parity] {label}: backward")
+    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev))
+    say(f"[parity] {label}: oracle")
+    r_out = oracle.forward(*_args(inp))
+    r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
+    e = [assert_close(f"{label} out", out, r_out, tol_f),
+         assert_close(f"{label} grad_feat", gf, r_gf, tol_b),
+         assert_close(f"{label} grad_loc", gl, r_gl, tol_b),
+         assert_close(f"{label} grad_weights", gw, r_gw, tol_b)]
+    say(f"[parity] {label}: max err out {e[0]:.2e} gf {e[1]:.2e} gl {e[2]:.2e} gw {e[3]:.2e}")
+    return dev, out
+
+
+# ---------------------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------------------
+
+def test_tiny_full():
+    inp = W.make_inputs(W.WORKLOADS["tiny"])
+    _full_check(inp, TOL_FWD, TOL_BWD, "tiny")
+
+
+def test_nuscenes_forward_full():
+    inp = W.make_inputs(W.WORKLOADS["nuscenes_fwd"], with_grad_out=False)
+    dev = to_device(inp)
+    say("[parity] nuscenes_fwd: forward")
+    out = gpu_forward(dev).cpu().numpy()
+    ref = oracle.forward(*_args(inp))
+    say(f"[parity] nuscenes_fwd max err {assert_close('nuscenes out', out, ref, TOL_FWD):.2e}")
+    out2 = gpu_forward(dev).cpu().numpy()
+    assert np.array_equal(out, out2), "forward is not deterministic"
+
+
+def test_nuscenes_backward_full():
+    inp = W.make_inputs(W.WORKLOADS["nuscenes_bwd"])
+    dev = to_device(inp)
+    say("[parity] nuscenes_bwd: backward x2")
+    r1 = [t.cpu().numpy() for t in gpu_backward(dev)]
+    r2 = [t.cpu().numpy() for t in gpu_backward(dev)]
+    ref = oracle.backward(*_args(inp), inp["grad_out"])
+    for run, r in (("run1", r1), ("run2", r2)):
+        for name, g, rr in zip(("grad_feat", "grad_loc", "grad_weights"), r, ref):
+            assert_close(f"nuscenes {run} {name}", g, rr, TOL_BWD)
+    # only the atomically accumulated feature gradient may differ between runs
+    assert np.array_equal(r1[1], r2[1]) and np.array_equal(r1[2], r2[2])
+    say(f"[parity] nuscenes_bwd run-to-run max |d grad_feat| = "
+        f"{np.abs(r1[0] - r2[0]).max():.3e}")
+
+
+def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0):
+    say(f"[parity] {wl.name}: generate")
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    say(f"[parity] {wl.name}: forward + backward")
+    out = gpu_forward(dev)
+    gf, gl, gw = gpu_backward(dev)
+    rng = np.random.default_rng(seed)
+    ids = rng.choice(wl.bs * wl.anchors, size=n_anchor, replace=False)
+    ids.sort()
+    say(f"[parity] {wl.name}: oracle on {n_anchor} anchors")
+    out_h = out.cpu().numpy().reshape(-1, wl.C)
+    assert_close(f"{wl.name} out", out_h[ids], oracle.forward(*_args(inp), anchor_ids=ids), tol_f)
+    r_gl, r_gw = oracle.backward_anchors(*_args(inp), inp["grad_out"], ids)
+    assert_close(f"{wl.name} grad_loc", gl.cpu().numpy().reshape(-1, *gl.shape[2:])[ids], r_gl, tol_b)
+    assert_close(f"{wl.name} grad_weights", gw.cpu().numpy().reshape(-1, *gw.shape[2:])[ids], r_gw,
+                 tol_b)
+    # feature-gradient rows: mostly rows the GPU touched, plus random ones
+    gf_flat = gf.view(-1, wl.C)
+    touched = torch.nonzero(gf_flat.abs().sum(1) > 0).flatten().cpu().numpy()
+    rows = np.unique(np.concatenate([rng.choice(touched, size=min(n_rows, touched.size), replace=False),
+                                     rng.integers(0, gf_flat.shape[0], size=n_rows // 4)]))
+    say(f"[parity] {wl.name}: oracle on {rows.size} grad_feat rows")
+    r_gf = oracle.grad_feat_rows(*_args(inp), inp["grad_out"], rows)
+    idx = torch.from_numpy(rows).to(gf.device)
+    assert_close(f"{wl.name} grad_feat rows", gf_flat[idx].cpu().numpy(), r_gf, tol_b)
+    # identities at full size: <grad_out, out> = <grad_feat, feat> = <grad_weights, weights>
+    go = dev["grad_out"].double()
+    s_out = float((go * out.double()).sum())
+    s_feat = float((gf.double() * dev["feat"].double()).sum())
+    s_w = float((gw.double() * dev["weights"].double()).sum())
+    scale = float((go.abs() * out.double().abs()).sum())
+    assert abs(s_feat - s_out) <= 1e-4 * scale, (s_feat, s_out)
+    assert abs(s_w - s_out) <= 1e-4 * scale, (s_w, s_out)
+    say(f"[parity] {wl.name}: ok ({touched.size} touched rows)")
+
+
+def test_large_sampled():
+    _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD)
+
+
+def test_large_bf16_sampled():
+    _sampled_check(W.WORKLOADS["large_bf16"], TOL_BF16, TOL_BF16)
+
+
+# ---------------------------------------------------------------------------------------
+# ragged shapes, several tiles, edge cases
+# ---------------------------------------------------------------------------------------
+
+RAGGED = [
+    # (name, kwargs) -- channel counts that exercise each lane layout
+    ("c96_g3", dict(bs=2, num_cams=3, levels=((13, 29), (7, 15), (3, 8)), C=96, groups=3,
+                    anchors=37, pts=5, loc_lo=-0.1, loc_hi=1.1)),
+    ("c48_g6", dict(bs=1, num_cams=2, levels=((11, 17), (6, 9)), C=48, groups=6, anchors=29,
+                    pts=7, loc_lo=-0.2, loc_hi=1.2)),
+    ("c2_g2", dict(bs=2, num_cams=1, levels=((5, 7),), C=2, groups=2, anchors=65, pts=3,
+                   loc_lo=-0.2, loc_hi=1.2, weight_kind="uniform01")),
+    ("c1_g1", dict(bs=1, num_cams=2, levels=((4, 6), (2, 3)), C=1, groups=1, anchors=130,
+                   pts=2, loc_lo=-0.3, loc_hi=1.3)),
+    ("c6_g3", dict(bs=1, num_cams=1, levels=((9, 9),), C=6, groups=3, anchors=40, pts=4,
+                   loc_lo=-0.1, loc_hi=1.1)),
+    ("c512_g8", dict(bs=1, num_cams=2, levels=((16, 40), (8, 20)), C=512, groups=8, anchors=21,
+                     pts=6, loc_lo=-0.05, loc_hi=1.05)),
+    ("c1024_g8", dict(bs=1, num_cams=1, levels=((8, 12),), C=1024, groups=8, anchors=9, pts=3,
+                      loc_lo=-0.05, loc_hi=1.05)),
+    ("c256_g8_many_pts", dict(bs=1, num_cams=6, levels=((12, 30), (6, 15)), C=256, groups=8,
+                              anchors=5, pts=97, loc_lo=-0.05, loc_hi=1.05)),
+    ("c32_g1_64_levels", dict(bs=1, num_cams=8, levels=tuple((2 + i, 3 + 2 * i) for i in range(8)),
+                              C=32, groups=1, anchors=11, pts=3, loc_lo=-0.1, loc_hi=1.1)),
+    ("c64_g64", dict(bs=1, num_cams=1, levels=((6, 6),), C=64, groups=64, anchors=12, pts=3,
+                     loc_lo=-0.1, loc_hi=1.1)),
+    ("clustered", dict(bs=2, num_cams=3, levels=((20, 50), (10, 25)), C=128, groups=4,
+                       anchors=33, pts=13, loc_kind="clustered", loc_sigma=0.01)),
+]
+
+
+@pytest.mark.parametrize("name, kw", RAGGED, ids=[r[0] for r in RAGGED])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_full(name, kw, dtype):
+    wl = W.custom(f"{name}_{dtype}", feat_dtype=dtype, seed=zlib.crc32(name.encode()) % 1000, **kw)
+    inp = W.make_inputs(wl)
+    tol_f, tol_b = (TOL_BF16, TOL_BF16) if dtype == "bf16" else (TOL_FWD, TOL_BWD)
+    _full_check(inp, tol_f, tol_b, wl.name)
+
+
+def test_per_camera_pyramids_and_permuted_level_order():
+    """Cameras with different pyramids, levels stored scale-major in reverse order."""
+    wl = W.custom("percam", bs=2, num_cams=3, levels=((9, 14), (5, 7)),
+                  cam_levels=(((9, 14), (5, 7)), ((12, 10), (6, 5)), ((7, 21), (4, 11))),
+                  C=64, groups=4, anchors=23, pts=6, loc_lo=-0.1, loc_hi=1.1, seed=77)
+    inp = W.make_inputs(wl)
+    shape, start = inp["spatial_shape"], inp["scale_start_index"]
+    order = [(k, s) for s in reversed(range(wl.num_scale)) for k in reversed(range(wl.num_cams))]
+    feat = inp["feat"]
+    new_feat = np.empty_like(feat)
+    new_start = np.zeros_like(start)
+    row = 0
+    for k, s in order:
+        n = int(shape[k, s, 0] * shape[k, s, 1])
+        new_feat[:, row:row + n] = feat[:, start[k, s]:start[k, s] + n]
+        new_start[k, s] = row
+        row += n
+    inp2 = dict(inp, feat=new_feat, scale_start_index=new_start)
+    _full_check(inp2, TOL_FWD, TOL_BWD, "permuted")
+
+
+def test_golden_fixtures_on_gpu():
+    from golden_fixtures import fixture_paths, load
+    for path in fixture_paths():
+        d, inp, exp = load(path)
+        dev = to_device(inp)
+        out = gpu_forward(dev).cpu().numpy()
+        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev))
+        assert_close("golden out", out, exp["out"], TOL_FWD)
+        assert_close("golden grad_feat", gf, exp["grad_feat"], TOL_BWD)
+        assert_close("golden grad_loc", gl, exp["grad_loc"], TOL_BWD)
+        assert_close("golden grad_weights", gw, exp["grad_weights"], TOL_BWD)
+
+
+def test_exact_texels_bit_exact():
+    """Pixel-centre locations with one-hot weights return the stored texel exactly."""
+    wl = W.WORKLOADS["tiny"]
+    inp = W.make_inputs(wl)
+    rng = np.random.default_rng(3)
+    ij = rng.integers(0, 16, size=(wl.anchors, wl.pts, 2))
+    loc = np.empty((1, wl.anchors, wl.pts, 1, 2), np.float32)
+    loc[0, :, :, 0, 0] = (ij[..., 1] + 0.5) / 16
+    loc[0, :, :, 0, 1] = (ij[..., 0] + 0.5) / 16
+    w = np.zeros_like(inp["weights"])
+    w[0, :, 1] = 1.0
+    dev = to_device(dict(inp, loc=loc, weights=w))
+    out = gpu_forward(dev).cpu().numpy()
+    for a in range(wl.anchors):
+        i, j = ij[a, 1]
+        assert np.array_equal(out[0, a], inp["feat"][0, i * 16 + j])
+
+
+def test_no_points_and_empty_batches():
+    wl = W.custom("nopts", bs=2, num_cams=2, levels=((4, 5),), C=32, groups=4, anchors=3, pts=0,
+                  weight_kind="uniform01")
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    out = gpu_forward(dev)
+    assert out.shape == (2, 3, 32) and torch.count_nonzero(out) == 0
+    gf = torch.full(tuple(dev["feat"].shape), 7.0, device="cuda")
+    import view_deformable_feature_amd as vdf
+    gf, gl, gw = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
+                                 dev["loc"], dev["weights"], dev["grad_out"], grad_feat=gf)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gf) == 0 and gl.numel() == 0 and gw.numel() == 0
+    for kw in (dict(anchors=0, pts=4), dict(bs=0, anchors=3, pts=4)):
+        wl = W.custom("empty", num_cams=2, levels=((4, 5),), C=32, groups=4,
+                      **dict(dict(bs=1), **kw))
+        inp = W.make_inputs(wl)
+        dev = to_device(inp)
+        out = gpu_forward(dev)
+        gf, gl, gw = gpu_backward(dev)
+        assert out.numel() == 0 and gl.numel() == 0 and gw.numel() == 0
+        assert torch.count_nonzero(gf) == 0
+
+
+def test_nan_and_far_locations_contribute_nothing():
+    wl = W.custom("nanloc", bs=1, num_cams=2, levels=((8, 8), (4, 4)), C=32, groups=2,
+                  anchors=10, pts=4, loc_lo=-0.1, loc_hi=1.1, seed=5)
+    inp = W.make_inputs(wl)
+    loc = inp["loc"].copy()
+    loc[0, :, 0, :, 0] = np.nan
+    loc[0, :, 1, :, 1] = np.inf
+    loc[0, :, 2, :, :] = -3e38
+    inp["loc"] = loc
+    _full_check(inp, TOL_FWD, TOL_BWD, "nanloc")
+
+
+def test_max_extent_levels():
+    """Levels at DA_MAX_EXTENT along one axis."""
+    wl = W.custom("maxext", bs=1, num_cams=1, levels=((32768, 1),), C=8, groups=2,
+                  anchors=40, pts=8, loc_lo=-0.05, loc_hi=1.05, seed=9,
+                  cam_levels=None)
+    inp = W.make_inputs(wl)
+    _full_check(inp, TOL_FWD, TOL_BWD, "maxext_h")
+    wl = W.custom("maxext_w", bs=1, num_cams=1, levels=((1, 32768),), C=8, groups=2,
+                  anchors=40, pts=8, loc_lo=-0.05, loc_hi=1.05, seed=10)
+    _full_check(W.make_inputs(wl), TOL_FWD, TOL_BWD, "maxext_w")
+
+
+def test_accumulate_adds_into_existing_gradient():
+    inp = W.make_inputs(W.custom("acc", bs=1, num_cams=2, levels=((10, 12), (5, 6)), C=64,
+                                 groups=4, anchors=17, pts=5, loc_lo=-0.1, loc_hi=1.1, seed=12))
+    dev = to_device(inp)
+    base = torch.randn(tuple(dev["feat"].shape), device="cuda", generator=None)
+    gf0, gl0, gw0 = gpu_backward(dev)
+    gf1, gl1, gw1 = gpu_backward(dev, accumulate_into=base.clone())
+    assert_close("accumulate", gf1.cpu().numpy(), (base + gf0).cpu().numpy(), 1e-6)
+    assert torch.equal(gl0, gl1) and torch.equal(gw0, gw1)
+
+
+def test_autograd_function_and_side_stream():
+    import view_deformable_feature_amd as vdf
+    inp = W.make_inputs(W.custom("ag", bs=2, num_cams=2, levels=((9, 11), (5, 6)), C=64,
+                                 groups=8, anchors=14, pts=4, loc_lo=-0.1, loc_hi=1.1, seed=21))
+    dev = to_device(inp)
+    feat = dev["feat"].clone().requires_grad_(True)
+    loc = dev["loc"].clone().requires_grad_(True)
+    w = dev["weights"].clone().requires_grad_(True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = vdf.DeformableAggregationFunction.apply(feat, inp["spatial_shape"],
+                                                      torch.from_numpy(inp["scale_start_index"]),
+                                                      loc, w)
+        out.backward(dev["grad_out"])
+    torch.cuda.synchronize()
+    r_out = oracle.forward(*_args(inp))
+    r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
+    assert_close("autograd out", out.detach().cpu().numpy(), r_out, TOL_FWD)
+    assert_close("autograd grad_feat", feat.grad.cpu().numpy(), r_gf, TOL_BWD)
+    assert_close("autograd grad_loc", loc.grad.cpu().numpy(), r_gl, TOL_BWD)
+    assert_close("autograd grad_weights", w.grad.cpu().numpy(), r_gw, TOL_BWD)
+
+
+def test_errors_surface_as_exceptions():
+    import view_deformable_feature_amd as vdf
+    from view_deformable_feature_amd._lib import DAError
+    inp = W.make_inputs(W.WORKLOADS["tiny"])
+    dev = to_device(inp)
+    bad_start = np.array([[5]], np.int32)
+    with pytest.raises(DAError, match="inside num_feat"):
+        vdf.da_forward(dev["feat"], dev["spatial_shape"], bad_start, dev["loc"], dev["weights"])

@@ -1,0 +1,10 @@
+"""Sparse4D-style deformable aggregation for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libdeformagg.so`` (HIP kernels behind a C ABI,
+declared in ``include/deformagg.h``); ``api`` binds it to PyTorch tensors.
+``workloads`` draws seeded synthetic inputs.
+"""
+from .api import (DeformableAggregationFunction, da_backward, da_backward_accumulate,  # noqa: F401
+                  da_forward, deformable_aggregation)
+
+__version__ = "1.0.0"

@@ -1,0 +1,84 @@
+"""ctypes declarations of the libdeformagg C ABI (include/deformagg.h).
+
+Only marshalling lives here.  Loading fails loudly when the library has not
+been built: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "deformagg.h")
+
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
+DA_F32, DA_BF16 = 0, 1
+
+
+class DAProblem(ctypes.Structure):
+    _fields_ = [
+        ("bs", ctypes.c_int64),
+        ("num_feat", ctypes.c_int64),
+        ("num_embeds", ctypes.c_int64),
+        ("num_anchors", ctypes.c_int64),
+        ("num_pts", ctypes.c_int64),
+        ("num_cams", ctypes.c_int64),
+        ("num_scale", ctypes.c_int64),
+        ("num_groups", ctypes.c_int64),
+        ("feat_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class DAError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed with status {status}: {detail}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdeformagg.so; raises if it is missing (build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m view_deformable_feature_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    prob = ctypes.POINTER(DAProblem)
+    lib.da_forward.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp]
+    lib.da_forward.restype = ctypes.c_int
+    for name in ("da_backward", "da_backward_accumulate"):
+        f = getattr(lib, name)
+        f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp]
+        f.restype = ctypes.c_int
+    lib.da_status_string.argtypes = [ctypes.c_int]
+    lib.da_status_string.restype = ctypes.c_char_p
+    lib.da_last_error.argtypes = []
+    lib.da_last_error.restype = ctypes.c_char_p
+    lib.da_version.argtypes = []
+    lib.da_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def check(status: int, func: str) -> None:
+    if status != DA_OK:
+        lib = load()
+        raise DAError(status, func, lib.da_last_error().decode(errors="replace"))
+
+
+def declared_functions() -> List[str]:
+    """Names of the functions include/deformagg.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(da_[a-z_]+)\s*\(", text)

@@ -1,0 +1,192 @@
+"""PyTorch-facing binding of libdeformagg.
+
+Same names as the C ABI (``da_forward``, ``da_backward``,
+``da_backward_accumulate``) plus the autograd wrapper
+``DeformableAggregationFunction`` whose ``forward(ctx, mc_ms_feat,
+spatial_shape, scale_start_index, sampling_location, weights)`` follows the
+signature shown in section 6 of the Sparse4D deformable_aggregation
+walkthrough (mhpn.cn/news/1081857).
+
+This module only checks tensor metadata and passes pointers: every step of
+the computation runs in the HIP kernels of libdeformagg.  torch supplies
+device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+from . import _lib
+
+__all__ = ["da_forward", "da_backward", "da_backward_accumulate",
+           "DeformableAggregationFunction", "deformable_aggregation", "problem_of"]
+
+IntTable = Union[torch.Tensor, np.ndarray, Sequence]
+
+
+def _host_i32(x: IntTable) -> np.ndarray:
+    """Level tables are read on the host; a device tensor is copied (synchronising)."""
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
+               sampling_location: torch.Tensor, weights: torch.Tensor) -> _lib.DAProblem:
+    if mc_ms_feat.dim() != 3:
+        raise ValueError("mc_ms_feat must be [bs, num_feat, C]")
+    if sampling_location.dim() != 5 or sampling_location.shape[-1] != 2:
+        raise ValueError("sampling_location must be [bs, A, P, K, 2]")
+    if weights.dim() != 6:
+        raise ValueError("weights must be [bs, A, P, K, S, G]")
+    if spatial_shape.ndim != 3 or spatial_shape.shape[-1] != 2:
+        raise ValueError("spatial_shape must be [num_cams, num_scale, 2]")
+    bs, num_feat, C = mc_ms_feat.shape
+    _, A, P, K, _ = sampling_location.shape
+    S, G = weights.shape[4], weights.shape[5]
+    if spatial_shape.shape[:2] != (K, S):
+        raise ValueError(f"spatial_shape is {spatial_shape.shape}, expected ({K}, {S}, 2)")
+    dt = _lib.DA_BF16 if mc_ms_feat.dtype == torch.bfloat16 else _lib.DA_F32
+    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt, 0)
+
+
+def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights):
+    shape = _host_i32(spatial_shape)
+    start = _host_i32(scale_start_index)
+    dev = mc_ms_feat.device
+    _need(mc_ms_feat, "mc_ms_feat", (torch.float32, torch.bfloat16), dev)
+    _need(sampling_location, "sampling_location", torch.float32, dev)
+    _need(weights, "weights", torch.float32, dev)
+    prob = problem_of(mc_ms_feat, shape, sampling_location, weights)
+    bs, A, P, K = (sampling_location.shape[i] for i in range(4))
+    if tuple(weights.shape[:4]) != (bs, A, P, K) or mc_ms_feat.shape[0] != bs:
+        raise ValueError("batch / anchor / point / camera sizes disagree between inputs")
+    if start.shape != shape.shape[:2]:
+        raise ValueError(f"scale_start_index is {start.shape}, expected {shape.shape[:2]}")
+    return prob, shape, start
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def da_forward(mc_ms_feat: torch.Tensor, spatial_shape: IntTable, scale_start_index: IntTable,
+               sampling_location: torch.Tensor, weights: torch.Tensor,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[bs, A, C] (float32) on the current stream of mc_ms_feat's device."""
+    lib = _lib.load()
+    prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
+                                  sampling_location, weights)
+    dev = mc_ms_feat.device
+    if out is None:
+        out = torch.empty((prob.bs, prob.num_anchors, prob.num_embeds), device=dev,
+                          dtype=torch.float32)
+    _need(out, "out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
+    with torch.cuda.device(dev):
+        st = lib.da_forward(ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
+                            _ptr(sampling_location), _ptr(weights), _ptr(out), _stream(dev))
+    _lib.check(st, "da_forward")
+    return out
+
+
+def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
+              weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None):
+    lib = _lib.load()
+    prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
+                                  sampling_location, weights)
+    dev = mc_ms_feat.device
+    _need(grad_out, "grad_out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
+    if grad_feat is None:
+        if func == "da_backward_accumulate":
+            raise ValueError("da_backward_accumulate needs an existing grad_feat")
+        grad_feat = torch.empty(tuple(mc_ms_feat.shape), device=dev, dtype=torch.float32)
+    if grad_loc is None:
+        grad_loc = torch.empty(tuple(sampling_location.shape), device=dev, dtype=torch.float32)
+    if grad_weights is None:
+        grad_weights = torch.empty(tuple(weights.shape), device=dev, dtype=torch.float32)
+    _need(grad_feat, "grad_feat", torch.float32, dev, tuple(mc_ms_feat.shape))
+    _need(grad_loc, "grad_loc", torch.float32, dev, tuple(sampling_location.shape))
+    _need(grad_weights, "grad_weights", torch.float32, dev, tuple(weights.shape))
+    with torch.cuda.device(dev):
+        st = getattr(lib, func)(ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
+                                _ptr(sampling_location), _ptr(weights), _ptr(grad_out),
+                                _ptr(grad_feat), _ptr(grad_loc), _ptr(grad_weights), _stream(dev))
+    _lib.check(st, func)
+    return grad_feat, grad_loc, grad_weights
+
+
+def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
+                grad_out, grad_feat=None, grad_loc=None, grad_weights=None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
+    return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
+                     sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights)
+
+
+def da_backward_accumulate(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
+                           weights, grad_out, grad_feat, grad_loc=None, grad_weights=None):
+    """As da_backward, adding the feature gradient into the existing ``grad_feat``."""
+    return _backward("da_backward_accumulate", mc_ms_feat, spatial_shape, scale_start_index,
+                     sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights)
+
+
+class DeformableAggregationFunction(torch.autograd.Function):
+    """Autograd wrapper: gradients for mc_ms_feat, sampling_location and weights.
+
+    The feature gradient is float32 (for bf16 features it is cast back to bf16
+    for autograd; use ``da_backward`` directly to keep the float32 values).
+    """
+
+    @staticmethod
+    def forward(ctx, mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights):
+        shape = _host_i32(spatial_shape)
+        start = _host_i32(scale_start_index)
+        mc_ms_feat = mc_ms_feat.contiguous()
+        sampling_location = sampling_location.contiguous().float()
+        weights = weights.contiguous().float()
+        out = da_forward(mc_ms_feat, shape, start, sampling_location, weights)
+        ctx.save_for_backward(mc_ms_feat, sampling_location, weights)
+        ctx.tables = (shape, start)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        mc_ms_feat, sampling_location, weights = ctx.saved_tensors
+        shape, start = ctx.tables
+        gf, gl, gw = da_backward(mc_ms_feat, shape, start, sampling_location, weights,
+                                 grad_out.contiguous().float())
+        if mc_ms_feat.dtype != torch.float32:
+            gf = gf.to(mc_ms_feat.dtype)
+        return gf, None, None, gl, gw
+
+
+def deformable_aggregation(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
+                           weights):
+    return DeformableAggregationFunction.apply(mc_ms_feat, spatial_shape, scale_start_index,
+                                               sampling_location, weights)

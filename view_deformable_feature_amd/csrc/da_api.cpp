@@ -1,0 +1,308 @@
+// libdeformagg host side: argument checks, launch-shape selection, dispatch.
+//
+// Every check runs before anything is enqueued, so a failing call leaves all
+// outputs untouched and needs no GPU.  See include/deformagg.h for the
+// contract of each entry point.
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "da_internal.h"
+#include "deformagg.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+da_status fail(da_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t pow2_factor(int64_t x) { return x & -x; }   // largest power of two dividing x (x > 0)
+
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << (r + 1)) <= x) ++r;
+    return r;
+}
+
+int next_pow2(int64_t x) {
+    int r = 1;
+    while (r < x) r <<= 1;
+    return r;
+}
+
+constexpr uint64_t kU32Max = 0xffffffffull;
+
+struct Plan {
+    da::KArgs ka;
+    da::LaunchShape shape;
+    int64_t n_anchors;   // bs * A
+    bool bf16;
+};
+
+// Checks shared by both directions: problem sizes, the level table, the input
+// pointers.  Fills ka with everything but the output pointers and the layout.
+da_status check_common(const da_problem* p, const void* feat, const int32_t* shape,
+                       const int32_t* start, const float* loc, const float* weights,
+                       Plan& plan) {
+    if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->reserved != 0) return fail(DA_ERR_INVALID_ARG, "problem.reserved must be 0");
+    if (p->bs < 0 || p->num_anchors < 0 || p->num_pts < 0)
+        return fail(DA_ERR_INVALID_ARG, "bs, num_anchors and num_pts must be >= 0");
+    if (p->num_feat < 1 || p->num_embeds < 1 || p->num_cams < 1 || p->num_scale < 1 ||
+        p->num_groups < 1)
+        return fail(DA_ERR_INVALID_ARG,
+                    "num_feat, num_embeds, num_cams, num_scale and num_groups must be >= 1");
+    if (p->num_cams > DA_MAX_LEVELS || p->num_scale > DA_MAX_LEVELS ||
+        p->num_cams * p->num_scale > DA_MAX_LEVELS)
+        return fail(DA_ERR_INVALID_ARG, "num_cams * num_scale = %lld exceeds DA_MAX_LEVELS (%d)",
+                    (long long)(p->num_cams * p->num_scale), DA_MAX_LEVELS);
+    if (p->num_embeds % p->num_groups != 0)
+        return fail(DA_ERR_INVALID_ARG, "num_embeds (%lld) is not a multiple of num_groups (%lld)",
+                    (long long)p->num_embeds, (long long)p->num_groups);
+    if (p->feat_dtype != DA_F32 && p->feat_dtype != DA_BF16)
+        return fail(DA_ERR_INVALID_ARG, "feat_dtype %d is neither DA_F32 nor DA_BF16",
+                    (int)p->feat_dtype);
+    if (!shape || !start) return fail(DA_ERR_INVALID_ARG, "spatial_shape / scale_start_index is NULL");
+    // sizes that must fit the kernels' 32-bit index arithmetic
+    if (p->num_embeds > (1 << 20)) return fail(DA_ERR_UNSUPPORTED, "num_embeds > 2^20");
+    if (p->num_anchors > INT32_MAX || p->num_pts > INT32_MAX ||
+        p->num_pts * p->num_cams > INT32_MAX / 64)
+        return fail(DA_ERR_UNSUPPORTED, "num_anchors or num_pts * num_cams too large");
+
+    const int elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    const int64_t C = p->num_embeds;
+    const int64_t nlev = p->num_cams * p->num_scale;
+    da::KArgs& ka = plan.ka;
+    memset(&ka, 0, sizeof ka);
+    for (int64_t l = 0; l < nlev; ++l) {
+        const int64_t H = shape[2 * l], W = shape[2 * l + 1], st = start[l];
+        if (H < 1 || W < 1 || H > DA_MAX_EXTENT || W > DA_MAX_EXTENT)
+            return fail(DA_ERR_INVALID_ARG, "level %lld: (H, W) = (%lld, %lld) outside [1, %d]",
+                        (long long)l, (long long)H, (long long)W, DA_MAX_EXTENT);
+        if (st < 0 || st + H * W > p->num_feat)
+            return fail(DA_ERR_INVALID_ARG,
+                        "level %lld: rows [%lld, %lld) do not lie inside num_feat = %lld",
+                        (long long)l, (long long)st, (long long)(st + H * W),
+                        (long long)p->num_feat);
+        ka.lv.H[l] = (int32_t)H;
+        ka.lv.W[l] = (int32_t)W;
+        ka.lv.start[l] = (int32_t)st;
+    }
+    // one batch image is addressed by a 32-bit buffer offset, with one row of
+    // headroom for the "outside" offset plus a lane offset
+    const uint64_t feat_img = (uint64_t)p->num_feat * (uint64_t)C * (uint64_t)elem;
+    if (feat_img + 2 * (uint64_t)C * elem > kU32Max)
+        return fail(DA_ERR_UNSUPPORTED, "one batch image of mc_ms_feat (%llu bytes) exceeds 4 GiB",
+                    (unsigned long long)feat_img);
+
+    const int64_t n_anchor = p->bs * p->num_anchors;
+    const bool any_sample = n_anchor > 0 && p->num_pts > 0;
+    if (p->bs > 0 && !feat) return fail(DA_ERR_INVALID_ARG, "mc_ms_feat is NULL");
+    if (any_sample && (!loc || !weights))
+        return fail(DA_ERR_INVALID_ARG, "sampling_location / weights is NULL");
+    if (!aligned(feat, elem)) return fail(DA_ERR_INVALID_ARG, "mc_ms_feat is not element aligned");
+    if (!aligned(loc, 8)) return fail(DA_ERR_INVALID_ARG, "sampling_location is not 8-byte aligned");
+    if (!aligned(weights, 4)) return fail(DA_ERR_INVALID_ARG, "weights is not 4-byte aligned");
+    if ((uint64_t)n_anchor * (da::kWave * da::kMaxWaves) > kU32Max)
+        return fail(DA_ERR_UNSUPPORTED, "bs * num_anchors = %lld exceeds the grid limit",
+                    (long long)n_anchor);
+
+    ka.feat = feat;
+    ka.loc = loc;
+    ka.weights = weights;
+    ka.A = (int32_t)p->num_anchors;
+    ka.C = (int32_t)C;
+    ka.P = (int32_t)p->num_pts;
+    ka.K = (int32_t)p->num_cams;
+    ka.S = (int32_t)p->num_scale;
+    ka.G = (int32_t)p->num_groups;
+    ka.D = (int32_t)(C / p->num_groups);
+    ka.npk = (int32_t)(p->num_pts * p->num_cams);
+    ka.feat_batch_bytes = (int64_t)feat_img;
+    ka.feat_image_bytes = (uint32_t)feat_img;
+    ka.row_bytes = (int32_t)(C * elem);
+    ka.grow_bytes = (int32_t)(C * 4);
+    plan.n_anchors = n_anchor;
+    plan.bf16 = p->feat_dtype == DA_BF16;
+    return DA_OK;
+}
+
+// Largest number of (point, camera) pairs whose stencils and weights fit LDS.
+da_status choose_pk_chunk(da::KArgs& ka, int desc_bytes, size_t fixed, size_t& lds) {
+    const size_t per_pair = (size_t)ka.S * (desc_bytes + 4 * (size_t)ka.G);
+    if (fixed + per_pair > (size_t)da::kLdsBudget)
+        return fail(DA_ERR_UNSUPPORTED,
+                    "one (point, camera) pair needs %zu bytes of LDS (num_scale * num_groups too large)",
+                    per_pair + fixed);
+    const int64_t fit = (int64_t)((da::kLdsBudget - fixed) / per_pair);
+    ka.pk_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ka.npk, fit));
+    lds = fixed + per_pair * ka.pk_chunk;
+    return DA_OK;
+}
+
+da_status plan_forward(const da_problem* p, Plan& plan) {
+    da::KArgs& ka = plan.ka;
+    const int64_t C = ka.C, D = ka.D;
+    const int elem = plan.bf16 ? 2 : 4;
+    const int vwide = plan.bf16 ? 8 : 4;   // 16-byte vectors
+    const int vec = (C % vwide == 0 && D % vwide == 0 && aligned(ka.feat, 16)) ? vwide : 1;
+    const int64_t nvec = C / vec;                       // vectors per row
+    const int64_t L = std::min<int64_t>(da::kWave, pow2_factor(nvec));
+    ka.L = (int32_t)L;
+    ka.log2L = ilog2(L);
+    ka.nv = (int32_t)(nvec / L);
+    const int64_t cap = std::max<int64_t>(1, 1024 / (L * vec));   // <= 1024 channels per chunk
+    ka.nv_chunk = (int32_t)std::min<int64_t>({(int64_t)ka.nv, 8, cap});
+    da::LaunchShape& s = plan.shape;
+    s.vec = vec;
+    s.nvc = next_pow2(ka.nv_chunk);
+    s.chunks = (int)((ka.nv + ka.nv_chunk - 1) / ka.nv_chunk);
+    const int64_t spw = da::kWave / L;
+    const int64_t ns = (int64_t)ka.npk * ka.S;
+    s.waves = (int)std::max<int64_t>(1, std::min<int64_t>(da::kMaxWaves, (ns + 4 * spw - 1) / (4 * spw)));
+    const size_t red = (size_t)s.waves * ka.nv_chunk * L * vec * 4;
+    (void)elem;
+    (void)p;
+    return choose_pk_chunk(ka, da::kFwdDescBytes, red, s.lds_bytes);
+}
+
+da_status plan_backward(const da_problem* p, Plan& plan) {
+    da::KArgs& ka = plan.ka;
+    const int64_t C = ka.C, D = ka.D;
+    int64_t L = std::min<int64_t>(da::kWave, pow2_factor(C));
+    int64_t seg;
+    if (D % L == 0) {
+        seg = L;                                  // a lane row lies inside one group
+    } else if (pow2_factor(D) == D) {
+        seg = D;                                  // a lane row spans L / D whole groups
+    } else {
+        L = std::min<int64_t>(da::kWave, pow2_factor(D));
+        seg = L;
+    }
+    const int64_t nv = C / L;
+    if (nv > 16)
+        return fail(DA_ERR_UNSUPPORTED,
+                    "backward: %lld channels per lane (num_embeds / %lld) exceeds 16",
+                    (long long)nv, (long long)L);
+    ka.L = (int32_t)L;
+    ka.log2L = ilog2(L);
+    ka.nv = (int32_t)nv;
+    ka.nv_chunk = (int32_t)nv;
+    ka.seg = (int32_t)seg;
+    const uint64_t gimg = (uint64_t)p->num_feat * (uint64_t)C * 4u;
+    if (gimg + 8 * (uint64_t)C > kU32Max)
+        return fail(DA_ERR_UNSUPPORTED, "one batch image of grad_feat (%llu bytes) exceeds 4 GiB",
+                    (unsigned long long)gimg);
+    ka.gfeat_batch_bytes = (int64_t)gimg;
+    ka.gfeat_image_bytes = (uint32_t)gimg;
+    da::LaunchShape& s = plan.shape;
+    s.vec = 1;
+    s.nvc = next_pow2(nv);
+    s.chunks = 1;
+    const int64_t spw = da::kWave / L;
+    s.waves = (int)std::max<int64_t>(
+        1, std::min<int64_t>(da::kMaxWaves, (ka.npk + 2 * spw - 1) / (2 * spw)));
+    return choose_pk_chunk(ka, da::kBwdDescBytes, 0, s.lds_bytes);
+}
+
+da_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DA_OK;
+    return fail(DA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+da_status backward_impl(bool zero_first, const da_problem* p, const void* feat,
+                        const int32_t* shape, const int32_t* start, const float* loc,
+                        const float* weights, const float* grad_out, float* grad_feat,
+                        float* grad_loc, float* grad_weights, void* stream) {
+    Plan plan;
+    da_status st = check_common(p, feat, shape, start, loc, weights, plan);
+    if (st != DA_OK) return st;
+    const bool any_sample = plan.n_anchors > 0 && p->num_pts > 0;
+    if (p->bs > 0 && !grad_feat) return fail(DA_ERR_INVALID_ARG, "grad_feat is NULL");
+    if (plan.n_anchors > 0 && !grad_out) return fail(DA_ERR_INVALID_ARG, "grad_out is NULL");
+    if (any_sample && (!grad_loc || !grad_weights))
+        return fail(DA_ERR_INVALID_ARG, "grad_loc / grad_weights is NULL");
+    if (!aligned(grad_out, 4) || !aligned(grad_feat, 4) || !aligned(grad_weights, 4))
+        return fail(DA_ERR_INVALID_ARG, "grad_out / grad_feat / grad_weights not 4-byte aligned");
+    if (!aligned(grad_loc, 8)) return fail(DA_ERR_INVALID_ARG, "grad_loc is not 8-byte aligned");
+    st = plan_backward(p, plan);
+    if (st != DA_OK) return st;
+    plan.ka.grad_out = grad_out;
+    plan.ka.grad_feat = grad_feat;
+    plan.ka.grad_loc = grad_loc;
+    plan.ka.grad_weights = grad_weights;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (zero_first && p->bs > 0) {
+        st = hip_status(da::launch_zero(grad_feat, p->bs * p->num_feat * p->num_embeds, s),
+                        "grad_feat zero fill");
+        if (st != DA_OK) return st;
+    }
+    if (!any_sample) return DA_OK;
+    return hip_status(da::launch_backward(plan.ka, plan.shape, plan.n_anchors, plan.bf16, s),
+                      "backward kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape,
+                     const int32_t* start, const float* loc, const float* weights, float* out,
+                     void* stream) {
+    Plan plan;
+    da_status st = check_common(p, feat, shape, start, loc, weights, plan);
+    if (st != DA_OK) return st;
+    if (plan.n_anchors > 0 && !out) return fail(DA_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(out, 4)) return fail(DA_ERR_INVALID_ARG, "out is not 4-byte aligned");
+    st = plan_forward(p, plan);
+    if (st != DA_OK) return st;
+    if (plan.n_anchors == 0) return DA_OK;
+    plan.ka.out = out;
+    return hip_status(da::launch_forward(plan.ka, plan.shape, plan.n_anchors, plan.bf16,
+                                         static_cast<hipStream_t>(stream)),
+                      "forward kernel launch");
+}
+
+da_status da_backward(const da_problem* p, const void* feat, const int32_t* shape,
+                      const int32_t* start, const float* loc, const float* weights,
+                      const float* grad_out, float* grad_feat, float* grad_loc,
+                      float* grad_weights, void* stream) {
+    return backward_impl(true, p, feat, shape, start, loc, weights, grad_out, grad_feat, grad_loc,
+                         grad_weights, stream);
+}
+
+da_status da_backward_accumulate(const da_problem* p, const void* feat, const int32_t* shape,
+                                 const int32_t* start, const float* loc, const float* weights,
+                                 const float* grad_out, float* grad_feat, float* grad_loc,
+                                 float* grad_weights, void* stream) {
+    return backward_impl(false, p, feat, shape, start, loc, weights, grad_out, grad_feat, grad_loc,
+                         grad_weights, stream);
+}
+
+const char* da_status_string(da_status s) {
+    switch (s) {
+        case DA_OK: return "DA_OK";
+        case DA_ERR_INVALID_ARG: return "DA_ERR_INVALID_ARG: malformed argument";
+        case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED: outside what the kernels handle";
+        case DA_ERR_HIP: return "DA_ERR_HIP: the HIP runtime refused the launch";
+    }
+    return "unknown da_status";
+}
+
+const char* da_last_error(void) { return g_last_error; }
+
+int32_t da_version(void) { return DA_VERSION; }
+
+}  // extern "C"
