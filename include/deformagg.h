@@ -37,20 +37,22 @@
  *     allocated on the current HIP device; `stream` is a hipStream_t (NULL = the
  *     legacy default stream).  spatial_shape and scale_start_index are HOST arrays
  *     read during the call; they are not retained.
- *   - The caller owns every buffer.  The library never allocates or frees device
- *     memory and keeps no state between calls; calls are asynchronous on `stream`
- *     and may be captured into a HIP graph.  Faults inside a kernel surface at the
- *     caller's next synchronisation.
+ *   - The caller owns every buffer, including the backward workspace.  The library
+ *     never allocates or frees device memory and keeps no state between calls;
+ *     calls are asynchronous on `stream` and may be captured into a HIP graph
+ *     (zero fills are kernels, not memset nodes).  Faults inside a kernel surface
+ *     at the caller's next synchronisation.
  *   - All argument checks run on the host before anything is enqueued.  On any
  *     error no work is enqueued and no output is touched; da_last_error() returns
  *     a message naming the failed check (per calling thread).
  *   - Floating-point results are computed in binary32.  The forward pass is
- *     deterministic (no atomics).  The backward feature gradient is accumulated
- *     with binary32 atomic adds, so its rounding may differ from run to run.
+ *     deterministic (no atomics); so are the location and weight gradients.  The
+ *     feature gradient's summation order may vary from run to run (see da_backward).
  */
 #ifndef DEFORMAGG_H
 #define DEFORMAGG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -94,18 +96,21 @@ typedef struct {
  *
  *   mc_ms_feat         device [bs, num_feat, C], feat_dtype.  Level (k, s) occupies rows
  *                      scale_start_index[k,s] .. + H*W - 1 of each batch image, row-major
- *                      (H, W), C contiguous channels per row.  16-byte aligned, and
- *                      C * element size must be a multiple of 4 bytes.
+ *                      (H, W), C contiguous channels per row.  Element aligned; 16-byte
+ *                      alignment with C and C/G multiples of 16 bytes' worth of elements
+ *                      enables 16-byte vector loads.
  *   spatial_shape      HOST int32 [K, S, 2]: (H, W) of each level, 1 <= H, W <= DA_MAX_EXTENT.
  *   scale_start_index  HOST int32 [K, S]: first row of each level; start + H*W <= num_feat.
  *   sampling_location  device float [bs, A, P, K, 2], normalised (x, y); 8-byte aligned.
  *   weights            device float [bs, A, P, K, S, G]; 4-byte aligned.
- *   out                device float [bs, A, C], fully overwritten; 16-byte aligned.
+ *   out                device float [bs, A, C], fully overwritten; 4-byte aligned.
  *
- * Returns DA_OK, DA_ERR_INVALID_ARG (null pointer where data is needed, malformed
- * sizes or level table), DA_ERR_UNSUPPORTED (alignment, one batch image of the
- * features or of the feature gradient larger than 4 GiB - 64 KiB, grid limits) or
- * DA_ERR_HIP.
+ * Returns DA_OK, DA_ERR_INVALID_ARG (null pointer where data is needed, misaligned
+ * pointer, malformed sizes or level table), DA_ERR_UNSUPPORTED (one batch image of the
+ * features -- or, in the backward, of the feature gradient -- plus two rows above
+ * 2^32 - 1 bytes; num_embeds > 2^20; bs * A * 512 >= 2^32; one (point, camera) pair's
+ * stencils and weights above 48 KiB of LDS; in the backward, num_embeds more than 16
+ * times the largest power of two dividing C / G, capped at 64) or DA_ERR_HIP.
  */
 da_status da_forward(const da_problem* problem,
                      const void* mc_ms_feat,
@@ -117,16 +122,33 @@ da_status da_forward(const da_problem* problem,
                      void* stream);
 
 /*
+ * da_backward_workspace_size -- bytes of device workspace da_backward and
+ * da_backward_accumulate need for `problem` (0 when there is no sample).  Only the
+ * sizes in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
+ * >= 2^32 or the sample count bs*A*P*K*S >= 2^30 (da_backward_atomic still works).
+ */
+da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
+
+/*
  * da_backward -- the backward pass (section 4.1).  Same inputs as da_forward, plus
  *
  *   grad_out           device float [bs, A, C]; 4-byte aligned.
  *   grad_feat          device float [bs, num_feat, C] (binary32 also for bf16 features):
- *                      zeroed by the call, then accumulated; 16-byte aligned.
- *   grad_loc           device float [bs, A, P, K, 2], fully overwritten.
+ *                      fully overwritten (rows no sample touches are zero); 4-byte aligned.
+ *   grad_loc           device float [bs, A, P, K, 2], fully overwritten; 8-byte aligned.
  *   grad_weights       device float [bs, A, P, K, S, G], fully overwritten.
+ *   workspace          device scratch of at least da_backward_workspace_size() bytes,
+ *                      256-byte aligned, owned by the caller; its contents on entry do
+ *                      not matter and are garbage on return.  May be NULL when the size
+ *                      is 0.  Calls that overlap in time must not share a workspace.
  *
- * Rows of grad_feat that no sample touches come back as zero.  Same errors as
- * da_forward.
+ * The feature gradient is formed as a gather: every (sample, corner) term is first
+ * bucketed by feature row, then each row is summed by one wave and stored, so almost
+ * no floating-point atomics are issued.  The order in which a row's terms are added
+ * depends on the order integer atomics retire in, so grad_feat may differ in rounding
+ * from run to run; grad_loc and grad_weights are deterministic.
+ * Same errors as da_forward, plus DA_ERR_INVALID_ARG for a missing, misaligned or too
+ * small workspace and the DA_ERR_UNSUPPORTED cases of da_backward_workspace_size.
  */
 da_status da_backward(const da_problem* problem,
                       const void* mc_ms_feat,
@@ -138,14 +160,15 @@ da_status da_backward(const da_problem* problem,
                       float* grad_feat,
                       float* grad_loc,
                       float* grad_weights,
+                      void* workspace,
+                      size_t workspace_bytes,
                       void* stream);
 
 /*
- * da_backward_accumulate -- as da_backward, except that grad_feat is NOT zeroed: the
- * feature gradient is added to what grad_feat already holds (for several
- * aggregations that read one feature map, or for a caller that keeps a
- * zero-initialised gradient buffer).  grad_loc and grad_weights are still
- * overwritten.  Same arguments and errors as da_backward.
+ * da_backward_accumulate -- as da_backward, except that grad_feat is NOT overwritten:
+ * the feature gradient is added to what grad_feat already holds (for several
+ * aggregations that read one feature map, or a caller that keeps a running gradient).
+ * grad_loc and grad_weights are still overwritten.  Same arguments and errors.
  */
 da_status da_backward_accumulate(const da_problem* problem,
                                  const void* mc_ms_feat,
@@ -157,7 +180,28 @@ da_status da_backward_accumulate(const da_problem* problem,
                                  float* grad_feat,
                                  float* grad_loc,
                                  float* grad_weights,
+                                 void* workspace,
+                                 size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * da_backward_atomic -- the backward pass in the page's scatter form, with no
+ * workspace: grad_feat is zero-filled, then every (sample, corner, channel) term is
+ * added with a binary32 atomic (section 4.1 adds them the same way).  Results equal
+ * da_backward's up to rounding; it is slower wherever atomics are the bottleneck.
+ * Arguments as da_backward without the workspace; same errors as da_forward.
+ */
+da_status da_backward_atomic(const da_problem* problem,
+                             const void* mc_ms_feat,
+                             const int32_t* spatial_shape,
+                             const int32_t* scale_start_index,
+                             const float* sampling_location,
+                             const float* weights,
+                             const float* grad_out,
+                             float* grad_feat,
+                             float* grad_loc,
+                             float* grad_weights,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* da_status_string(da_status status);

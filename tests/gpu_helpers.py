@@ -46,9 +46,15 @@ def gpu_forward(dev):
     return out
 
 
-def gpu_backward(dev, accumulate_into=None):
+def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None):
     import view_deformable_feature_amd as vdf
-    if accumulate_into is None:
+    if atomic:
+        r = vdf.da_backward_atomic(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
+                                   dev["loc"], dev["weights"], dev["grad_out"])
+    elif workspace is not None:
+        r = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
+                            dev["loc"], dev["weights"], dev["grad_out"], workspace=workspace)
+    elif accumulate_into is None:
         r = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
                             dev["loc"], dev["weights"], dev["grad_out"])
     else:

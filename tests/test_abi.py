@@ -23,6 +23,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_functions()
     assert set(names) >= {"da_forward", "da_backward", "da_backward_accumulate",
+                          "da_backward_atomic", "da_backward_workspace_size",
                           "da_status_string", "da_last_error", "da_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in deformagg.h but not exported"
@@ -60,10 +61,13 @@ def _fwd(lib, prob, feat=FAKE, shape=HOST_SHAPE, start=HOST_START, loc=FAKE, w=F
 
 
 def _bwd(lib, prob, name="da_backward", feat=FAKE, loc=FAKE, w=FAKE, go=FAKE, gf=FAKE, gl=FAKE,
-         gw=FAKE, shape=HOST_SHAPE, start=HOST_START):
+         gw=FAKE, shape=HOST_SHAPE, start=HOST_START, ws=FAKE, ws_bytes=1 << 40):
     vp = ctypes.c_void_p
-    return getattr(lib, name)(ctypes.byref(prob), vp(feat), _i32p(shape), _i32p(start), vp(loc),
-                              vp(w), vp(go), vp(gf), vp(gl), vp(gw), None)
+    args = [ctypes.byref(prob), vp(feat), _i32p(shape), _i32p(start), vp(loc), vp(w), vp(go),
+            vp(gf), vp(gl), vp(gw)]
+    if name == "da_backward_atomic":
+        return lib.da_backward_atomic(*args, None)
+    return getattr(lib, name)(*args, vp(ws), ws_bytes, None)
 
 
 def _msg(lib):
@@ -123,7 +127,7 @@ def test_rejects_null_pointers(lib):
     assert _fwd(lib, p, out=0) == 1 and "out is NULL" in _msg(lib)
     for kw, needle in ((dict(go=0), "grad_out"), (dict(gf=0), "grad_feat"),
                        (dict(gl=0), "grad_loc"), (dict(gw=0), "grad_loc / grad_weights")):
-        for name in ("da_backward", "da_backward_accumulate"):
+        for name in ("da_backward", "da_backward_accumulate", "da_backward_atomic"):
             assert _bwd(lib, p, name, **kw) == 1
             assert needle in _msg(lib)
 
@@ -185,3 +189,23 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(1, 1, 1, 1, 1, 1)
     with pytest.raises(ValueError, match="no CPU path"):
         vdf.da_forward(feat, wl_shape, np.zeros((1, 1), np.int32), loc, w)
+
+
+def test_workspace_size_and_checks(lib):
+    n = ctypes.c_size_t(0)
+    p = _prob()
+    assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    # counts + local prefix + tile prefix + ranks + 16-byte entries, each 256-aligned
+    n_rows, n_samples = 256, 8 * 4
+    expect = 2 * 1024 + 256 + 512 + n_samples * 4 * 16
+    assert n.value == expect
+    assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_pts=0)), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.da_backward_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.da_backward_workspace_size(ctypes.byref(p), None) == 1
+    big = _prob(bs=1 << 12, num_anchors=1 << 12, num_pts=1 << 7)
+    assert lib.da_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 2
+    for name in ("da_backward", "da_backward_accumulate"):
+        assert _bwd(lib, p, name, ws=0) == 1 and "workspace is NULL" in _msg(lib)
+        assert _bwd(lib, p, name, ws=FAKE + 16) == 1 and "256-byte" in _msg(lib)
+        assert _bwd(lib, p, name, ws_bytes=expect - 1) == 1 and "needed" in _msg(lib)

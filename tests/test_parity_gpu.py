@@ -303,3 +303,50 @@ def test_errors_surface_as_exceptions():
     bad_start = np.array([[5]], np.int32)
     with pytest.raises(DAError, match="inside num_feat"):
         vdf.da_forward(dev["feat"], dev["spatial_shape"], bad_start, dev["loc"], dev["weights"])
+
+
+# ---------------------------------------------------------------------------------------
+# the scatter form and workspace handling
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "nuscenes_bwd"])
+def test_backward_atomic_form(name):
+    inp = W.make_inputs(W.WORKLOADS[name])
+    dev = to_device(inp)
+    say(f"[parity] {name}: da_backward_atomic")
+    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, atomic=True))
+    r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
+    assert_close(f"{name} atomic grad_feat", gf, r_gf, TOL_BWD)
+    assert_close(f"{name} atomic grad_loc", gl, r_gl, TOL_BWD)
+    assert_close(f"{name} atomic grad_weights", gw, r_gw, TOL_BWD)
+
+
+def test_backward_atomic_form_ragged_bf16():
+    wl = W.custom("atomic_ragged", bs=2, num_cams=3, levels=((13, 29), (7, 15)), C=96, groups=3,
+                  anchors=19, pts=5, feat_dtype="bf16", loc_lo=-0.1, loc_hi=1.1, seed=41)
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, atomic=True))
+    r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
+    assert_close("atomic bf16 grad_feat", gf, r_gf, TOL_BF16)
+    assert_close("atomic bf16 grad_loc", gl, r_gl, TOL_BF16)
+    assert_close("atomic bf16 grad_weights", gw, r_gw, TOL_BF16)
+
+
+def test_workspace_reused_across_calls():
+    """One caller-owned workspace serves two calls in a row, the second smaller; its
+    stale contents from the first call must not leak into the second."""
+    import view_deformable_feature_amd as vdf
+    big = W.make_inputs(W.custom("ws_big", bs=2, num_cams=2, levels=((20, 30), (10, 15)), C=64,
+                                 groups=4, anchors=40, pts=7, loc_lo=-0.1, loc_hi=1.1, seed=51))
+    small = W.make_inputs(W.custom("ws_small", bs=1, num_cams=2, levels=((6, 9), (3, 5)), C=64,
+                                   groups=4, anchors=9, pts=3, loc_lo=-0.1, loc_hi=1.1, seed=52))
+    dev_b, dev_s = to_device(big), to_device(small)
+    n = vdf.workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"], dev_b["weights"])
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    for inp, dev in ((big, dev_b), (small, dev_s), (big, dev_b)):
+        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, workspace=ws))
+        r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
+        assert_close("ws grad_feat", gf, r_gf, TOL_BWD)
+        assert_close("ws grad_loc", gl, r_gl, TOL_BWD)
+        assert_close("ws grad_weights", gw, r_gw, TOL_BWD)

@@ -58,8 +58,12 @@ def load() -> ctypes.CDLL:
     lib.da_forward.restype = ctypes.c_int
     for name in ("da_backward", "da_backward_accumulate"):
         f = getattr(lib, name)
-        f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp]
+        f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         f.restype = ctypes.c_int
+    lib.da_backward_atomic.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp]
+    lib.da_backward_atomic.restype = ctypes.c_int
+    lib.da_backward_workspace_size.argtypes = [prob, ctypes.POINTER(ctypes.c_size_t)]
+    lib.da_backward_workspace_size.restype = ctypes.c_int
     lib.da_status_string.argtypes = [ctypes.c_int]
     lib.da_status_string.restype = ctypes.c_char_p
     lib.da_last_error.argtypes = []

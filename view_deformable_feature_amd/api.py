@@ -1,7 +1,7 @@
 """PyTorch-facing binding of libdeformagg.
 
 Same names as the C ABI (``da_forward``, ``da_backward``,
-``da_backward_accumulate``) plus the autograd wrapper
+``da_backward_accumulate``, ``da_backward_atomic``) plus the autograd wrapper
 ``DeformableAggregationFunction`` whose ``forward(ctx, mc_ms_feat,
 spatial_shape, scale_start_index, sampling_location, weights)`` follows the
 signature shown in section 6 of the Sparse4D deformable_aggregation
@@ -21,8 +21,9 @@ import torch
 
 from . import _lib
 
-__all__ = ["da_forward", "da_backward", "da_backward_accumulate",
-           "DeformableAggregationFunction", "deformable_aggregation", "problem_of"]
+__all__ = ["da_forward", "da_backward", "da_backward_accumulate", "da_backward_atomic",
+           "workspace_size", "DeformableAggregationFunction", "deformable_aggregation",
+           "problem_of"]
 
 IntTable = Union[torch.Tensor, np.ndarray, Sequence]
 
@@ -115,8 +116,19 @@ def da_forward(mc_ms_feat: torch.Tensor, spatial_shape: IntTable, scale_start_in
     return out
 
 
+def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights) -> int:
+    """Bytes of workspace da_backward / da_backward_accumulate need for these shapes."""
+    lib = _lib.load()
+    prob = problem_of(mc_ms_feat, _host_i32(spatial_shape), sampling_location, weights)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
+               "da_backward_workspace_size")
+    return int(n.value)
+
+
 def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
-              weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None):
+              weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None,
+              workspace=None):
     lib = _lib.load()
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
                                   sampling_location, weights)
@@ -134,25 +146,50 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
     _need(grad_loc, "grad_loc", torch.float32, dev, tuple(sampling_location.shape))
     _need(grad_weights, "grad_weights", torch.float32, dev, tuple(weights.shape))
     with torch.cuda.device(dev):
-        st = getattr(lib, func)(ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
-                                _ptr(sampling_location), _ptr(weights), _ptr(grad_out),
-                                _ptr(grad_feat), _ptr(grad_loc), _ptr(grad_weights), _stream(dev))
+        common = (ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
+                  _ptr(sampling_location), _ptr(weights), _ptr(grad_out), _ptr(grad_feat),
+                  _ptr(grad_loc), _ptr(grad_weights))
+        if func == "da_backward_atomic":
+            st = lib.da_backward_atomic(*common, _stream(dev))
+        else:
+            n = ctypes.c_size_t(0)
+            _lib.check(lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
+                       "da_backward_workspace_size")
+            if workspace is None and n.value:
+                # torch's caching allocator: no device allocation on the steady path
+                workspace = torch.empty(int(n.value), device=dev, dtype=torch.uint8)
+            if workspace is not None:
+                _need(workspace, "workspace", torch.uint8, dev)
+                if workspace.numel() < n.value:
+                    raise ValueError(f"workspace has {workspace.numel()} bytes, {n.value} needed")
+            st = getattr(lib, func)(*common, _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(dev))
     _lib.check(st, func)
     return grad_feat, grad_loc, grad_weights
 
 
 def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
-                grad_out, grad_feat=None, grad_loc=None, grad_weights=None
+                grad_out, grad_feat=None, grad_loc=None, grad_weights=None, workspace=None
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
     return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
-                     sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights)
+                     sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
+                     workspace)
 
 
 def da_backward_accumulate(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
-                           weights, grad_out, grad_feat, grad_loc=None, grad_weights=None):
+                           weights, grad_out, grad_feat, grad_loc=None, grad_weights=None,
+                           workspace=None):
     """As da_backward, adding the feature gradient into the existing ``grad_feat``."""
     return _backward("da_backward_accumulate", mc_ms_feat, spatial_shape, scale_start_index,
+                     sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
+                     workspace)
+
+
+def da_backward_atomic(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
+                       weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None):
+    """As da_backward, with the feature gradient scattered by binary32 atomics (no workspace)."""
+    return _backward("da_backward_atomic", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights)
 
 

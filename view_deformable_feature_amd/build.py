@@ -14,8 +14,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
-SOURCES = [os.path.join(CSRC, "da_kernels.hip"), os.path.join(CSRC, "da_api.cpp")]
-HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(CSRC, "da_internal.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("da_forward.hip", "da_backward.hip", "da_api.cpp")]
+HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(CSRC, "da_internal.h"),
+           os.path.join(CSRC, "da_device.h")]
 ARCH = "gfx950"
 
 

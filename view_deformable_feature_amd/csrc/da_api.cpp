@@ -36,12 +36,6 @@ int ilog2(int64_t x) {
     return r;
 }
 
-int next_pow2(int64_t x) {
-    int r = 1;
-    while (r < x) r <<= 1;
-    return r;
-}
-
 constexpr uint64_t kU32Max = 0xffffffffull;
 
 struct Plan {
@@ -163,44 +157,74 @@ da_status plan_forward(const da_problem* p, Plan& plan) {
     ka.L = (int32_t)L;
     ka.log2L = ilog2(L);
     ka.nv = (int32_t)(nvec / L);
-    const int64_t cap = std::max<int64_t>(1, 1024 / (L * vec));   // <= 1024 channels per chunk
-    ka.nv_chunk = (int32_t)std::min<int64_t>({(int64_t)ka.nv, 8, cap});
+    // vectors per lane handled by one workgroup: the largest divisor of nv that
+    // is <= 8 and keeps a chunk within 1024 channels; grid.y covers the rest
+    const int64_t cap = std::min<int64_t>(8, std::max<int64_t>(1, 1024 / (L * vec)));
+    int64_t nvc = 1;
+    for (int64_t d = std::min<int64_t>(cap, ka.nv); d >= 1; --d)
+        if (ka.nv % d == 0) { nvc = d; break; }
+    ka.nv_chunk = (int32_t)nvc;
     da::LaunchShape& s = plan.shape;
     s.vec = vec;
-    s.nvc = next_pow2(ka.nv_chunk);
-    s.chunks = (int)((ka.nv + ka.nv_chunk - 1) / ka.nv_chunk);
+    s.nvc = (int)nvc;
+    s.chunks = (int)(ka.nv / nvc);
     const int64_t spw = da::kWave / L;
     const int64_t ns = (int64_t)ka.npk * ka.S;
     s.waves = (int)std::max<int64_t>(1, std::min<int64_t>(da::kMaxWaves, (ns + 4 * spw - 1) / (4 * spw)));
-    const size_t red = (size_t)s.waves * ka.nv_chunk * L * vec * 4;
+    // cross-wave partial sums plus the null descriptor slot
+    const size_t fixed = (size_t)s.waves * ka.nv_chunk * L * vec * 4 + da::kFwdDescBytes;
     (void)elem;
     (void)p;
-    return choose_pk_chunk(ka, da::kFwdDescBytes, red, s.lds_bytes);
+    return choose_pk_chunk(ka, da::kFwdDescBytes, fixed, s.lds_bytes);
 }
 
-da_status plan_backward(const da_problem* p, Plan& plan) {
-    da::KArgs& ka = plan.ka;
-    const int64_t C = ka.C, D = ka.D;
-    int64_t L = std::min<int64_t>(da::kWave, pow2_factor(C));
-    int64_t seg;
-    if (D % L == 0) {
+// Lane layout of the per-anchor backward kernel for vectors of `vec` channels:
+// L lanes per row group, `seg` lanes per weight-gradient group reduction, nv
+// vectors per lane.  False when more than max_nv vectors per lane are needed.
+bool bwd_layout(int64_t C, int64_t D, int64_t vec, int64_t max_nv, int64_t& L, int64_t& seg,
+                int64_t& nv) {
+    const int64_t Cv = C / vec, Dv = D / vec;
+    L = std::min<int64_t>(da::kWave, pow2_factor(Cv));
+    if (Dv % L == 0) {
         seg = L;                                  // a lane row lies inside one group
-    } else if (pow2_factor(D) == D) {
-        seg = D;                                  // a lane row spans L / D whole groups
+    } else if (pow2_factor(Dv) == Dv) {
+        seg = Dv;                                 // a lane row spans L / Dv whole groups
     } else {
-        L = std::min<int64_t>(da::kWave, pow2_factor(D));
+        L = std::min<int64_t>(da::kWave, pow2_factor(Dv));
         seg = L;
     }
-    const int64_t nv = C / L;
-    if (nv > 16)
+    nv = Cv / L;
+    return nv <= max_nv;
+}
+
+da_status plan_backward(const da_problem* p, Plan& plan, bool gather) {
+    da::KArgs& ka = plan.ka;
+    int s_gather_nv_out = 1;
+    const int64_t C = ka.C, D = ka.D;
+    // the gather form only reads features: 16-byte vectors per lane when the
+    // rows and groups allow; the scatter form keeps one channel per lane so that
+    // each atomic instruction covers consecutive floats
+    const int64_t vw = plan.bf16 ? 8 : 4;
+    int64_t L = 0, seg = 0, nv = 0, vec = 1;
+    if (gather && C % vw == 0 && D % vw == 0 && aligned(ka.feat, 16) &&
+        bwd_layout(C, D, vw, 8, L, seg, nv)) {
+        vec = vw;
+    } else if (!bwd_layout(C, D, 1, 16, L, seg, nv)) {
         return fail(DA_ERR_UNSUPPORTED,
                     "backward: %lld channels per lane (num_embeds / %lld) exceeds 16",
                     (long long)nv, (long long)L);
+    }
     ka.L = (int32_t)L;
     ka.log2L = ilog2(L);
     ka.nv = (int32_t)nv;
     ka.nv_chunk = (int32_t)nv;
     ka.seg = (int32_t)seg;
+    // feature-gradient gather: 16-byte vectors when rows and groups allow
+    ka.gather_vec = (C % 4 == 0 && D % 4 == 0) ? 4 : 1;
+    const int64_t gvec = (C / ka.gather_vec + da::kWave - 1) / da::kWave;
+    int gnv = 1;
+    while (gnv < gvec) gnv <<= 1;
+    s_gather_nv_out = gnv;
     const uint64_t gimg = (uint64_t)p->num_feat * (uint64_t)C * 4u;
     if (gimg + 8 * (uint64_t)C > kU32Max)
         return fail(DA_ERR_UNSUPPORTED, "one batch image of grad_feat (%llu bytes) exceeds 4 GiB",
@@ -208,13 +232,14 @@ da_status plan_backward(const da_problem* p, Plan& plan) {
     ka.gfeat_batch_bytes = (int64_t)gimg;
     ka.gfeat_image_bytes = (uint32_t)gimg;
     da::LaunchShape& s = plan.shape;
-    s.vec = 1;
-    s.nvc = next_pow2(nv);
+    s.vec = (int)vec;
+    s.nvc = (int)nv;
+    s.gather_nv = s_gather_nv_out;
     s.chunks = 1;
     const int64_t spw = da::kWave / L;
     s.waves = (int)std::max<int64_t>(
         1, std::min<int64_t>(da::kMaxWaves, (ka.npk + 2 * spw - 1) / (2 * spw)));
-    return choose_pk_chunk(ka, da::kBwdDescBytes, 0, s.lds_bytes);
+    return choose_pk_chunk(ka, da::kBwdDescBytes, da::kBwdDescBytes, s.lds_bytes);
 }
 
 da_status hip_status(hipError_t e, const char* what) {
@@ -222,10 +247,50 @@ da_status hip_status(hipError_t e, const char* what) {
     return fail(DA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-da_status backward_impl(bool zero_first, const da_problem* p, const void* feat,
+// Workspace of the gather form of the backward, each part 256-byte aligned.
+struct WsLayout {
+    size_t cnt, local_start, tile_prefix, rank, entries, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
+    WsLayout w;
+    const uint64_t n_tiles = (n_rows + da::kScanTile - 1) / da::kScanTile;
+    size_t off = 0;
+    w.cnt = off;
+    off += align256(n_rows * 4);
+    w.local_start = off;
+    off += align256(n_rows * 4);
+    w.tile_prefix = off;
+    off += align256((n_tiles + 1) * 4);
+    w.rank = off;
+    off += align256(n_samples * 16);
+    w.entries = off;
+    off += align256(n_samples * 4 * sizeof(da::Entry));
+    w.total = off;
+    return w;
+}
+
+// Sizes of the gather form; fails when its 32-bit row / entry indices overflow.
+da_status gather_sizes(const da_problem* p, uint64_t& n_rows, uint64_t& n_samples) {
+    n_rows = (uint64_t)p->bs * (uint64_t)p->num_feat;
+    n_samples = (uint64_t)p->bs * p->num_anchors * p->num_pts * p->num_cams * p->num_scale;
+    if (n_rows >= (1ull << 32) || n_samples >= (1ull << 30))
+        return fail(DA_ERR_UNSUPPORTED,
+                    "backward: bs * num_feat (%llu) or the sample count (%llu) is too large for the "
+                    "gather workspace (use da_backward_atomic)",
+                    (unsigned long long)n_rows, (unsigned long long)n_samples);
+    return DA_OK;
+}
+
+enum class BwdMode { kGather, kGatherAccumulate, kScatter };
+
+da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                         const int32_t* shape, const int32_t* start, const float* loc,
                         const float* weights, const float* grad_out, float* grad_feat,
-                        float* grad_loc, float* grad_weights, void* stream) {
+                        float* grad_loc, float* grad_weights, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     Plan plan;
     da_status st = check_common(p, feat, shape, start, loc, weights, plan);
     if (st != DA_OK) return st;
@@ -237,20 +302,52 @@ da_status backward_impl(bool zero_first, const da_problem* p, const void* feat,
     if (!aligned(grad_out, 4) || !aligned(grad_feat, 4) || !aligned(grad_weights, 4))
         return fail(DA_ERR_INVALID_ARG, "grad_out / grad_feat / grad_weights not 4-byte aligned");
     if (!aligned(grad_loc, 8)) return fail(DA_ERR_INVALID_ARG, "grad_loc is not 8-byte aligned");
-    st = plan_backward(p, plan);
+    st = plan_backward(p, plan, mode != BwdMode::kScatter);
     if (st != DA_OK) return st;
-    plan.ka.grad_out = grad_out;
-    plan.ka.grad_feat = grad_feat;
-    plan.ka.grad_loc = grad_loc;
-    plan.ka.grad_weights = grad_weights;
+    da::KArgs& ka = plan.ka;
+    ka.grad_out = grad_out;
+    ka.grad_feat = grad_feat;
+    ka.grad_loc = grad_loc;
+    ka.grad_weights = grad_weights;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (zero_first && p->bs > 0) {
-        st = hip_status(da::launch_zero(grad_feat, p->bs * p->num_feat * p->num_embeds, s),
+
+    if (mode != BwdMode::kScatter) {
+        uint64_t n_rows = 0, n_samples = 0;
+        st = gather_sizes(p, n_rows, n_samples);
+        if (st != DA_OK) return st;
+        if (any_sample) {
+            const WsLayout w = ws_layout(n_rows, n_samples);
+            if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
+            if (!aligned(workspace, 256))
+                return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+            if (workspace_bytes < w.total)
+                return fail(DA_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed",
+                            workspace_bytes, w.total);
+            unsigned char* base = static_cast<unsigned char*>(workspace);
+            ka.cnt = reinterpret_cast<uint32_t*>(base + w.cnt);
+            ka.local_start = reinterpret_cast<uint32_t*>(base + w.local_start);
+            ka.tile_prefix = reinterpret_cast<uint32_t*>(base + w.tile_prefix);
+            ka.rank = reinterpret_cast<uint32_t*>(base + w.rank);
+            ka.entries = reinterpret_cast<da::Entry*>(base + w.entries);
+            ka.n_rows = (uint32_t)n_rows;
+            ka.n_samples = (uint32_t)n_samples;
+            ka.n_anchors = (uint32_t)plan.n_anchors;
+            ka.n_tiles = (uint32_t)((n_rows + da::kScanTile - 1) / da::kScanTile);
+            ka.num_feat = (int32_t)p->num_feat;
+            ka.accumulate = mode == BwdMode::kGatherAccumulate ? 1 : 0;
+            if (ka.gather_vec == 4 && !aligned(grad_feat, 16)) ka.gather_vec = 1;
+        }
+    }
+    if (mode != BwdMode::kGatherAccumulate && p->bs > 0) {
+        st = hip_status(da::launch_fill_zero(grad_feat, p->bs * p->num_feat * p->num_embeds, s),
                         "grad_feat zero fill");
         if (st != DA_OK) return st;
     }
     if (!any_sample) return DA_OK;
-    return hip_status(da::launch_backward(plan.ka, plan.shape, plan.n_anchors, plan.bf16, s),
+    if (mode == BwdMode::kScatter)
+        return hip_status(da::launch_backward_scatter(ka, plan.shape, plan.n_anchors, plan.bf16, s),
+                          "backward kernel launch");
+    return hip_status(da::launch_backward_gather(ka, plan.shape, plan.n_anchors, plan.bf16, s),
                       "backward kernel launch");
 }
 
@@ -275,20 +372,43 @@ da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape
                       "forward kernel launch");
 }
 
+da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
+    if (!bytes) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
+    if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->bs < 0 || p->num_anchors < 0 || p->num_pts < 0 || p->num_feat < 1 ||
+        p->num_cams < 1 || p->num_scale < 1)
+        return fail(DA_ERR_INVALID_ARG, "malformed problem sizes");
+    uint64_t n_rows = 0, n_samples = 0;
+    const da_status st = gather_sizes(p, n_rows, n_samples);
+    if (st != DA_OK) return st;
+    *bytes = n_samples == 0 ? 0 : ws_layout(n_rows, n_samples).total;
+    return DA_OK;
+}
+
 da_status da_backward(const da_problem* p, const void* feat, const int32_t* shape,
                       const int32_t* start, const float* loc, const float* weights,
                       const float* grad_out, float* grad_feat, float* grad_loc,
-                      float* grad_weights, void* stream) {
-    return backward_impl(true, p, feat, shape, start, loc, weights, grad_out, grad_feat, grad_loc,
-                         grad_weights, stream);
+                      float* grad_weights, void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(BwdMode::kGather, p, feat, shape, start, loc, weights, grad_out,
+                         grad_feat, grad_loc, grad_weights, workspace, workspace_bytes, stream);
 }
 
 da_status da_backward_accumulate(const da_problem* p, const void* feat, const int32_t* shape,
                                  const int32_t* start, const float* loc, const float* weights,
                                  const float* grad_out, float* grad_feat, float* grad_loc,
-                                 float* grad_weights, void* stream) {
-    return backward_impl(false, p, feat, shape, start, loc, weights, grad_out, grad_feat, grad_loc,
-                         grad_weights, stream);
+                                 float* grad_weights, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return backward_impl(BwdMode::kGatherAccumulate, p, feat, shape, start, loc, weights,
+                         grad_out, grad_feat, grad_loc, grad_weights, workspace, workspace_bytes,
+                         stream);
+}
+
+da_status da_backward_atomic(const da_problem* p, const void* feat, const int32_t* shape,
+                             const int32_t* start, const float* loc, const float* weights,
+                             const float* grad_out, float* grad_feat, float* grad_loc,
+                             float* grad_weights, void* stream) {
+    return backward_impl(BwdMode::kScatter, p, feat, shape, start, loc, weights, grad_out,
+                         grad_feat, grad_loc, grad_weights, nullptr, 0, stream);
 }
 
 const char* da_status_string(da_status s) {

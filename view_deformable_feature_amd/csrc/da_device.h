@@ -1,0 +1,170 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// buffer resources, vector loads, the bilinear stencil, LDS descriptors.
+//
+// Definition followed: the Sparse4D deformable_aggregation walkthrough
+// (mhpn.cn/news/1081857), section 3.1 (HWC offsets) and section 3.2
+// (bilinear sampling with per-corner zero padding).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "da_internal.h"
+
+namespace da {
+
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts:
+// 32-bit data format, range checking on the byte offset.  Loads whose offset
+// lies past num_records return 0 and atomics there are dropped, without any
+// memory request.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRawBufferWord3);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Load VEC consecutive channels as floats.  voff: per-lane byte offset (an
+// out-of-range value yields zeros); soff: wave-uniform byte offset.
+template <typename T, int VEC>
+struct VecLoad;
+
+template <>
+struct VecLoad<float, 1> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[1]) {
+        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+};
+
+template <>
+struct VecLoad<float, 4> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[4]) {
+        auto q = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        v[0] = __uint_as_float(q[0]);
+        v[1] = __uint_as_float(q[1]);
+        v[2] = __uint_as_float(q[2]);
+        v[3] = __uint_as_float(q[3]);
+    }
+};
+
+template <>
+struct VecLoad<uint16_t, 1> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[1]) {
+        v[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)
+                               << 16);
+    }
+};
+
+template <>
+struct VecLoad<uint16_t, 8> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[8]) {
+        auto q = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_lo(q[e]);
+            v[2 * e + 1] = bf16_hi(q[e]);
+        }
+    }
+};
+
+struct FwdDesc {
+    uint32_t off[4];   // byte offsets of the four corner rows in the feature image
+    float cw[4];       // hh*hw, hh*lw, lh*hw, lh*lw
+};
+static_assert(sizeof(FwdDesc) == kFwdDescBytes, "FwdDesc layout");
+
+struct BwdDesc {
+    uint32_t off[4];   // feature image byte offsets
+    uint32_t goff[4];  // feature-gradient image byte offsets (scatter path)
+    float cw[4];       // corner weights
+    float gx[4];       // d val / d x per corner value: W * (-hh, hh, -lh, lh)
+    float gy[4];       // d val / d y per corner value: H * (-hw, -lw, hw, lw)
+};
+static_assert(sizeof(BwdDesc) == kBwdDescBytes, "BwdDesc layout");
+
+// Bilinear stencil of sample t = pk * S + s of anchor `ba` (section 3.2).  The
+// pixel coordinate is a binary32 product rounded, then a rounded subtraction:
+// floor() of it selects the corner cell, so it must not be fused.
+struct Stencil {
+    bool inside;
+    int32_t row[4];        // absolute row in the batch image or -1
+    float cw[4];
+    float lh, lw, hh, hw;
+    float H, W;
+};
+
+__device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int t) {
+    // t < P*K*S and ba < 2^23 are guaranteed by the host checks
+    Stencil st;
+    const int pk = t / a.S;
+    const int s = t - pk * a.S;
+    const int k = pk % a.K;
+    const int lvl = k * a.S + s;
+    const int32_t H = a.lv.H[lvl], W = a.lv.W[lvl], start = a.lv.start[lvl];
+    const float2 xy = *reinterpret_cast<const float2*>(a.loc + (ba * a.npk + pk) * 2);
+    float w_im, h_im;
+    {
+#pragma clang fp contract(off)
+        const float wx = xy.x * (float)W;
+        const float hy = xy.y * (float)H;
+        w_im = wx - 0.5f;
+        h_im = hy - 0.5f;
+    }
+    st.H = (float)H;
+    st.W = (float)W;
+    st.inside = h_im > -1.0f && w_im > -1.0f && h_im < (float)H && w_im < (float)W;
+    const float hlf = st.inside ? floorf(h_im) : 0.0f;
+    const float wlf = st.inside ? floorf(w_im) : 0.0f;
+    const int h_low = (int)hlf, w_low = (int)wlf;
+    st.lh = st.inside ? h_im - hlf : 0.0f;
+    st.lw = st.inside ? w_im - wlf : 0.0f;
+    st.hh = 1.0f - st.lh;
+    st.hw = 1.0f - st.lw;
+    const int hs[4] = {h_low, h_low, h_low + 1, h_low + 1};
+    const int ws[4] = {w_low, w_low + 1, w_low, w_low + 1};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = st.inside && hs[i] >= 0 && hs[i] <= H - 1 && ws[i] >= 0 && ws[i] <= W - 1;
+        st.row[i] = ok ? start + hs[i] * W + ws[i] : -1;
+    }
+    const float m = st.inside ? 1.0f : 0.0f;
+    st.cw[0] = m * st.hh * st.hw;
+    st.cw[1] = m * st.hh * st.lw;
+    st.cw[2] = m * st.lh * st.hw;
+    st.cw[3] = m * st.lh * st.lw;
+    return st;
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// Launch-shape bookkeeping common to the per-anchor kernels: one workgroup per
+// (batch, anchor); row group rg = L consecutive lanes.
+struct AnchorCtx {
+    int64_t ba, b;
+    int tid, nthreads, wave, lane, L, spw, rg, n_rg, li;
+};
+
+__device__ __forceinline__ AnchorCtx anchor_ctx(const KArgs& a) {
+    AnchorCtx c;
+    c.ba = blockIdx.x;
+    c.b = (int64_t)(blockIdx.x / (uint32_t)a.A);
+    c.tid = threadIdx.x;
+    c.nthreads = blockDim.x;
+    c.wave = c.tid / kWave;
+    c.lane = c.tid % kWave;
+    c.L = a.L;
+    c.spw = kWave >> a.log2L;
+    c.rg = c.wave * c.spw + (c.lane >> a.log2L);
+    c.n_rg = (c.nthreads / kWave) * c.spw;
+    c.li = c.lane & (c.L - 1);
+    return c;
+}
+
+}  // namespace da

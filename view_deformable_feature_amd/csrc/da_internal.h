@@ -1,7 +1,8 @@
 // Internal launch description shared by the host API (da_api.cpp) and the
-// gfx950 kernels (da_kernels.hip).  Not part of the public ABI.
+// gfx950 kernels (da_forward.hip, da_backward.hip).  Not part of the public ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -13,6 +14,24 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kMaxWaves = 8;       // waves per workgroup (512 threads)
 constexpr int kLdsBudget = 48 * 1024;
 
+// Scan of the per-row entry counts: one workgroup per tile of kScanTile rows.
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kScanThreads * kScanItems;   // 4096
+// Levels with at most this many rows are counted in an LDS histogram first.
+constexpr int kCountLdsRows = 4096;
+// Entries summed by one wave of the feature-gradient gather.
+constexpr int kGatherChunk = 128;
+
+// One (sample, corner) contribution to the feature gradient, bucketed by row.
+struct Entry {
+    uint32_t row;      // flat row b * num_feat + r
+    uint32_t sample;   // flat sample ((b*A + a) * P*K + pk) * S + s
+    float cw;          // bilinear corner weight
+    uint32_t ba;       // flat anchor b*A + a
+};
+static_assert(sizeof(Entry) == 16, "Entry layout");
+
 // (H, W, first row) of every (camera, scale) level, camera-major.
 struct LevelTable {
     int32_t H[kMaxLevels];
@@ -20,7 +39,7 @@ struct LevelTable {
     int32_t start[kMaxLevels];
 };
 
-// Everything a forward or backward launch needs.  One workgroup handles one
+// Everything a launch needs.  The per-anchor kernels run one workgroup per
 // (batch, anchor); its waves split the anchor's samples.  Inside a wave, a
 // "row group" of L lanes (L a power of two, 64 / L row groups per wave) reads
 // one feature row: lane li covers vectors li, li + L, li + 2L, ... of VEC
@@ -34,29 +53,44 @@ struct KArgs {
     float* grad_feat;          // [bs, num_feat, C]
     float* grad_loc;           // [bs, A, P, K, 2]
     float* grad_weights;       // [bs, A, P, K, S, G]
+    // feature-gradient gather workspace
+    uint32_t* cnt;             // [n_rows] entries per row, then per-row rank source
+    uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile
+    uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
+    uint32_t* rank;            // [4 * n_samples] rank of (sample, corner) inside its row
+    Entry* entries;            // [4 * n_samples] row-sorted entries
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
     uint32_t gfeat_image_bytes;
+    uint32_t n_rows;           // bs * num_feat
+    uint32_t n_samples;        // bs * A * P * K * S
+    uint32_t n_anchors;        // bs * A
+    uint32_t n_tiles;          // ceil(n_rows / kScanTile)
+    int32_t num_feat;
     int32_t A, C, P, K, S, G, D;   // D = C / G
     int32_t npk;               // P * K (point, camera) pairs per anchor
     int32_t pk_chunk;          // pairs staged in LDS at once
     int32_t L, log2L;          // lanes per row group
     int32_t nv;                // vectors per lane over all channels: C / (L * VEC)
-    int32_t nv_chunk;          // vectors per lane handled by one workgroup (grid.y splits C)
+    int32_t nv_chunk;          // vectors per lane handled by one workgroup (a divisor of nv;
+                               // grid.y = nv / nv_chunk splits the channels)
     int32_t row_bytes;         // C * elem
     int32_t grow_bytes;        // C * 4
     int32_t seg;               // backward: group-reduction segment (lanes), see kernels
+    int32_t gather_vec;        // feature-gradient gather: channels per lane vector (1 or 4)
+    int32_t accumulate;        // feature-gradient gather: add to grad_feat instead of overwrite
     LevelTable lv;
 };
 
 // Launch shapes chosen by the host.
 struct LaunchShape {
     int vec;            // channels per lane vector (1, 4 for f32 / 8 for bf16)
-    int nvc;            // compile-time vectors per lane (1, 2, 4, 8, 16)
+    int nvc;            // compile-time vectors per lane (forward 1..8, backward 1..16)
     int waves;          // waves per workgroup
     int chunks;         // grid.y
     size_t lds_bytes;   // dynamic LDS
+    int gather_nv;      // feature-gradient gather: vectors per lane (1, 2, 4, 8, 16)
 };
 
 // Sizes of the per-sample descriptors kept in LDS.
@@ -65,8 +99,13 @@ constexpr int kBwdDescBytes = 80;   // 4 feat offsets + 4 grad offsets + 3 x 4 c
 
 hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                           bool bf16, hipStream_t stream);
-hipError_t launch_backward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                           bool bf16, hipStream_t stream);
-hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+// Backward, scatter form: grad_feat must already hold zeros (or the sum to add to).
+hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
+                                   bool bf16, hipStream_t stream);
+// Backward, gather form: count, scan, per-anchor pass (location / weight
+// gradients and entry fill), then the row-parallel feature-gradient gather.
+hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
+                                  bool bf16, hipStream_t stream);
+hipError_t launch_fill_zero(void* p, int64_t n_words, hipStream_t stream);
 
 }  // namespace da
