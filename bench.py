@@ -2,15 +2,17 @@
 """Benchmark of deformable aggregation on one MI355X.
 
 One step = one pass of the whole hot path on one batch: da_forward then
-da_backward (which zero-fills grad_feat and scatters into it) on the
-nuScenes-shaped workload (bs=1, 6 cameras, 4 scales 64x176 / 32x88 / 16x44 /
+da_backward (location, weight and feature gradients, the latter gathered per
+feature row through a caller-side workspace) on the nuScenes-shaped workload (bs=1, 6 cameras, 4 scales 64x176 / 32x88 / 16x44 /
 8x22, C=256, G=8, 900 anchors, 13 keypoints), inputs resident in HBM.
 
 Prints ONE JSON line.  value = bilinear sample-channels per second over
 forward + backward (bs*A*P*K*S*C per step / step time).  The roofline
 entries use the algorithmic bytes of each direction (feature rows of the
 four corners, locations, weights, outputs; backward also the feature-gradient
-atomic payload) over the HIP-event time of that call.  cpu_baseline is the
+payload of every (sample, corner, channel) term) over the HIP-event time of
+that call; traffic is the counter-measured HBM bytes of the same call from
+profiles/traffic_nuscenes.json while the kernel sources are unchanged.  cpu_baseline is the
 plain fp64 C oracle, single-threaded, on the same workload.
 """
 from __future__ import annotations
@@ -28,6 +30,48 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nuscenes.json")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counter-derived traffic is reported only for the
+    kernels it was measured on."""
+    import hashlib
+    from view_deformable_feature_amd.build import HEADERS, SOURCES
+    h = hashlib.sha256()
+    for f in sorted(SOURCES + HEADERS):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per call from the committed rocprofv3 counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of known size, to scale the FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+
+
+FWD_KERNEL = "da_forward_kernel"
+BWD_KERNELS = ("da_backward call: fill_zero x2, count_kernel, scan_tiles_kernel, "
+               "scan_tile_totals_kernel, da_backward_anchor_kernel, gather_kernel")
 
 
 def algorithmic_bytes(wl):
@@ -70,6 +114,8 @@ def main():
                     help="workload name (nuscenes_bwd is the headline one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -78,6 +124,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import view_deformable_feature_amd as vdf
     from view_deformable_feature_amd import workloads as W
@@ -130,10 +180,15 @@ def main():
     fwd_s, bwd_s = float(t_fwd.mean()), float(t_bwd.mean())
     dominant = "backward" if bwd_s >= fwd_s else "forward"
 
-    def roof(bytes_, secs, kernel):
+    traffic = measured_traffic(wl.name)
+
+    def roof(bytes_, secs, kernel, direction):
         a = bytes_ / secs / 1e9
+        t = None
+        if traffic is not None and direction in traffic:
+            t = int(traffic[direction]["fetch_bytes"] + traffic[direction]["write_bytes"])
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": t, "kernel": kernel,
                 "algorithmic_bytes": int(bytes_), "avg_launch_us": round(secs * 1e6, 2)}
 
     rec = {
@@ -156,9 +211,9 @@ def main():
                    "sample_channels_per_step": sc},
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
-        "roofline": roof(b_bwd, bwd_s, "da_backward (zero fill + scatter kernel)")
-        if dominant == "backward" else roof(b_fwd, fwd_s, "da_forward_kernel"),
-        "roofline_forward": roof(b_fwd, fwd_s, "da_forward_kernel"),
+        "roofline": roof(b_bwd, bwd_s, BWD_KERNELS, "backward")
+        if dominant == "backward" else roof(b_fwd, fwd_s, FWD_KERNEL, "forward"),
+        "roofline_forward": roof(b_fwd, fwd_s, FWD_KERNEL, "forward"),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
