@@ -125,7 +125,8 @@ da_status da_forward(const da_problem* problem,
  * da_backward_workspace_size -- bytes of device workspace da_backward and
  * da_backward_accumulate need for `problem` (0 when there is no sample).  Only the
  * sizes in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
- * >= 2^32 or the sample count bs*A*P*K*S >= 2^30 (da_backward_atomic still works).
+ * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
+ * 2^32 - 1 bytes (da_backward_atomic still works).
  */
 da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
 

@@ -350,3 +350,13 @@ def test_workspace_reused_across_calls():
         assert_close("ws grad_feat", gf, r_gf, TOL_BWD)
         assert_close("ws grad_loc", gl, r_gl, TOL_BWD)
         assert_close("ws grad_weights", gw, r_gw, TOL_BWD)
+
+
+def test_hot_rows_span_many_chunks():
+    """A 2x3 level hit by 4000 samples: each of its rows collects thousands of
+    feature-gradient terms, far more than one wave's chunk of the row-sorted list,
+    next to a large level with a few terms per row."""
+    wl = W.custom("hot_rows", bs=2, num_cams=2, levels=((2, 3), (40, 60)), C=64, groups=4,
+                  anchors=250, pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)
+    inp = W.make_inputs(wl)
+    _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows")

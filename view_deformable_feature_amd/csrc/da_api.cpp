@@ -276,7 +276,15 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
 da_status gather_sizes(const da_problem* p, uint64_t& n_rows, uint64_t& n_samples) {
     n_rows = (uint64_t)p->bs * (uint64_t)p->num_feat;
     n_samples = (uint64_t)p->bs * p->num_anchors * p->num_pts * p->num_cams * p->num_scale;
-    if (n_rows >= (1ull << 32) || n_samples >= (1ull << 30))
+    // the gather reads grad_out and weights through 32-bit buffer offsets
+    const uint64_t go_bytes = (uint64_t)p->bs * p->num_anchors * p->num_embeds * 4;
+    const uint64_t w_bytes = n_samples * (uint64_t)p->num_groups * 4;
+    if (go_bytes > kU32Max || w_bytes > kU32Max)
+        return fail(DA_ERR_UNSUPPORTED,
+                    "backward: grad_out (%llu bytes) or weights (%llu bytes) exceed 4 GiB for the "
+                    "gather workspace (use da_backward_atomic)",
+                    (unsigned long long)go_bytes, (unsigned long long)w_bytes);
+    if (n_rows >= (1ull << 31) || n_samples >= (1ull << 30))
         return fail(DA_ERR_UNSUPPORTED,
                     "backward: bs * num_feat (%llu) or the sample count (%llu) is too large for the "
                     "gather workspace (use da_backward_atomic)",
@@ -338,7 +346,10 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             if (ka.gather_vec == 4 && !aligned(grad_feat, 16)) ka.gather_vec = 1;
         }
     }
-    if (mode != BwdMode::kGatherAccumulate && p->bs > 0) {
+    // the scatter form adds into zeros; the gather form zeroes only the rows no
+    // sample touches (inside launch_backward_gather), unless nothing is sampled
+    const bool full_fill = mode == BwdMode::kScatter || (mode == BwdMode::kGather && !any_sample);
+    if (full_fill && p->bs > 0) {
         st = hip_status(da::launch_fill_zero(grad_feat, p->bs * p->num_feat * p->num_embeds, s),
                         "grad_feat zero fill");
         if (st != DA_OK) return st;

@@ -19,10 +19,11 @@
 //               the forward does, reduces the location and weight gradients
 //               across lanes (stored once, no atomics) and writes each
 //               (sample, corner) entry into its row's bucket;
-//   4. gather:  each wave sums a fixed-size chunk of the row-sorted entries,
-//               lanes over channels, and writes every row it owns with a plain
-//               store; only a row split between two chunks is added with
-//               atomics (at most two per chunk).
+//   4. gather:  each wave owns the short rows whose first entry falls in its
+//               64-entry range of the row-sorted list and writes each once with
+//               plain stores (lanes over channels); the few long rows are added
+//               range by range with atomics; rows with no entry are zeroed by a
+//               separate pass.
 // The scatter form (binary32 atomics straight into the feature gradient) is
 // kept for callers that cannot provide the workspace.
 
@@ -153,10 +154,11 @@ da_backward_anchor_kernel(KArgs a) {
                         const uint32_t flat_row =
                             (uint32_t)b * (uint32_t)a.num_feat + (uint32_t)st.row[i];
                         Entry e;
-                        e.row = flat_row;
-                        e.sample = q;
+                        e.row = flat_row |
+                                (a.cnt[flat_row] > (uint32_t)kGatherLong ? kEntryLongRow : 0u);
+                        e.w_off = q * (uint32_t)a.G * 4u;
                         e.cw = st.cw[i];
-                        e.ba = (uint32_t)ba;
+                        e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u;
                         const uint32_t pos = row_first_entry(a, flat_row) + rks[i];
                         if (pos < 4u * a.n_samples) a.entries[pos] = e;
                     }
@@ -405,120 +407,250 @@ __global__ void __launch_bounds__(1024) scan_tile_totals_kernel(KArgs a) {
     if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry_s;
 }
 
-// Each wave sums entries [e0, e0 + kGatherChunk) of the row-sorted list.  A row
-// whose entries all lie in the chunk is written with plain stores (or added
-// to, when accumulating); a row cut by the chunk boundary is added with
-// atomics onto the zero-filled (or existing) gradient.
+// Each wave covers the range [e0, e0 + kGatherChunk) of the row-sorted entry
+// list.  A row with at most kGatherLong entries is owned by the wave whose
+// range holds its first entry: that wave follows it past the range end and
+// writes it once with plain stores (or adds to it, when accumulating), so the
+// sum of a short row needs no atomic.  A longer row (the coarse levels'
+// rows, hit by hundreds of samples) is summed range by range and each range's
+// partial sum is added with atomics onto the pre-zeroed row; this keeps every
+// wave's walk under 2 * kGatherChunk entries instead of letting one wave walk
+// a whole hot row.
+//
+// The walk is scalar work per entry (the wave moves through the entries one at
+// a time, lanes over channels), and the scalar unit is shared by the whole
+// compute unit, so it is kept to a few instructions per entry: the entries
+// (two windows of 64) sit in lane registers and are read back with readlane;
+// they carry ready byte offsets; grad_out rows and weights are read through
+// buffer resources with a scalar offset; the walk is split into the entries
+// inside the range (only a row-change test each) and a tail (the rest of a
+// short row that crosses the range end).  Batches of U entries are issued one
+// batch ahead of the one being added up.
 template <int VEC, int NV>
 __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
-    constexpr int U = 4;   // entries in flight per wave
-    const uint32_t total = min(a.tile_prefix[a.n_tiles], 4u * a.n_samples);
-    const uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    constexpr int U = NV >= 8 ? 1 : 8 / NV;   // entries per batch, within the register budget
+    constexpr uint32_t kNone = 0xffffffffu;
+    static_assert(kGatherChunk == kWave && kGatherLong <= kGatherChunk, "window layout");
+    static_assert(kWave % U == 0, "batches tile a window");
+    // Every value the walk branches on is wave-uniform; readfirstlane says so,
+    // so that the loops below run on scalar branches.
+    auto uni = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); };
+    const uint32_t total = uni(min(a.tile_prefix[a.n_tiles], 4u * a.n_samples));
+    const uint32_t w = uni((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
     const int lane = threadIdx.x % kWave;
     const uint32_t e0 = w * (uint32_t)kGatherChunk;
     if (e0 >= total) return;
-    const uint32_t e1 = min(e0 + (uint32_t)kGatherChunk, total);
-    const int C = a.C, G = a.G;
+    const int n1 = (int)(min(e0 + (uint32_t)kGatherChunk, total) - e0);   // entries in range
+    const int C = a.C;
+    const uint32_t go_bytes = a.n_anchors * (uint32_t)C * 4u;
+    const uint32_t w_bytes = a.n_samples * (uint32_t)a.G * 4u;
+
+    // 64 consecutive entries, one per lane; past the end the row is kNone.  An
+    // entry that is out of range anyway (a workspace shared by overlapping
+    // calls) is read as a zero-weight term of row 0.
+    auto load_window = [&](uint32_t base) -> uint4 {
+        const uint32_t e = base + (uint32_t)lane;
+        uint4 v = make_uint4(kNone, 0u, 0u, 0u);
+        if (e < total) {
+            v = *reinterpret_cast<const uint4*>(a.entries + e);
+            if ((v.x & ~kEntryLongRow) >= a.n_rows || v.y >= w_bytes || v.w >= go_bytes)
+                v = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return v;
+    };
+    const uint4 win0 = load_window(e0);
+    const uint4 win1 = load_window(e0 + (uint32_t)kWave);
+    const uint32_t before = (e0 == 0) ? kNone : uni(a.entries[e0 - 1].row);
+
+    // where this wave starts: at e0, unless the row there began earlier and is
+    // short (then its owner covers it) -- then at the first row start in range.
+    // The shuffle runs on all lanes before the select: executed only by lanes
+    // != 0 it would read lane 0 as inactive, i.e. as 0.
+    const uint32_t up0 = (uint32_t)__shfl_up((int)win0.x, 1, kWave);
+    const uint32_t prev0 = lane == 0 ? before : up0;
+    const uint64_t starts = __ballot(lane < n1 && win0.x != prev0);
+    const uint32_t row_at_e0 = (uint32_t)__builtin_amdgcn_readlane((int)win0.x, 0);
+    int sp = 0;
+    if (before == row_at_e0 && !(row_at_e0 & kEntryLongRow)) {
+        if (starts == 0) return;            // the whole range continues a short row owned earlier
+        sp = __ffsll((unsigned long long)starts) - 1;
+    }
+    uint32_t cur = (uint32_t)__builtin_amdgcn_readlane((int)win0.x, sp);
+
     const int nvec = C / VEC;
-    bool on[NV];
-    int gi[NV];
+    int vv[NV];
+    uint32_t lo_go[NV], lo_w[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int v = lane + kWave * i;
-        on[i] = v < nvec;
-        gi[i] = on[i] ? v * VEC / a.D : 0;
+        vv[i] = v < nvec ? v : 0;
+        lo_go[i] = (uint32_t)(vv[i] * VEC * 4);
+        lo_w[i] = (uint32_t)(vv[i] * VEC / a.D * 4);
     }
-    const Entry* ent = a.entries;
-    uint32_t cur = ent[e0].row;
-    bool cur_whole_start = (e0 == 0) || ent[e0 - 1].row != cur;
-    if (cur >= a.n_rows) cur = 0u;   // out-of-range entries are read as row 0 (see below)
+    const __amdgpu_buffer_rsrc_t r_go = make_rsrc(a.grad_out, go_bytes);
+    const __amdgpu_buffer_rsrc_t r_w = make_rsrc(a.weights, w_bytes);
+
     float acc[NV][VEC];
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[i][j] = 0.0f;
+        for (int k = 0; k < VEC; ++k) acc[i][k] = 0.0f;
 
-    auto flush = [&](uint32_t row, bool whole) {
-        float* dst = a.grad_feat + (size_t)row * C;
+    // Write (or add) the row's sum through a buffer resource that spans exactly
+    // that row: lanes past its last vector fall outside the range and their
+    // stores / atomics are dropped by the hardware, so no lane-dependent branch
+    // enters the walk (it would turn every exit of the loops into exec-masked
+    // code).
+    auto flush = [&](uint32_t row_bits) {
+        const uint32_t row = row_bits & ~kEntryLongRow;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.grad_feat + (size_t)row * C, (uint32_t)C * 4u);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            if (!on[i]) continue;
-            float* p = dst + (lane + kWave * i) * VEC;
-            if (whole) {
-                if constexpr (VEC == 4) {
-                    float4 o = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-                    if (a.accumulate) {
-                        const float4 old = *reinterpret_cast<const float4*>(p);
-                        o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-                    }
-                    *reinterpret_cast<float4*>(p) = o;
-                } else {
+            const uint32_t off = (uint32_t)((lane + kWave * i) * VEC * 4);
+            if (row_bits & kEntryLongRow) {
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) p[j] = a.accumulate ? p[j] + acc[i][j] : acc[i][j];
-                }
+                for (int k = 0; k < VEC; ++k)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][k], r, off + 4u * k, 0, 0);
             } else {
+                float o[VEC];
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) unsafeAtomicAdd(p + j, acc[i][j]);
+                for (int k = 0; k < VEC; ++k) o[k] = acc[i][k];
+                if (a.accumulate) {
+                    float old[VEC];
+                    VecLoad<float, VEC>::run(r, off, 0u, old);
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) o[k] += old[k];
+                }
+                if constexpr (VEC == 4) {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                                           make_float4(o[0], o[1], o[2], o[3])),
+                        r, off, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[0]), r, off, 0, 0);
+                }
             }
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[i][j] = 0.0f;
+            for (int k = 0; k < VEC; ++k) acc[i][k] = 0.0f;
         }
     };
 
-    for (uint32_t e = e0; e < e1; e += U) {
-        Entry en[U];
-        float gov[U][NV][VEC];
-        float wv[U][NV];
+    struct Batch {
+        uint32_t row[U];
+        float cw[U];
+        float go[U][NV][VEC];
+        float wt[U][NV];
+    };
+    // entries at positions p0 .. p0+U-1 of window `win` (p0 a multiple of U)
+    auto issue = [&](const uint4& win, int p0, Batch& B) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            en[u] = ent[min(e + u, e1 - 1)];
-            // every slot below the total was filled by the anchor pass; an entry
-            // that is out of range anyway (a workspace shared by overlapping
-            // calls) is read as a zero-weight term of row 0
-            if (en[u].row >= a.n_rows || en[u].ba >= a.n_anchors || en[u].sample >= a.n_samples) {
-                en[u].row = 0u;
-                en[u].ba = 0u;
-                en[u].sample = 0u;
-                en[u].cw = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float* gorow = a.grad_out + (size_t)en[u].ba * C;
-            const float* wrow = a.weights + (size_t)en[u].sample * G;
+            const int idx = p0 + u;
+            B.row[u] = (uint32_t)__builtin_amdgcn_readlane((int)win.x, idx);
+            const uint32_t wo = (uint32_t)__builtin_amdgcn_readlane((int)win.y, idx);
+            B.cw[u] = __int_as_float(__builtin_amdgcn_readlane((int)win.z, idx));
+            const uint32_t go = (uint32_t)__builtin_amdgcn_readlane((int)win.w, idx);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int v = on[i] ? lane + kWave * i : 0;
-                if constexpr (VEC == 4) {
-                    const float4 g4 = *reinterpret_cast<const float4*>(gorow + v * 4);
-                    gov[u][i][0] = g4.x;
-                    gov[u][i][1] = g4.y;
-                    gov[u][i][2] = g4.z;
-                    gov[u][i][3] = g4.w;
-                } else {
-                    gov[u][i][0] = gorow[v];
+                VecLoad<float, VEC>::run(r_go, lo_go[i], go, B.go[u][i]);
+                B.wt[u][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_w, lo_w[i], wo, 0));
+            }
+        }
+    };
+    auto add = [&](const Batch& B, int u) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float sc = B.cw[u] * B.wt[u][i];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[i][k] += sc * B.go[u][i][k];
+        }
+    };
+
+    // phase 1: positions sp .. n1-1 of win0; a row change flushes the finished row
+    Batch A, B;
+    {
+        const int first = sp - sp % U;
+        int p = first;
+        issue(win0, p, A);
+        while (true) {
+            const int pn = min(p + U, kWave - U);
+            issue(win0, pn, B);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int pos = p + u;
+                if (pos >= sp && pos < n1) {
+                    if (A.row[u] != cur) {
+                        flush(cur);
+                        cur = A.row[u];
+                    }
+                    add(A, u);
                 }
-                wv[u][i] = wrow[gi[i]];
             }
+            p += U;
+            if (p >= n1) break;
+            const int pn2 = min(p + U, kWave - U);
+            issue(win0, pn2, A);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int pos = p + u;
+                if (pos < n1) {
+                    if (B.row[u] != cur) {
+                        flush(cur);
+                        cur = B.row[u];
+                    }
+                    add(B, u);
+                }
+            }
+            p += U;
+            if (p >= n1) break;
         }
+    }
+    // phase 2: a short row that runs past the range end is finished here (it can
+    // only continue into win1: a range that ends early ends at the last entry)
+    if (n1 == kWave && !(cur & kEntryLongRow)) {
+        bool done = false;
+        for (int p = 0; p < kWave && !done; p += U) {
+            issue(win1, p, A);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (e + u >= e1) break;
-            if (en[u].row != cur) {
-                flush(cur, cur_whole_start);
-                cur = en[u].row;
-                cur_whole_start = true;
-            }
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const float s = en[u].cw * wv[u][i];
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) acc[i][j] += s * gov[u][i][j];
+            for (int u = 0; u < U; ++u) {
+                if (!done) {
+                    if (A.row[u] != cur) {   // row ended (kNone past the last entry)
+                        done = true;
+                    } else {
+                        add(A, u);
+                    }
+                }
             }
         }
     }
-    const bool ends_here = (e1 == total) || ent[e1].row != cur;
-    flush(cur, cur_whole_start && ends_here);
+    flush(cur);
+}
+
+// Rows no sample touches, and the long rows that gather_kernel adds to piece
+// by piece: zero them (short rows are written whole by gather_kernel).  One
+// wave per 64 rows.
+template <int VEC>
+__global__ void __launch_bounds__(256) zero_empty_rows_kernel(KArgs a) {
+    const uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int lane = threadIdx.x % kWave;
+    const uint32_t r0 = w * (uint32_t)kWave;
+    if (r0 >= a.n_rows) return;
+    const uint32_t r = r0 + (uint32_t)lane;
+    // rows with no entry, and the long rows gather_kernel adds to piece by piece
+    const bool empty = r < a.n_rows && (a.cnt[r] == 0u || a.cnt[r] > (uint32_t)kGatherLong);
+    uint64_t m = __ballot(empty);
+    const int nvec = a.C / VEC;
+    while (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        float* row = a.grad_feat + (size_t)(r0 + (uint32_t)l) * a.C;
+        for (int v = lane; v < nvec; v += kWave) {
+            if constexpr (VEC == 4)
+                reinterpret_cast<float4*>(row)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                row[v] = 0.0f;
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -587,12 +719,23 @@ hipError_t anchor_dispatch_vec(const KArgs& a, const LaunchShape& s, dim3 grid, 
 
 template <int VEC>
 hipError_t gather_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    // C <= 1024 in the backward: 16-byte vectors need at most 4 per lane
     switch (s.gather_nv) {
         case 1: hipLaunchKernelGGL((gather_kernel<VEC, 1>), grid, dim3(256), 0, st, a); break;
         case 2: hipLaunchKernelGGL((gather_kernel<VEC, 2>), grid, dim3(256), 0, st, a); break;
         case 4: hipLaunchKernelGGL((gather_kernel<VEC, 4>), grid, dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((gather_kernel<VEC, 8>), grid, dim3(256), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((gather_kernel<VEC, 16>), grid, dim3(256), 0, st, a); break;
+        case 8:
+            if constexpr (VEC == 1) {
+                hipLaunchKernelGGL((gather_kernel<1, 8>), grid, dim3(256), 0, st, a);
+                break;
+            }
+            return hipErrorInvalidValue;
+        case 16:
+            if constexpr (VEC == 1) {
+                hipLaunchKernelGGL((gather_kernel<1, 16>), grid, dim3(256), 0, st, a);
+                break;
+            }
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -634,6 +777,15 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_tile_totals_kernel, dim3(1), dim3(1024), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.accumulate) {
+        const int64_t zwaves = ((int64_t)a.n_rows + kWave - 1) / kWave;
+        const dim3 zgrid(blocks_for(zwaves, 256 / kWave));
+        if (a.gather_vec == 4)
+            hipLaunchKernelGGL((zero_empty_rows_kernel<4>), zgrid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((zero_empty_rows_kernel<1>), zgrid, dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const dim3 grid((unsigned)n_anchors_total, 1);
     if (bf16)
         e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(a, s, grid, stream)

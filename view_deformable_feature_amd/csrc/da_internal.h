@@ -20,17 +20,22 @@ constexpr int kScanItems = 16;
 constexpr int kScanTile = kScanThreads * kScanItems;   // 4096
 // Levels with at most this many rows are counted in an LDS histogram first.
 constexpr int kCountLdsRows = 4096;
-// Entries summed by one wave of the feature-gradient gather.
-constexpr int kGatherChunk = 128;
+// Entries covered by one wave of the feature-gradient gather, and the longest
+// row a single wave sums whole (longer rows are added range by range).
+constexpr int kGatherChunk = 64;
+constexpr int kGatherLong = 64;
 
 // One (sample, corner) contribution to the feature gradient, bucketed by row.
+// Offsets are stored in bytes so that the gather does no index arithmetic.
 struct Entry {
-    uint32_t row;      // flat row b * num_feat + r
-    uint32_t sample;   // flat sample ((b*A + a) * P*K + pk) * S + s
+    uint32_t row;      // flat row b * num_feat + r; bit 31 set when the row is long
+                       // (more than kGatherLong entries: summed range by range)
+    uint32_t w_off;    // byte offset of the sample's weight row: sample * G * 4
     float cw;          // bilinear corner weight
-    uint32_t ba;       // flat anchor b*A + a
+    uint32_t go_off;   // byte offset of the anchor's grad_out row: (b*A + a) * C * 4
 };
 static_assert(sizeof(Entry) == 16, "Entry layout");
+constexpr uint32_t kEntryLongRow = 0x80000000u;
 
 // (H, W, first row) of every (camera, scale) level, camera-major.
 struct LevelTable {
