@@ -69,9 +69,10 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
-FWD_KERNEL = "da_forward_kernel"
-BWD_KERNELS = ("da_backward call: fill_zero x2, count_kernel, scan_tiles_kernel, "
-               "scan_tile_totals_kernel, da_backward_anchor_kernel, gather_kernel")
+FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
+BWD_KERNELS = ("da_backward call: fill_zero_kernel, count_kernel, scan_tiles_kernel, "
+               "zero_empty_rows_kernel, da_backward_sliced_kernel, "
+               "loc_reduce_kernel, gather_kernel")
 
 
 def algorithmic_bytes(wl):
@@ -148,15 +149,19 @@ def main():
     gf = torch.empty(tuple(feat.shape), device=dev, dtype=torch.float32)
     gl = torch.empty(tuple(loc.shape), device=dev, dtype=torch.float32)
     gw = torch.empty(tuple(w.shape), device=dev, dtype=torch.float32)
+    # caller-owned workspaces, allocated once, as a training loop would hold them
+    fws_n = vdf.forward_workspace_size(feat, shape, loc, w)
+    fws = torch.empty(fws_n, device=dev, dtype=torch.uint8) if fws_n else None
+    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w), device=dev, dtype=torch.uint8)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        vdf.da_forward(feat, shape, start, loc, w, out=out)
+        vdf.da_forward(feat, shape, start, loc, w, out=out, workspace=fws)
         if ev is not None:
             ev[1].record()
         vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
-                        grad_weights=gw)
+                        grad_weights=gw, workspace=bws)
         if ev is not None:
             ev[2].record()
 
@@ -212,8 +217,8 @@ def main():
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
         "roofline": roof(b_bwd, bwd_s, BWD_KERNELS, "backward")
-        if dominant == "backward" else roof(b_fwd, fwd_s, FWD_KERNEL, "forward"),
-        "roofline_forward": roof(b_fwd, fwd_s, FWD_KERNEL, "forward"),
+        if dominant == "backward" else roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
+        "roofline_forward": roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

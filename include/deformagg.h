@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DA_VERSION 100         /* 1.0.0 */
+#define DA_VERSION 110         /* 1.1.0 */
 #define DA_MAX_LEVELS 64       /* num_cams * num_scale */
 #define DA_MAX_EXTENT 32768    /* H and W of every level */
 
@@ -75,6 +75,19 @@ typedef enum {
     DA_BF16 = 1                /* mc_ms_feat holds bfloat16 (raw 16-bit patterns) */
 } da_dtype;
 
+/*
+ * Level slices.  MI355X places workgroup i on accelerator die (XCD) i mod 8, and each
+ * die has its own 4 MiB L2.  When the features of one batch image exceed 8 MiB and the
+ * num_cams * num_scale levels split into 8 nearly equal shares (at least 8 levels, at
+ * most a quarter of the slots idle), the per-anchor kernels run 8 workgroups per anchor:
+ * workgroup (anchor, x) takes only the samples of the levels in slice x (levels dealt
+ * largest first, round-robin), so each die's L2 caches one eighth of the features.  The
+ * partial sums are then added in a fixed order, so results stay deterministic; they may
+ * differ from the unsliced kernels' in rounding.  These flags override the choice:
+ */
+#define DA_FLAG_SLICES_ALWAYS 1  /* slice whatever the sizes (where the lane layout allows) */
+#define DA_FLAG_SLICES_NEVER 2   /* one workgroup per anchor                                */
+
 /* Problem sizes.  bs, num_anchors and num_pts may be 0 (then there is nothing to
  * sample: out and grad_feat are filled with zeros).  All other sizes are >= 1,
  * num_embeds % num_groups == 0 and num_cams * num_scale <= DA_MAX_LEVELS. */
@@ -88,8 +101,15 @@ typedef struct {
     int64_t num_scale;    /* S                                             */
     int64_t num_groups;   /* G, weight groups over the channels            */
     int32_t feat_dtype;   /* da_dtype                                      */
-    int32_t reserved;     /* must be 0                                     */
+    int32_t flags;        /* 0 or one DA_FLAG_SLICES_* value               */
 } da_problem;
+
+/*
+ * da_forward_workspace_size -- bytes of device workspace that let da_forward use level
+ * slices for `problem`: 8 * bs * A * C * 4 when slices are wanted, else 0.  Only the
+ * sizes and flags in `problem` are read.
+ */
+da_status da_forward_workspace_size(const da_problem* problem, size_t* bytes);
 
 /*
  * da_forward -- the forward pass (sections 3.2 and 5.1).
@@ -104,9 +124,15 @@ typedef struct {
  *   sampling_location  device float [bs, A, P, K, 2], normalised (x, y); 8-byte aligned.
  *   weights            device float [bs, A, P, K, S, G]; 4-byte aligned.
  *   out                device float [bs, A, C], fully overwritten; 4-byte aligned.
+ *   workspace          NULL, or device scratch of at least da_forward_workspace_size()
+ *                      bytes, 256-byte aligned, owned by the caller (contents on entry do
+ *                      not matter; garbage on return).  With NULL the forward always runs
+ *                      one workgroup per anchor; with a workspace it uses level slices
+ *                      when they are wanted.  Overlapping calls must not share it.
  *
  * Returns DA_OK, DA_ERR_INVALID_ARG (null pointer where data is needed, misaligned
- * pointer, malformed sizes or level table), DA_ERR_UNSUPPORTED (one batch image of the
+ * pointer, malformed sizes, flags or level table, a misaligned or too small
+ * workspace), DA_ERR_UNSUPPORTED (one batch image of the
  * features -- or, in the backward, of the feature gradient -- plus two rows above
  * 2^32 - 1 bytes; num_embeds > 2^20; bs * A * 512 >= 2^32; one (point, camera) pair's
  * stencils and weights above 48 KiB of LDS; in the backward, num_embeds more than 16
@@ -119,12 +145,14 @@ da_status da_forward(const da_problem* problem,
                      const float* sampling_location,
                      const float* weights,
                      float* out,
+                     void* workspace,
+                     size_t workspace_bytes,
                      void* stream);
 
 /*
  * da_backward_workspace_size -- bytes of device workspace da_backward and
- * da_backward_accumulate need for `problem` (0 when there is no sample).  Only the
- * sizes in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
+ * da_backward_accumulate need for `problem` (0 when there is no sample): about
+ * 8 * bs * num_feat + 88 * bs*A*P*K*S.  Only the sizes in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */
@@ -145,7 +173,9 @@ da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
  *
  * The feature gradient is formed as a gather: every (sample, corner) term is first
  * bucketed by feature row, then each row is summed by one wave and stored, so almost
- * no floating-point atomics are issued.  The order in which a row's terms are added
+ * no floating-point atomics are issued.  The per-anchor pass uses level slices when
+ * they are wanted (see DA_FLAG_SLICES_ALWAYS); the workspace then also holds every
+ * sample's location-gradient partial.  The order in which a row's terms are added
  * depends on the order integer atomics retire in, so grad_feat may differ in rounding
  * from run to run; grad_loc and grad_weights are deterministic.
  * Same errors as da_forward, plus DA_ERR_INVALID_ARG for a missing, misaligned or too

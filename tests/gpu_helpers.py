@@ -38,29 +38,26 @@ def to_device(inp, device="cuda"):
     return d
 
 
-def gpu_forward(dev):
+def gpu_forward(dev, slices=None, workspace=None):
+    """slices: None = the library's choice, True / False = level slices forced on / off."""
     import view_deformable_feature_amd as vdf
     out = vdf.da_forward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                         dev["loc"], dev["weights"])
+                         dev["loc"], dev["weights"], workspace=workspace, slices=slices)
     torch.cuda.synchronize()
     return out
 
 
-def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None):
+def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices=None):
     import view_deformable_feature_amd as vdf
+    args = (dev["feat"], dev["spatial_shape"], dev["scale_start_index"], dev["loc"],
+            dev["weights"], dev["grad_out"])
     if atomic:
-        r = vdf.da_backward_atomic(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                                   dev["loc"], dev["weights"], dev["grad_out"])
-    elif workspace is not None:
-        r = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                            dev["loc"], dev["weights"], dev["grad_out"], workspace=workspace)
+        r = vdf.da_backward_atomic(*args)
     elif accumulate_into is None:
-        r = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                            dev["loc"], dev["weights"], dev["grad_out"])
+        r = vdf.da_backward(*args, workspace=workspace, slices=slices)
     else:
-        r = vdf.da_backward_accumulate(dev["feat"], dev["spatial_shape"],
-                                       dev["scale_start_index"], dev["loc"], dev["weights"],
-                                       dev["grad_out"], accumulate_into)
+        r = vdf.da_backward_accumulate(*args, accumulate_into, workspace=workspace,
+                                       slices=slices)
     torch.cuda.synchronize()
     return r
 

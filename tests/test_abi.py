@@ -24,13 +24,14 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_functions()
     assert set(names) >= {"da_forward", "da_backward", "da_backward_accumulate",
                           "da_backward_atomic", "da_backward_workspace_size",
-                          "da_status_string", "da_last_error", "da_version"}
+                          "da_forward_workspace_size", "da_status_string", "da_last_error",
+                          "da_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in deformagg.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.da_version() == 100
+    assert lib.da_version() == 110
     for code in range(4):
         assert lib.da_status_string(code)
     assert b"unknown" in lib.da_status_string(99)
@@ -43,7 +44,7 @@ HOST_START = np.array([[0]], np.int32)
 
 def _prob(**kw):
     d = dict(bs=1, num_feat=256, num_embeds=32, num_anchors=8, num_pts=4, num_cams=1,
-             num_scale=1, num_groups=1, feat_dtype=0, reserved=0)
+             num_scale=1, num_groups=1, feat_dtype=0, flags=0)
     d.update(kw)
     return _lib.DAProblem(**d)
 
@@ -52,12 +53,13 @@ def _i32p(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _fwd(lib, prob, feat=FAKE, shape=HOST_SHAPE, start=HOST_START, loc=FAKE, w=FAKE, out=FAKE):
+def _fwd(lib, prob, feat=FAKE, shape=HOST_SHAPE, start=HOST_START, loc=FAKE, w=FAKE, out=FAKE,
+         ws=0, ws_bytes=0):
     vp = ctypes.c_void_p
     return lib.da_forward(ctypes.byref(prob) if prob is not None else None, vp(feat),
                           _i32p(shape) if shape is not None else None,
                           _i32p(start) if start is not None else None,
-                          vp(loc), vp(w), vp(out), None)
+                          vp(loc), vp(w), vp(out), vp(ws), ws_bytes, None)
 
 
 def _bwd(lib, prob, name="da_backward", feat=FAKE, loc=FAKE, w=FAKE, go=FAKE, gf=FAKE, gl=FAKE,
@@ -84,7 +86,9 @@ def _msg(lib):
     (dict(num_anchors=-2), 1, ">= 0"),
     (dict(num_pts=-1), 1, ">= 0"),
     (dict(feat_dtype=7), 1, "feat_dtype"),
-    (dict(reserved=1), 1, "reserved"),
+    (dict(flags=3), 1, "flags"),
+    (dict(flags=4), 1, "flags"),
+    (dict(flags=-1), 1, "flags"),
     (dict(num_feat=255), 1, "inside num_feat"),
     (dict(num_cams=9, num_scale=8), 1, "DA_MAX_LEVELS"),
 ])
@@ -118,7 +122,7 @@ def test_rejects_bad_level_table(lib, H, W, st, needle):
 
 def test_rejects_null_pointers(lib):
     p = _prob()
-    assert lib.da_forward(None, None, None, None, None, None, None, None) == 1
+    assert lib.da_forward(None, None, None, None, None, None, None, None, 0, None) == 1
     assert "problem is NULL" in _msg(lib)
     assert _fwd(lib, p, shape=None) == 1
     assert _fwd(lib, p, feat=0) == 1 and "mc_ms_feat" in _msg(lib)
@@ -195,9 +199,10 @@ def test_workspace_size_and_checks(lib):
     n = ctypes.c_size_t(0)
     p = _prob()
     assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
-    # counts + local prefix + tile prefix + ranks + 16-byte entries, each 256-aligned
+    # scan counter + counts + local prefix + tile prefix + ranks + 16-byte entries + location
+    # partials, each 256-aligned
     n_rows, n_samples = 256, 8 * 4
-    expect = 2 * 1024 + 256 + 512 + n_samples * 4 * 16
+    expect = 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256
     assert n.value == expect
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_pts=0)), ctypes.byref(n)) == 0
     assert n.value == 0
@@ -209,3 +214,40 @@ def test_workspace_size_and_checks(lib):
         assert _bwd(lib, p, name, ws=0) == 1 and "workspace is NULL" in _msg(lib)
         assert _bwd(lib, p, name, ws=FAKE + 16) == 1 and "256-byte" in _msg(lib)
         assert _bwd(lib, p, name, ws_bytes=expect - 1) == 1 and "needed" in _msg(lib)
+
+
+def _fws(lib, prob):
+    n = ctypes.c_size_t(123)
+    assert lib.da_forward_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_forward_workspace_size_follows_the_slicing_rule(lib):
+    # nuScenes-shaped: 6 cameras x 4 scales, 89,760 rows of 256 floats (92 MB)
+    nus = dict(num_feat=89760, num_embeds=256, num_groups=8, num_anchors=900, num_pts=13,
+               num_cams=6, num_scale=4)
+    assert _fws(lib, _prob(**nus)) == 8 * 900 * 256 * 4
+    assert _fws(lib, _prob(bs=2, **nus)) == 8 * 2 * 900 * 256 * 4
+    assert _fws(lib, _prob(flags=2, **nus)) == 0                  # slices never
+    # features within twice one die's L2: no slices unless forced
+    assert _fws(lib, _prob(**dict(nus, num_feat=8000))) == 0
+    assert _fws(lib, _prob(flags=1, **dict(nus, num_feat=8000))) == 8 * 900 * 256 * 4
+    # 12 levels leave a third of the 16 slots idle; 20 leave a sixth
+    assert _fws(lib, _prob(**dict(nus, num_cams=3))) == 0
+    assert _fws(lib, _prob(**dict(nus, num_cams=5))) == 8 * 900 * 256 * 4
+    assert _fws(lib, _prob(**dict(nus, num_cams=1))) == 0         # 4 levels
+    assert _fws(lib, _prob(flags=1)) == 8 * 8 * 32 * 4            # forced, one level
+    assert _fws(lib, _prob()) == 0
+    assert _fws(lib, _prob(num_anchors=0, flags=1)) == 0
+    n = ctypes.c_size_t(0)
+    assert lib.da_forward_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.da_forward_workspace_size(ctypes.byref(_prob()), None) == 1
+
+
+def test_forward_workspace_checks(lib):
+    p = _prob(flags=1)
+    need = 8 * 8 * 32 * 4
+    assert _fwd(lib, p, ws=FAKE + 16, ws_bytes=need) == 1 and "256-byte" in _msg(lib)
+    assert _fwd(lib, p, ws=FAKE, ws_bytes=need - 1) == 1 and "needed" in _msg(lib)
+    # a malformed problem is reported before the workspace is looked at
+    assert _fwd(lib, _prob(flags=3), ws=FAKE + 16, ws_bytes=0) == 1 and "flags" in _msg(lib)

@@ -22,13 +22,13 @@ def _args(inp):
     return [inp[k] for k in KEYS]
 
 
-def _full_check(inp, tol_f, tol_b, label):
+def _full_check(inp, tol_f, tol_b, label, slices=None):
     say(f"[parity] {label}: upload")
     dev = to_device(inp)
-    say(f"[parity] {label}: forward")
-    out = gpu_forward(dev).cpu().numpy()
-    say(f"[parity] {label}: backward")
-    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev))
+    say(f"[parity] {label}: forward (slices={slices})")
+    out = gpu_forward(dev, slices=slices).cpu().numpy()
+    say(f"[parity] {label}: backward (slices={slices})")
+    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, slices=slices))
     say(f"[parity] {label}: oracle")
     r_out = oracle.forward(*_args(inp))
     r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
@@ -44,28 +44,32 @@ def _full_check(inp, tol_f, tol_b, label):
 # the five workloads
 # ---------------------------------------------------------------------------------------
 
-def test_tiny_full():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_tiny_full(slices):
     inp = W.make_inputs(W.WORKLOADS["tiny"])
-    _full_check(inp, TOL_FWD, TOL_BWD, "tiny")
+    _full_check(inp, TOL_FWD, TOL_BWD, "tiny", slices)
 
 
-def test_nuscenes_forward_full():
+# nuScenes-shaped workloads take level slices by default (92 MB of features, 24 levels)
+@pytest.mark.parametrize("slices", [None, False], ids=["auto", "unsliced"])
+def test_nuscenes_forward_full(slices):
     inp = W.make_inputs(W.WORKLOADS["nuscenes_fwd"], with_grad_out=False)
     dev = to_device(inp)
-    say("[parity] nuscenes_fwd: forward")
-    out = gpu_forward(dev).cpu().numpy()
+    say(f"[parity] nuscenes_fwd: forward (slices={slices})")
+    out = gpu_forward(dev, slices=slices).cpu().numpy()
     ref = oracle.forward(*_args(inp))
     say(f"[parity] nuscenes_fwd max err {assert_close('nuscenes out', out, ref, TOL_FWD):.2e}")
-    out2 = gpu_forward(dev).cpu().numpy()
+    out2 = gpu_forward(dev, slices=slices).cpu().numpy()
     assert np.array_equal(out, out2), "forward is not deterministic"
 
 
-def test_nuscenes_backward_full():
+@pytest.mark.parametrize("slices", [None, False], ids=["auto", "unsliced"])
+def test_nuscenes_backward_full(slices):
     inp = W.make_inputs(W.WORKLOADS["nuscenes_bwd"])
     dev = to_device(inp)
-    say("[parity] nuscenes_bwd: backward x2")
-    r1 = [t.cpu().numpy() for t in gpu_backward(dev)]
-    r2 = [t.cpu().numpy() for t in gpu_backward(dev)]
+    say(f"[parity] nuscenes_bwd: backward x2 (slices={slices})")
+    r1 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices)]
+    r2 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices)]
     ref = oracle.backward(*_args(inp), inp["grad_out"])
     for run, r in (("run1", r1), ("run2", r2)):
         for name, g, rr in zip(("grad_feat", "grad_loc", "grad_weights"), r, ref):
@@ -76,13 +80,13 @@ def test_nuscenes_backward_full():
         f"{np.abs(r1[0] - r2[0]).max():.3e}")
 
 
-def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0):
+def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=None):
     say(f"[parity] {wl.name}: generate")
     inp = W.make_inputs(wl)
     dev = to_device(inp)
-    say(f"[parity] {wl.name}: forward + backward")
-    out = gpu_forward(dev)
-    gf, gl, gw = gpu_backward(dev)
+    say(f"[parity] {wl.name}: forward + backward (slices={slices})")
+    out = gpu_forward(dev, slices=slices)
+    gf, gl, gw = gpu_backward(dev, slices=slices)
     rng = np.random.default_rng(seed)
     ids = rng.choice(wl.bs * wl.anchors, size=n_anchor, replace=False)
     ids.sort()
@@ -113,8 +117,9 @@ def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0):
     say(f"[parity] {wl.name}: ok ({touched.size} touched rows)")
 
 
-def test_large_sampled():
-    _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD)
+@pytest.mark.parametrize("slices", [None, False], ids=["auto", "unsliced"])
+def test_large_sampled(slices):
+    _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD, slices=slices)
 
 
 def test_large_bf16_sampled():
@@ -154,11 +159,12 @@ RAGGED = [
 
 @pytest.mark.parametrize("name, kw", RAGGED, ids=[r[0] for r in RAGGED])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_ragged_full(name, kw, dtype):
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_ragged_full(name, kw, dtype, slices):
     wl = W.custom(f"{name}_{dtype}", feat_dtype=dtype, seed=zlib.crc32(name.encode()) % 1000, **kw)
     inp = W.make_inputs(wl)
     tol_f, tol_b = (TOL_BF16, TOL_BF16) if dtype == "bf16" else (TOL_FWD, TOL_BWD)
-    _full_check(inp, tol_f, tol_b, wl.name)
+    _full_check(inp, tol_f, tol_b, wl.name, slices)
 
 
 def test_per_camera_pyramids_and_permuted_level_order():
@@ -213,17 +219,22 @@ def test_exact_texels_bit_exact():
         assert np.array_equal(out[0, a], inp["feat"][0, i * 16 + j])
 
 
-def test_no_points_and_empty_batches():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_no_points_and_empty_batches(slices):
     wl = W.custom("nopts", bs=2, num_cams=2, levels=((4, 5),), C=32, groups=4, anchors=3, pts=0,
                   weight_kind="uniform01")
     inp = W.make_inputs(wl)
     dev = to_device(inp)
-    out = gpu_forward(dev)
-    assert out.shape == (2, 3, 32) and torch.count_nonzero(out) == 0
-    gf = torch.full(tuple(dev["feat"].shape), 7.0, device="cuda")
+    out = torch.full((2, 3, 32), 5.0, device="cuda")
     import view_deformable_feature_amd as vdf
+    vdf.da_forward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"], dev["loc"],
+                   dev["weights"], out=out, slices=slices)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    gf = torch.full(tuple(dev["feat"].shape), 7.0, device="cuda")
     gf, gl, gw = vdf.da_backward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                                 dev["loc"], dev["weights"], dev["grad_out"], grad_feat=gf)
+                                 dev["loc"], dev["weights"], dev["grad_out"], grad_feat=gf,
+                                 slices=slices)
     torch.cuda.synchronize()
     assert torch.count_nonzero(gf) == 0 and gl.numel() == 0 and gw.numel() == 0
     for kw in (dict(anchors=0, pts=4), dict(bs=0, anchors=3, pts=4)):
@@ -231,13 +242,14 @@ def test_no_points_and_empty_batches():
                       **dict(dict(bs=1), **kw))
         inp = W.make_inputs(wl)
         dev = to_device(inp)
-        out = gpu_forward(dev)
-        gf, gl, gw = gpu_backward(dev)
+        out = gpu_forward(dev, slices=slices)
+        gf, gl, gw = gpu_backward(dev, slices=slices)
         assert out.numel() == 0 and gl.numel() == 0 and gw.numel() == 0
         assert torch.count_nonzero(gf) == 0
 
 
-def test_nan_and_far_locations_contribute_nothing():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_nan_and_far_locations_contribute_nothing(slices):
     wl = W.custom("nanloc", bs=1, num_cams=2, levels=((8, 8), (4, 4)), C=32, groups=2,
                   anchors=10, pts=4, loc_lo=-0.1, loc_hi=1.1, seed=5)
     inp = W.make_inputs(wl)
@@ -246,7 +258,7 @@ def test_nan_and_far_locations_contribute_nothing():
     loc[0, :, 1, :, 1] = np.inf
     loc[0, :, 2, :, :] = -3e38
     inp["loc"] = loc
-    _full_check(inp, TOL_FWD, TOL_BWD, "nanloc")
+    _full_check(inp, TOL_FWD, TOL_BWD, "nanloc", slices)
 
 
 def test_max_extent_levels():
@@ -261,13 +273,14 @@ def test_max_extent_levels():
     _full_check(W.make_inputs(wl), TOL_FWD, TOL_BWD, "maxext_w")
 
 
-def test_accumulate_adds_into_existing_gradient():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_accumulate_adds_into_existing_gradient(slices):
     inp = W.make_inputs(W.custom("acc", bs=1, num_cams=2, levels=((10, 12), (5, 6)), C=64,
                                  groups=4, anchors=17, pts=5, loc_lo=-0.1, loc_hi=1.1, seed=12))
     dev = to_device(inp)
     base = torch.randn(tuple(dev["feat"].shape), device="cuda", generator=None)
-    gf0, gl0, gw0 = gpu_backward(dev)
-    gf1, gl1, gw1 = gpu_backward(dev, accumulate_into=base.clone())
+    gf0, gl0, gw0 = gpu_backward(dev, slices=slices)
+    gf1, gl1, gw1 = gpu_backward(dev, accumulate_into=base.clone(), slices=slices)
     assert_close("accumulate", gf1.cpu().numpy(), (base + gf0).cpu().numpy(), 1e-6)
     assert torch.equal(gl0, gl1) and torch.equal(gw0, gw1)
 
@@ -333,9 +346,11 @@ def test_backward_atomic_form_ragged_bf16():
     assert_close("atomic bf16 grad_weights", gw, r_gw, TOL_BF16)
 
 
-def test_workspace_reused_across_calls():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_workspace_reused_across_calls(slices):
     """One caller-owned workspace serves two calls in a row, the second smaller; its
-    stale contents from the first call must not leak into the second."""
+    stale contents from the first call must not leak into the second.  Same for the
+    forward's workspace."""
     import view_deformable_feature_amd as vdf
     big = W.make_inputs(W.custom("ws_big", bs=2, num_cams=2, levels=((20, 30), (10, 15)), C=64,
                                  groups=4, anchors=40, pts=7, loc_lo=-0.1, loc_hi=1.1, seed=51))
@@ -344,19 +359,25 @@ def test_workspace_reused_across_calls():
     dev_b, dev_s = to_device(big), to_device(small)
     n = vdf.workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"], dev_b["weights"])
     ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    nf = vdf.forward_workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"],
+                                    dev_b["weights"], slices=slices)
+    fws = torch.full((max(nf, 1),), 0xAB, dtype=torch.uint8, device="cuda")
     for inp, dev in ((big, dev_b), (small, dev_s), (big, dev_b)):
-        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, workspace=ws))
+        out = gpu_forward(dev, slices=slices, workspace=fws).cpu().numpy()
+        assert_close("ws out", out, oracle.forward(*_args(inp)), TOL_FWD)
+        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, workspace=ws, slices=slices))
         r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
         assert_close("ws grad_feat", gf, r_gf, TOL_BWD)
         assert_close("ws grad_loc", gl, r_gl, TOL_BWD)
         assert_close("ws grad_weights", gw, r_gw, TOL_BWD)
 
 
-def test_hot_rows_span_many_chunks():
+@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
+def test_hot_rows_span_many_chunks(slices):
     """A 2x3 level hit by 4000 samples: each of its rows collects thousands of
     feature-gradient terms, far more than one wave's chunk of the row-sorted list,
     next to a large level with a few terms per row."""
     wl = W.custom("hot_rows", bs=2, num_cams=2, levels=((2, 3), (40, 60)), C=64, groups=4,
                   anchors=250, pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)
     inp = W.make_inputs(wl)
-    _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows")
+    _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows", slices)

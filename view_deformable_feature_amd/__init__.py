@@ -5,6 +5,7 @@ declared in ``include/deformagg.h``); ``api`` binds it to PyTorch tensors.
 ``workloads`` draws seeded synthetic inputs.
 """
 from .api import (DeformableAggregationFunction, da_backward, da_backward_accumulate,  # noqa: F401
-                  da_backward_atomic, da_forward, deformable_aggregation, workspace_size)
+                  da_backward_atomic, da_forward, deformable_aggregation, forward_workspace_size,
+                  workspace_size)
 
-__version__ = "1.0.0"
+__version__ = "1.1.0"

@@ -16,6 +16,7 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "deformagg.h")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
 DA_F32, DA_BF16 = 0, 1
+DA_FLAG_SLICES_ALWAYS, DA_FLAG_SLICES_NEVER = 1, 2
 
 
 class DAProblem(ctypes.Structure):
@@ -29,7 +30,7 @@ class DAProblem(ctypes.Structure):
         ("num_scale", ctypes.c_int64),
         ("num_groups", ctypes.c_int64),
         ("feat_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -54,8 +55,10 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     prob = ctypes.POINTER(DAProblem)
-    lib.da_forward.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp]
+    lib.da_forward.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.da_forward.restype = ctypes.c_int
+    lib.da_forward_workspace_size.argtypes = [prob, ctypes.POINTER(ctypes.c_size_t)]
+    lib.da_forward_workspace_size.restype = ctypes.c_int
     for name in ("da_backward", "da_backward_accumulate"):
         f = getattr(lib, name)
         f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]

@@ -22,8 +22,8 @@ import torch
 from . import _lib
 
 __all__ = ["da_forward", "da_backward", "da_backward_accumulate", "da_backward_atomic",
-           "workspace_size", "DeformableAggregationFunction", "deformable_aggregation",
-           "problem_of"]
+           "workspace_size", "forward_workspace_size", "DeformableAggregationFunction",
+           "deformable_aggregation", "problem_of"]
 
 IntTable = Union[torch.Tensor, np.ndarray, Sequence]
 
@@ -54,8 +54,16 @@ def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _flags(slices: Optional[bool]) -> int:
+    """slices: None lets the library choose level slices, True / False force them on / off."""
+    if slices is None:
+        return 0
+    return _lib.DA_FLAG_SLICES_ALWAYS if slices else _lib.DA_FLAG_SLICES_NEVER
+
+
 def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
-               sampling_location: torch.Tensor, weights: torch.Tensor) -> _lib.DAProblem:
+               sampling_location: torch.Tensor, weights: torch.Tensor,
+               slices: Optional[bool] = None) -> _lib.DAProblem:
     if mc_ms_feat.dim() != 3:
         raise ValueError("mc_ms_feat must be [bs, num_feat, C]")
     if sampling_location.dim() != 5 or sampling_location.shape[-1] != 2:
@@ -70,17 +78,18 @@ def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
     if spatial_shape.shape[:2] != (K, S):
         raise ValueError(f"spatial_shape is {spatial_shape.shape}, expected ({K}, {S}, 2)")
     dt = _lib.DA_BF16 if mc_ms_feat.dtype == torch.bfloat16 else _lib.DA_F32
-    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt, 0)
+    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt, _flags(slices))
 
 
-def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights):
+def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
+             slices=None):
     shape = _host_i32(spatial_shape)
     start = _host_i32(scale_start_index)
     dev = mc_ms_feat.device
     _need(mc_ms_feat, "mc_ms_feat", (torch.float32, torch.bfloat16), dev)
     _need(sampling_location, "sampling_location", torch.float32, dev)
     _need(weights, "weights", torch.float32, dev)
-    prob = problem_of(mc_ms_feat, shape, sampling_location, weights)
+    prob = problem_of(mc_ms_feat, shape, sampling_location, weights, slices)
     bs, A, P, K = (sampling_location.shape[i] for i in range(4))
     if tuple(weights.shape[:4]) != (bs, A, P, K) or mc_ms_feat.shape[0] != bs:
         raise ValueError("batch / anchor / point / camera sizes disagree between inputs")
@@ -97,23 +106,54 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _workspace(lib, size_fn: str, prob, dev, workspace):
+    """The caller's workspace, checked, or a new one from torch's caching allocator
+    (no device allocation on the steady path); None when none is needed."""
+    n = ctypes.c_size_t(0)
+    _lib.check(getattr(lib, size_fn)(ctypes.byref(prob), ctypes.byref(n)), size_fn)
+    if workspace is None and n.value:
+        workspace = torch.empty(int(n.value), device=dev, dtype=torch.uint8)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < n.value:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, {n.value} needed")
+    return workspace
+
+
 def da_forward(mc_ms_feat: torch.Tensor, spatial_shape: IntTable, scale_start_index: IntTable,
                sampling_location: torch.Tensor, weights: torch.Tensor,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[bs, A, C] (float32) on the current stream of mc_ms_feat's device."""
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               slices: Optional[bool] = None) -> torch.Tensor:
+    """out[bs, A, C] (float32) on the current stream of mc_ms_feat's device.
+
+    slices=None lets the library choose level slices (given a workspace, allocated
+    here when not passed), True forces them, False runs one workgroup per anchor."""
     lib = _lib.load()
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
-                                  sampling_location, weights)
+                                  sampling_location, weights, slices)
     dev = mc_ms_feat.device
     if out is None:
         out = torch.empty((prob.bs, prob.num_anchors, prob.num_embeds), device=dev,
                           dtype=torch.float32)
     _need(out, "out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
+    workspace = _workspace(lib, "da_forward_workspace_size", prob, dev, workspace)
     with torch.cuda.device(dev):
         st = lib.da_forward(ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
-                            _ptr(sampling_location), _ptr(weights), _ptr(out), _stream(dev))
+                            _ptr(sampling_location), _ptr(weights), _ptr(out), _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), _stream(dev))
     _lib.check(st, "da_forward")
     return out
+
+
+def forward_workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
+                           slices: Optional[bool] = None) -> int:
+    """Bytes of workspace that let da_forward use level slices for these shapes."""
+    lib = _lib.load()
+    prob = problem_of(mc_ms_feat, _host_i32(spatial_shape), sampling_location, weights, slices)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.da_forward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
+               "da_forward_workspace_size")
+    return int(n.value)
 
 
 def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights) -> int:
@@ -128,10 +168,10 @@ def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights) -> int
 
 def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
               weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None,
-              workspace=None):
+              workspace=None, slices=None):
     lib = _lib.load()
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
-                                  sampling_location, weights)
+                                  sampling_location, weights, slices)
     dev = mc_ms_feat.device
     _need(grad_out, "grad_out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
     if grad_feat is None:
@@ -152,16 +192,7 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
         if func == "da_backward_atomic":
             st = lib.da_backward_atomic(*common, _stream(dev))
         else:
-            n = ctypes.c_size_t(0)
-            _lib.check(lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
-                       "da_backward_workspace_size")
-            if workspace is None and n.value:
-                # torch's caching allocator: no device allocation on the steady path
-                workspace = torch.empty(int(n.value), device=dev, dtype=torch.uint8)
-            if workspace is not None:
-                _need(workspace, "workspace", torch.uint8, dev)
-                if workspace.numel() < n.value:
-                    raise ValueError(f"workspace has {workspace.numel()} bytes, {n.value} needed")
+            workspace = _workspace(lib, "da_backward_workspace_size", prob, dev, workspace)
             st = getattr(lib, func)(*common, _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(dev))
     _lib.check(st, func)
@@ -169,21 +200,21 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
 
 
 def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
-                grad_out, grad_feat=None, grad_loc=None, grad_weights=None, workspace=None
-                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                grad_out, grad_feat=None, grad_loc=None, grad_weights=None, workspace=None,
+                slices=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
     return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
-                     workspace)
+                     workspace, slices)
 
 
 def da_backward_accumulate(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
                            weights, grad_out, grad_feat, grad_loc=None, grad_weights=None,
-                           workspace=None):
+                           workspace=None, slices=None):
     """As da_backward, adding the feature gradient into the existing ``grad_feat``."""
     return _backward("da_backward_accumulate", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
-                     workspace)
+                     workspace, slices)
 
 
 def da_backward_atomic(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,

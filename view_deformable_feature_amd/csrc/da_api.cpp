@@ -51,7 +51,10 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
                        const int32_t* start, const float* loc, const float* weights,
                        Plan& plan) {
     if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
-    if (p->reserved != 0) return fail(DA_ERR_INVALID_ARG, "problem.reserved must be 0");
+    if ((p->flags & ~(DA_FLAG_SLICES_ALWAYS | DA_FLAG_SLICES_NEVER)) != 0 ||
+        (p->flags & DA_FLAG_SLICES_ALWAYS && p->flags & DA_FLAG_SLICES_NEVER))
+        return fail(DA_ERR_INVALID_ARG, "problem.flags = %d is not a valid combination",
+                    (int)p->flags);
     if (p->bs < 0 || p->num_anchors < 0 || p->num_pts < 0)
         return fail(DA_ERR_INVALID_ARG, "bs, num_anchors and num_pts must be >= 0");
     if (p->num_feat < 1 || p->num_embeds < 1 || p->num_cams < 1 || p->num_scale < 1 ||
@@ -144,6 +147,101 @@ da_status choose_pk_chunk(da::KArgs& ka, int desc_bytes, size_t fixed, size_t& l
     ka.pk_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ka.npk, fit));
     lds = fixed + per_pair * ka.pk_chunk;
     return DA_OK;
+}
+
+// Level slices pay off once the features outgrow one XCD's L2 (4 MiB): take
+// them from twice that, when the levels split into 8 nearly equal shares.
+constexpr uint64_t kSliceMinImageBytes = 8ull << 20;
+
+bool want_slices(const da_problem* p) {
+    if (p->flags & DA_FLAG_SLICES_NEVER) return false;
+    if (p->flags & DA_FLAG_SLICES_ALWAYS) return true;
+    const int64_t nlev = p->num_cams * p->num_scale;
+    if (nlev < da::kSlices) return false;
+    const int64_t m = (nlev + da::kSlices - 1) / da::kSlices;
+    if (4 * m * da::kSlices > 5 * nlev) return false;   // more than 1/4 of the slots idle
+    const uint64_t elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    return (uint64_t)p->num_feat * (uint64_t)p->num_embeds * elem >= kSliceMinImageBytes;
+}
+
+// Assign the levels to slices: largest first (ties in level order), dealt
+// round-robin, so every slice holds the same number of levels give or take
+// one.  Returns P * the largest slice's level count.
+int32_t fill_slices(da::KArgs& ka) {
+    const int nlev = ka.K * ka.S;
+    int order[da::kMaxLevels];
+    for (int l = 0; l < nlev; ++l) order[l] = l;
+    std::stable_sort(order, order + nlev, [&](int u, int v) {
+        return (int64_t)ka.lv.H[u] * ka.lv.W[u] > (int64_t)ka.lv.H[v] * ka.lv.W[v];
+    });
+    for (int x = 0; x < da::kSlices; ++x) ka.lv.slice_nlev[x] = 0;
+    for (int i = 0; i < nlev; ++i) {
+        const int x = i % da::kSlices;
+        ka.lv.slice_level[x][ka.lv.slice_nlev[x]++] = (int8_t)order[i];
+    }
+    int m = 0;
+    for (int x = 0; x < da::kSlices; ++x) m = std::max<int>(m, ka.lv.slice_nlev[x]);
+    ka.max_slice_samples = ka.P * m;
+    return ka.max_slice_samples;
+}
+
+// Waves per workgroup of the sliced kernels.  A slice of one anchor holds few
+// samples (P * levels / 8, 39 for 13 points over 24 levels), so small
+// workgroups -- many of them resident per CU -- hide the staging latency best;
+// measured on MI355X over the nuScenes-shaped and 4 x 510k-row workloads.
+constexpr int kSlicedFwdWaves = 4;
+constexpr int kSlicedBwdWaves = 2;
+
+// Samples of a slice staged in LDS at once.
+bool choose_sample_chunk(da::KArgs& ka, size_t per_sample, size_t fixed, size_t& lds) {
+    if (fixed + per_sample > (size_t)da::kLdsBudget) return false;
+    const int64_t fit = (int64_t)((da::kLdsBudget - fixed) / per_sample);
+    ka.sample_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ka.max_slice_samples, fit));
+    lds = fixed + per_sample * ka.sample_chunk;
+    return true;
+}
+
+bool sliced_nv_supported(int nv) { return nv == 1 || nv == 2 || nv == 4; }
+
+uint64_t fwd_workspace_bytes(const da_problem* p) {
+    if (!want_slices(p)) return 0;
+    return (uint64_t)da::kSlices * p->bs * p->num_anchors * p->num_embeds * 4;
+}
+
+// Switch a planned forward to level slices when wanted and supported.
+void plan_forward_sliced(const da_problem* p, Plan& plan) {
+    da::KArgs& ka = plan.ka;
+    da::LaunchShape& s = plan.shape;
+    if (!want_slices(p) || !sliced_nv_supported(s.nvc) || plan.n_anchors * da::kSlices > INT32_MAX)
+        return;
+    const int64_t n = fill_slices(ka);
+    const int64_t spw = da::kWave / ka.L;
+    const int waves =
+        (int)std::max<int64_t>(1, std::min<int64_t>(kSlicedFwdWaves, (n + 4 * spw - 1) / (4 * spw)));
+    const size_t fixed = (size_t)waves * ka.nv_chunk * ka.L * s.vec * 4 + da::kFwdDescBytes;
+    size_t lds = 0;
+    if (!choose_sample_chunk(ka, da::kFwdDescBytes + 4 * (size_t)ka.G, fixed, lds)) return;
+    ka.sliced = 1;
+    s.waves = waves;
+    s.lds_bytes = lds;
+}
+
+// Switch a planned gather backward to level slices when wanted and supported.
+void plan_backward_sliced(const da_problem* p, Plan& plan) {
+    da::KArgs& ka = plan.ka;
+    da::LaunchShape& s = plan.shape;
+    if (!want_slices(p) || !sliced_nv_supported(s.nvc) || plan.n_anchors * da::kSlices > INT32_MAX)
+        return;
+    const int64_t n = fill_slices(ka);
+    const int64_t spw = da::kWave / ka.L;
+    const int waves =
+        (int)std::max<int64_t>(1, std::min<int64_t>(kSlicedBwdWaves, (n + 2 * spw - 1) / (2 * spw)));
+    size_t lds = 0;
+    if (!choose_sample_chunk(ka, da::kBwdDescBytes + 4 * (size_t)ka.G + 4, da::kBwdDescBytes, lds))
+        return;
+    ka.sliced = 1;
+    s.waves = waves;
+    s.lds_bytes = lds;
 }
 
 da_status plan_forward(const da_problem* p, Plan& plan) {
@@ -249,7 +347,7 @@ da_status hip_status(hipError_t e, const char* what) {
 
 // Workspace of the gather form of the backward, each part 256-byte aligned.
 struct WsLayout {
-    size_t cnt, local_start, tile_prefix, rank, entries, total;
+    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -258,6 +356,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
     WsLayout w;
     const uint64_t n_tiles = (n_rows + da::kScanTile - 1) / da::kScanTile;
     size_t off = 0;
+    w.scan_done = off;          // one counter; cnt follows it directly
+    off += 256;
     w.cnt = off;
     off += align256(n_rows * 4);
     w.local_start = off;
@@ -268,6 +368,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
     off += align256(n_samples * 16);
     w.entries = off;
     off += align256(n_samples * 4 * sizeof(da::Entry));
+    w.loc_part = off;
+    off += align256(n_samples * 8);
     w.total = off;
     return w;
 }
@@ -332,11 +434,13 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                 return fail(DA_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed",
                             workspace_bytes, w.total);
             unsigned char* base = static_cast<unsigned char*>(workspace);
+            ka.scan_done = reinterpret_cast<uint32_t*>(base + w.scan_done);
             ka.cnt = reinterpret_cast<uint32_t*>(base + w.cnt);
             ka.local_start = reinterpret_cast<uint32_t*>(base + w.local_start);
             ka.tile_prefix = reinterpret_cast<uint32_t*>(base + w.tile_prefix);
             ka.rank = reinterpret_cast<uint32_t*>(base + w.rank);
             ka.entries = reinterpret_cast<da::Entry*>(base + w.entries);
+            ka.loc_part = reinterpret_cast<float*>(base + w.loc_part);
             ka.n_rows = (uint32_t)n_rows;
             ka.n_samples = (uint32_t)n_samples;
             ka.n_anchors = (uint32_t)plan.n_anchors;
@@ -344,6 +448,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.num_feat = (int32_t)p->num_feat;
             ka.accumulate = mode == BwdMode::kGatherAccumulate ? 1 : 0;
             if (ka.gather_vec == 4 && !aligned(grad_feat, 16)) ka.gather_vec = 1;
+            plan_backward_sliced(p, plan);
         }
     }
     // the scatter form adds into zeros; the gather form zeroes only the rows no
@@ -366,9 +471,19 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
 
 extern "C" {
 
+da_status da_forward_workspace_size(const da_problem* p, size_t* bytes) {
+    if (!bytes) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
+    if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->bs < 0 || p->num_anchors < 0 || p->num_embeds < 1 || p->num_feat < 1 ||
+        p->num_cams < 1 || p->num_scale < 1)
+        return fail(DA_ERR_INVALID_ARG, "malformed problem sizes");
+    *bytes = (size_t)fwd_workspace_bytes(p);
+    return DA_OK;
+}
+
 da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape,
                      const int32_t* start, const float* loc, const float* weights, float* out,
-                     void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream) {
     Plan plan;
     da_status st = check_common(p, feat, shape, start, loc, weights, plan);
     if (st != DA_OK) return st;
@@ -376,10 +491,28 @@ da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape
     if (!aligned(out, 4)) return fail(DA_ERR_INVALID_ARG, "out is not 4-byte aligned");
     st = plan_forward(p, plan);
     if (st != DA_OK) return st;
+    if (workspace) {
+        const uint64_t need = fwd_workspace_bytes(p);
+        if (!aligned(workspace, 256))
+            return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(DA_ERR_INVALID_ARG, "workspace has %zu bytes, %llu needed",
+                        workspace_bytes, (unsigned long long)need);
+    }
     if (plan.n_anchors == 0) return DA_OK;
     plan.ka.out = out;
-    return hip_status(da::launch_forward(plan.ka, plan.shape, plan.n_anchors, plan.bf16,
-                                         static_cast<hipStream_t>(stream)),
+    plan.ka.n_anchors = (uint32_t)plan.n_anchors;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (workspace) {
+        plan_forward_sliced(p, plan);
+        if (plan.ka.sliced) {
+            plan.ka.fwd_part = static_cast<float*>(workspace);
+            return hip_status(da::launch_forward_sliced(plan.ka, plan.shape, plan.n_anchors,
+                                                        plan.bf16, s),
+                              "forward kernel launch");
+        }
+    }
+    return hip_status(da::launch_forward(plan.ka, plan.shape, plan.n_anchors, plan.bf16, s),
                       "forward kernel launch");
 }
 

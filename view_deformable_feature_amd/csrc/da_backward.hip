@@ -81,6 +81,109 @@ __device__ __forceinline__ uint32_t row_first_entry(const KArgs& a, uint32_t fla
     return a.tile_prefix[flat_row / (uint32_t)kScanTile] + a.local_start[flat_row];
 }
 
+// LDS descriptor of one sample: corner offsets and the per-corner factors of
+// the location gradient (section 4.1).
+__device__ __forceinline__ BwdDesc bwd_desc(const KArgs& a, const Stencil& st) {
+    BwdDesc d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = st.row[i] >= 0;
+        d.off[i] = ok ? (uint32_t)st.row[i] * (uint32_t)a.row_bytes : a.feat_image_bytes;
+        d.goff[i] = ok ? (uint32_t)st.row[i] * (uint32_t)a.grow_bytes : a.gfeat_image_bytes;
+        d.cw[i] = st.cw[i];
+    }
+    const float m = st.inside ? 1.0f : 0.0f;
+    d.gx[0] = -m * st.W * st.hh;
+    d.gx[1] = m * st.W * st.hh;
+    d.gx[2] = -m * st.W * st.lh;
+    d.gx[3] = m * st.W * st.lh;
+    d.gy[0] = -m * st.H * st.hw;
+    d.gy[1] = -m * st.H * st.lw;
+    d.gy[2] = m * st.H * st.hw;
+    d.gy[3] = m * st.H * st.lw;
+    return d;
+}
+
+// Bucket the inside corners of flat sample q for the feature-gradient gather:
+// each goes to its row's slot rank[q][corner] (taken by count_kernel).  All
+// lookups are issued before any store (outside corners read row 0 and store
+// nothing), so a thread waits for one round of loads, not one per corner.
+__device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st, int64_t b,
+                                              int64_t ba, uint32_t q) {
+    const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)q * 4);
+    const uint32_t rks[4] = {rk.x, rk.y, rk.z, rk.w};
+    const uint32_t base = (uint32_t)b * (uint32_t)a.num_feat;
+    uint32_t fr[4], cn[4], first[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fr[i] = base + (uint32_t)(st.row[i] >= 0 ? st.row[i] : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        cn[i] = a.cnt[fr[i]];
+        first[i] = a.tile_prefix[fr[i] / (uint32_t)kScanTile] + a.local_start[fr[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        Entry e;
+        e.row = fr[i] | (cn[i] > (uint32_t)kGatherLong ? kEntryLongRow : 0u);
+        e.w_off = q * (uint32_t)a.G * 4u;
+        e.cw = st.cw[i];
+        e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u;
+        const uint32_t pos = first[i] + rks[i];
+        if (st.row[i] >= 0 && pos < 4u * a.n_samples) a.entries[pos] = e;
+    }
+}
+
+// Per-lane dot products of one sample: tc[c] = sum over the lane's channels of
+// weight * grad_out * v_c, and gwp[i] = sum_c cw_c * (grad_out . v_c) over
+// vector i (the lane's share of the weight gradient of group gi[i]).
+template <int VEC, int NV>
+__device__ __forceinline__ void sample_dots(const BwdDesc& d, const float (&v)[NV][4][VEC],
+                                            const float (&go)[NV][VEC], const float* wrow,
+                                            const int (&gi)[NV], float (&tc)[4],
+                                            float (&gwp)[NV], float (&w)[NV]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tc[c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        w[i] = wrow[gi[i]];
+        float dot[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            dot[c] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dot[c] += go[i][e] * v[i][c][e];
+            tc[c] += w[i] * dot[c];
+        }
+        gwp[i] = d.cw[0] * dot[0] + d.cw[1] * dot[1] + d.cw[2] * dot[2] + d.cw[3] * dot[3];
+    }
+}
+
+// Sum gwp over the `seg` lanes that share a group and store the sample's
+// weight-gradient row (gwrow = grad_weights row of the sample).  The sums land
+// in the last lane of each seg-lane segment.
+template <int NV>
+__device__ __forceinline__ void store_grad_weights(float (&gwp)[NV], const int (&gi)[NV],
+                                                   float* gwrow, int seg, int L, int li) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) gwp[i] = group_sum(gwp[i], seg);
+    if (seg < L) {
+        if ((li & (seg - 1)) == seg - 1) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) gwrow[gi[i]] = gwp[i];
+        }
+    } else if (li == L - 1) {
+        float run = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            run += gwp[i];
+            if (i + 1 == NV || gi[i + 1 < NV ? i + 1 : i] != gi[i]) {
+                gwrow[gi[i]] = run;
+                run = 0.0f;
+            }
+        }
+    }
+}
+
 template <typename T, int VEC, int NV, bool SCATTER>
 __global__ void __launch_bounds__(kWave * kMaxWaves)
 da_backward_anchor_kernel(KArgs a) {
@@ -125,45 +228,8 @@ da_backward_anchor_kernel(KArgs a) {
         const int ns = npk_here * S;
         for (int t = x.tid; t < ns; t += x.nthreads) {
             const Stencil st = make_stencil(a, ba, pk0 * S + t);
-            BwdDesc d;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = st.row[i] >= 0;
-                d.off[i] = ok ? (uint32_t)st.row[i] * (uint32_t)a.row_bytes : a.feat_image_bytes;
-                d.goff[i] = ok ? (uint32_t)st.row[i] * (uint32_t)a.grow_bytes : a.gfeat_image_bytes;
-                d.cw[i] = st.cw[i];
-            }
-            const float m = st.inside ? 1.0f : 0.0f;
-            d.gx[0] = -m * st.W * st.hh;
-            d.gx[1] = m * st.W * st.hh;
-            d.gx[2] = -m * st.W * st.lh;
-            d.gx[3] = m * st.W * st.lh;
-            d.gy[0] = -m * st.H * st.hw;
-            d.gy[1] = -m * st.H * st.lw;
-            d.gy[2] = m * st.H * st.hw;
-            d.gy[3] = m * st.H * st.lw;
-            desc[t] = d;
-            if (!SCATTER) {
-                // bucket this sample's inside corners for the feature-gradient gather
-                const uint32_t q = q_anchor + (uint32_t)(pk0 * S + t);
-                const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)q * 4);
-                const uint32_t rks[4] = {rk.x, rk.y, rk.z, rk.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (st.row[i] >= 0) {
-                        const uint32_t flat_row =
-                            (uint32_t)b * (uint32_t)a.num_feat + (uint32_t)st.row[i];
-                        Entry e;
-                        e.row = flat_row |
-                                (a.cnt[flat_row] > (uint32_t)kGatherLong ? kEntryLongRow : 0u);
-                        e.w_off = q * (uint32_t)a.G * 4u;
-                        e.cw = st.cw[i];
-                        e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u;
-                        const uint32_t pos = row_first_entry(a, flat_row) + rks[i];
-                        if (pos < 4u * a.n_samples) a.entries[pos] = e;
-                    }
-                }
-            }
+            desc[t] = bwd_desc(a, st);
+            if (!SCATTER) bucket_sample(a, st, b, ba, q_anchor + (uint32_t)(pk0 * S + t));
         }
         const float* wsrc = a.weights + wbase + (int64_t)pk0 * S * a.G;
         for (int i = x.tid; i < ns * a.G; i += x.nthreads) wts[i] = wsrc[i];
@@ -174,22 +240,12 @@ da_backward_anchor_kernel(KArgs a) {
         // location partials
         auto process = [&](const BwdDesc& d, const float (&v)[NV][4][VEC], int pk, int s) {
             const int t = pk * S + s;
-            float tc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // sum over lanes' channels of top * v_c
-            float gwp[NV];
+            float tc[4], gwp[NV], w[NV];
+            sample_dots<VEC, NV>(d, v, go, wts + t * a.G, gi, tc, gwp, w);
+            if constexpr (SCATTER) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const float w = wts[t * a.G + gi[i]];
-                float dot[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    dot[c] = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) dot[c] += go[i][e] * v[i][c][e];
-                    tc[c] += w * dot[c];
-                }
-                gwp[i] = d.cw[0] * dot[0] + d.cw[1] * dot[1] + d.cw[2] * dot[2] + d.cw[3] * dot[3];
-                if constexpr (SCATTER) {
-                    const float top = go[i][0] * w;
+                for (int i = 0; i < NV; ++i) {
+                    const float top = go[i][0] * w[i];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
@@ -198,34 +254,13 @@ da_backward_anchor_kernel(KArgs a) {
             }
             gxs += d.gx[0] * tc[0] + d.gx[1] * tc[1] + d.gx[2] * tc[2] + d.gx[3] * tc[3];
             gys += d.gy[0] * tc[0] + d.gy[1] * tc[1] + d.gy[2] * tc[2] + d.gy[3] * tc[3];
-
             // weight gradient: grad_out * val summed over the channels of each group
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                for (int m = 1; m < seg; m <<= 1) gwp[i] += xor_shfl(gwp[i], m);
-            float* gwrow = a.grad_weights + wbase + ((int64_t)(pk0 + pk) * S + s) * a.G;
-            if (seg < L) {
-                if ((li & (seg - 1)) == 0) {
-#pragma unroll
-                    for (int i = 0; i < NV; ++i) gwrow[gi[i]] = gwp[i];
-                }
-            } else if (li == 0) {
-                float run = 0.0f;
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    run += gwp[i];
-                    if (i + 1 == NV || gi[i + 1 < NV ? i + 1 : i] != gi[i]) {
-                        gwrow[gi[i]] = run;
-                        run = 0.0f;
-                    }
-                }
-            }
+            store_grad_weights<NV>(gwp, gi, a.grad_weights + wbase + ((int64_t)(pk0 + pk) * S + s) * a.G,
+                                   seg, L, li);
             if (s == S - 1) {   // last scale of this pair: location gradient
-                for (int m = 1; m < L; m <<= 1) {
-                    gxs += xor_shfl(gxs, m);
-                    gys += xor_shfl(gys, m);
-                }
-                if (li == 0) {
+                gxs = group_sum(gxs, L);
+                gys = group_sum(gys, L);
+                if (li == L - 1) {
                     float2* gl = reinterpret_cast<float2*>(a.grad_loc + (ba * a.npk + pk0 + pk) * 2);
                     *gl = make_float2(gxs, gys);
                 }
@@ -266,6 +301,128 @@ da_backward_anchor_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// per-anchor kernel by level slices (gather form)
+// ------------------------------------------------------------------------------------
+// Workgroup (anchor, x) -- on XCD x -- takes the samples of the levels in
+// slice x only, in the order of slice_sample().  Everything but the location
+// gradient is per sample, as in the kernel above.  A point-camera pair's
+// scales are spread over slices, so each sample's location partial (summed
+// over the lanes of its row group) goes to loc_part[q], and loc_reduce_kernel
+// adds a pair's S partials in scale order.
+template <typename T, int VEC, int NV>
+__global__ void __launch_bounds__(kWave * kMaxWaves)
+da_backward_sliced_kernel(KArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int x = (int)(blockIdx.x % (uint32_t)kSlices);
+    const int64_t ba = blockIdx.x / (uint32_t)kSlices;
+    const int64_t b = ba / a.A;
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int L = a.L;
+    const int spw = kWave >> a.log2L;
+    const int rg = wave * spw + (lane >> a.log2L);
+    const int n_rg = (nthreads / kWave) * spw;
+    const int li = lane & (L - 1);
+    const int seg = a.seg;
+    constexpr int kElem = (int)sizeof(T);
+
+    const int ns_max = a.sample_chunk;           // desc[ns_max] is the null descriptor
+    BwdDesc* desc = reinterpret_cast<BwdDesc*>(smem);
+    float* wts = reinterpret_cast<float*>(smem + (size_t)(ns_max + 1) * sizeof(BwdDesc));
+    int32_t* tix = reinterpret_cast<int32_t*>(wts + (size_t)ns_max * a.G);
+
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(
+        static_cast<const unsigned char*>(a.feat) + b * a.feat_batch_bytes, a.feat_image_bytes);
+
+    const uint32_t lane_off = (uint32_t)(li * VEC * kElem);
+    uint32_t soff[NV];
+    float go[NV][VEC];
+    int gi[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c0 = (li + L * i) * VEC;
+        soff[i] = (uint32_t)(L * i * VEC * kElem);
+        gi[i] = c0 / a.D;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) go[i][e] = a.grad_out[ba * a.C + c0 + e];
+    }
+
+    if (tid == 0) desc[ns_max] = null_bwd_desc(a.feat_image_bytes, a.gfeat_image_bytes);
+    const int m = a.lv.slice_nlev[x];
+    const int n = a.P * m;
+    const int64_t wbase = ba * (int64_t)a.npk * a.S * a.G;
+    const uint32_t q_anchor = (uint32_t)ba * (uint32_t)(a.npk * a.S);   // first flat sample
+    for (int j0 = 0; j0 < n; j0 += ns_max) {
+        const int nsc = min(ns_max, n - j0);
+        for (int jj = tid; jj < nsc; jj += nthreads) {
+            const int t = slice_sample(a, x, m, j0 + jj);
+            const Stencil st = make_stencil(a, ba, t);
+            desc[jj] = bwd_desc(a, st);
+            tix[jj] = t;
+            bucket_sample(a, st, b, ba, q_anchor + (uint32_t)t);
+        }
+        for (int i = tid; i < nsc * a.G; i += nthreads) {
+            const int jj = i / a.G;
+            wts[i] = a.weights[wbase + (int64_t)slice_sample(a, x, m, j0 + jj) * a.G + (i - jj * a.G)];
+        }
+        __syncthreads();
+
+        auto process = [&](const BwdDesc& d, const float (&v)[NV][4][VEC], int jj) {
+            const int t = tix[jj];
+            float tc[4], gwp[NV], w[NV];
+            sample_dots<VEC, NV>(d, v, go, wts + jj * a.G, gi, tc, gwp, w);
+            float gx = d.gx[0] * tc[0] + d.gx[1] * tc[1] + d.gx[2] * tc[2] + d.gx[3] * tc[3];
+            float gy = d.gy[0] * tc[0] + d.gy[1] * tc[1] + d.gy[2] * tc[2] + d.gy[3] * tc[3];
+            store_grad_weights<NV>(gwp, gi, a.grad_weights + wbase + (int64_t)t * a.G, seg, L, li);
+            gx = group_sum(gx, L);
+            gy = group_sum(gy, L);
+            if (li == L - 1)
+                reinterpret_cast<float2*>(a.loc_part)[q_anchor + (uint32_t)t] = make_float2(gx, gy);
+        };
+
+        int j = rg;
+        if (j < nsc) {
+            BwdDesc dA = desc[j], dB;
+            float vA[NV][4][VEC], vB[NV][4][VEC];
+            bwd_load<T, VEC, NV>(rf, dA, lane_off, soff, vA);
+            while (true) {
+                int jn = j + n_rg;
+                dB = desc[jn < nsc ? jn : ns_max];
+                bwd_load<T, VEC, NV>(rf, dB, lane_off, soff, vB);
+                process(dA, vA, j);
+                if (jn >= nsc) break;
+                j = jn;
+                jn = j + n_rg;
+                dA = desc[jn < nsc ? jn : ns_max];
+                bwd_load<T, VEC, NV>(rf, dA, lane_off, soff, vA);
+                process(dB, vB, j);
+                if (jn >= nsc) break;
+                j = jn;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// grad_loc of each (anchor, point, camera) = sum of its S scale partials, in
+// scale order.
+__global__ void __launch_bounds__(256) loc_reduce_kernel(KArgs a) {
+    const int64_t n = (int64_t)a.n_anchors * a.npk;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float2* part = reinterpret_cast<const float2*>(a.loc_part);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float gx = 0.0f, gy = 0.0f;
+        for (int s = 0; s < a.S; ++s) {
+            const float2 v = part[i * a.S + s];
+            gx += v.x;
+            gy += v.y;
+        }
+        reinterpret_cast<float2*>(a.grad_loc)[i] = make_float2(gx, gy);
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // gather form: count, scan, gather
 // ------------------------------------------------------------------------------------
 // Level-major counting.  Workgroup (x, level, b) takes 256 consecutive
@@ -276,7 +433,7 @@ da_backward_anchor_kernel(KArgs a) {
 // the level; one global atomic per touched row then reserves the workgroup's
 // block of slots.  Large levels count straight into global memory.  The slot
 // order inside a row is whatever order the atomics retire in.
-__global__ void __launch_bounds__(256) count_kernel(KArgs a) {
+__global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     __shared__ uint32_t hist[kCountLdsRows];
     const int lvl = blockIdx.y;
     const int k = lvl / a.S, s = lvl - (lvl / a.S) * a.S;
@@ -309,10 +466,26 @@ __global__ void __launch_bounds__(256) count_kernel(KArgs a) {
             rk[c] = hit ? atomicAdd(a.cnt + row0 + (uint32_t)st.row[c], 1u) : 0u;
     }
     if (in_lds) {
+        // reserve each touched row's block of slots; every atomic is issued
+        // before any result is needed
+        constexpr int kPer = kCountLdsRows / kCountThreads;
         __syncthreads();
-        for (int j = threadIdx.x; j < nrow; j += blockDim.x) {
-            const uint32_t c = hist[j];
-            if (c) hist[j] = atomicAdd(a.cnt + row0 + (uint32_t)(start + j), c);
+        uint32_t c[kPer], base[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int j = (int)threadIdx.x + u * kCountThreads;
+            c[u] = j < nrow ? hist[j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int j = (int)threadIdx.x + u * kCountThreads;
+            base[u] = c[u] ? atomicAdd(a.cnt + row0 + (uint32_t)(start + j), c[u]) : 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int j = (int)threadIdx.x + u * kCountThreads;
+            if (c[u]) hist[j] = base[u];
         }
         __syncthreads();
 #pragma unroll
@@ -333,10 +506,15 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
     return v;
 }
 
-// Exclusive prefix sum of cnt inside tiles of kScanTile rows; tile totals to
-// tile_prefix[tile].
+// Exclusive prefix sum of cnt inside tiles of kScanTile rows, tile totals to
+// tile_prefix[tile]; the workgroup that finishes last then turns tile_prefix
+// into the exclusive prefix of the totals, with the grand total in
+// tile_prefix[n_tiles].  (Release: each tile's total is stored, then fenced at
+// device scope before the counter increment; acquire: the last workgroup
+// fences after seeing the count, before reading the totals.)
 __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
     __shared__ uint32_t wave_tot[kScanThreads / kWave];
+    __shared__ uint32_t is_last;
     const uint32_t n = a.n_rows;
     const uint32_t base = blockIdx.x * (uint32_t)kScanTile + threadIdx.x * (uint32_t)kScanItems;
     uint32_t v[kScanItems];
@@ -379,32 +557,31 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
         for (int j = 0; j < kScanItems; ++j)
             if (base + j < n) a.local_start[base + j] = excl + v[j];
     }
-    if (threadIdx.x == kScanThreads - 1) a.tile_prefix[blockIdx.x] = excl + tot;
-}
-
-// In-place exclusive prefix sum of the tile totals (one workgroup); the grand
-// total lands in tile_prefix[n_tiles].
-__global__ void __launch_bounds__(1024) scan_tile_totals_kernel(KArgs a) {
-    __shared__ uint32_t wave_tot[1024 / kWave];
-    __shared__ uint32_t carry_s;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    if (threadIdx.x == 0) carry_s = 0;
-    __syncthreads();
-    for (uint32_t base = 0; base < a.n_tiles; base += blockDim.x) {
-        const uint32_t i = base + threadIdx.x;
-        const uint32_t v = i < a.n_tiles ? a.tile_prefix[i] : 0u;
-        const uint32_t incl = wave_inclusive_scan(v, lane);
-        if (lane == kWave - 1) wave_tot[wave] = incl;
-        __syncthreads();
-        uint32_t before = 0;
-        for (int w = 0; w < wave; ++w) before += wave_tot[w];
-        const uint32_t carry = carry_s;
-        if (i < a.n_tiles) a.tile_prefix[i] = carry + before + incl - v;
-        __syncthreads();
-        if (threadIdx.x == blockDim.x - 1) carry_s = carry + before + incl;
-        __syncthreads();
+    if (threadIdx.x == kScanThreads - 1) {
+        a.tile_prefix[blockIdx.x] = excl + tot;
+        __threadfence();
+        is_last = atomicAdd(a.scan_done, 1u) == gridDim.x - 1 ? 1u : 0u;
     }
-    if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry_s;
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    uint32_t carry = 0;
+    for (uint32_t b0 = 0; b0 < a.n_tiles; b0 += kScanThreads) {
+        const uint32_t i = b0 + threadIdx.x;
+        const uint32_t t = i < a.n_tiles ? a.tile_prefix[i] : 0u;
+        const uint32_t inc = wave_inclusive_scan(t, lane);
+        __syncthreads();                       // wave_tot of the previous round is read
+        if (lane == kWave - 1) wave_tot[wave] = inc;
+        __syncthreads();
+        uint32_t pre = 0, all = 0;
+        for (int w2 = 0; w2 < kScanThreads / kWave; ++w2) {
+            if (w2 < wave) pre += wave_tot[w2];
+            all += wave_tot[w2];
+        }
+        if (i < a.n_tiles) a.tile_prefix[i] = carry + pre + inc - t;
+        carry += all;
+    }
+    if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry;
 }
 
 // Each wave covers the range [e0, e0 + kGatherChunk) of the row-sorted entry
@@ -717,6 +894,23 @@ hipError_t anchor_dispatch_vec(const KArgs& a, const LaunchShape& s, dim3 grid, 
     }
 }
 
+template <typename T, int VEC, int NV>
+hipError_t sliced_launch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((da_backward_sliced_kernel<T, VEC, NV>), grid, dim3(kWave * s.waves),
+                       s.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t sliced_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    switch (s.nvc) {
+        case 1: return sliced_launch<T, VEC, 1>(a, s, grid, st);
+        case 2: return sliced_launch<T, VEC, 2>(a, s, grid, st);
+        case 4: return sliced_launch<T, VEC, 4>(a, s, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int VEC>
 hipError_t gather_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
     // C <= 1024 in the backward: 16-byte vectors need at most 4 per lane
@@ -767,15 +961,14 @@ hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t
 
 hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                                   bool bf16, hipStream_t stream) {
-    hipError_t e = launch_fill_zero(a.cnt, a.n_rows, stream);
+    // the scan counter and the row counts are one zeroed range
+    hipError_t e = launch_fill_zero(a.scan_done, (int64_t)(a.cnt - a.scan_done) + a.n_rows, stream);
     if (e != hipSuccess) return e;
-    const dim3 cgrid(blocks_for((int64_t)a.A * a.P, 256), (unsigned)(a.K * a.S),
+    const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
-    hipLaunchKernelGGL(count_kernel, cgrid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(count_kernel, cgrid, dim3(kCountThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_tile_totals_kernel, dim3(1), dim3(1024), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!a.accumulate) {
         const int64_t zwaves = ((int64_t)a.n_rows + kWave - 1) / kWave;
@@ -786,14 +979,29 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
             hipLaunchKernelGGL((zero_empty_rows_kernel<1>), zgrid, dim3(256), 0, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)n_anchors_total, 1);
-    if (bf16)
-        e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(a, s, grid, stream)
-                       : anchor_dispatch_scalar<uint16_t, false>(a, s, grid, stream);
-    else
-        e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(a, s, grid, stream)
-                       : anchor_dispatch_scalar<float, false>(a, s, grid, stream);
-    if (e != hipSuccess) return e;
+    if (a.sliced) {
+        const dim3 grid((unsigned)(n_anchors_total * kSlices), 1);
+        if (bf16)
+            e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(a, s, grid, stream)
+                           : sliced_dispatch<uint16_t, 1>(a, s, grid, stream);
+        else
+            e = s.vec == 4 ? sliced_dispatch<float, 4>(a, s, grid, stream)
+                           : sliced_dispatch<float, 1>(a, s, grid, stream);
+        if (e != hipSuccess) return e;
+        int64_t blocks = blocks_for((int64_t)a.n_anchors * a.npk, 256);
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(loc_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        const dim3 grid((unsigned)n_anchors_total, 1);
+        if (bf16)
+            e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(a, s, grid, stream)
+                           : anchor_dispatch_scalar<uint16_t, false>(a, s, grid, stream);
+        else
+            e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(a, s, grid, stream)
+                           : anchor_dispatch_scalar<float, false>(a, s, grid, stream);
+        if (e != hipSuccess) return e;
+    }
     // one wave per chunk of the largest possible entry count (4 per sample);
     // waves past the real total return at once
     const int64_t waves = ((int64_t)a.n_samples * 4 + kGatherChunk - 1) / kGatherChunk;

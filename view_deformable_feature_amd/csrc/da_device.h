@@ -144,6 +144,44 @@ __device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int 
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// v from lane (DPP control `ctrl`) in the rows of `row_mask`, 0 in the others.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, row_mask, 0xF, false));
+}
+
+// Sum of v over each aligned group of n lanes (n a power of two, 1..64, the same
+// in every lane).  The group's total ends up in its LAST lane; the other lanes
+// hold partial sums.  Only gfx9 data-parallel-primitive forms whose source
+// lane lies in the same group are used, so a group whose lanes are all active
+// is summed correctly whatever the other groups of the wave do:
+//   quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, xor 2), row_half_mirror
+//   (lane i <-> 7-i inside 8), row_mirror (i <-> 15-i inside 16): after these
+//   every lane of a 16-lane row holds the row's total; row_bcast:15 then adds
+//   row r-1's total into odd rows, and row_bcast:31 the total of rows 0-1 into
+//   rows 2-3.
+__device__ __forceinline__ float group_sum(float v, int n) {
+    if (n > 1) v += dpp<0xB1, 0xF>(v);     // quad_perm [1,0,3,2]
+    if (n > 2) v += dpp<0x4E, 0xF>(v);     // quad_perm [2,3,0,1]
+    if (n > 4) v += dpp<0x141, 0xF>(v);    // row_half_mirror
+    if (n > 8) v += dpp<0x140, 0xF>(v);    // row_mirror
+    if (n > 16) v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    if (n > 32) v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Sample j of level slice x (m levels): j = p * m + i takes point p at the
+// slice's i-th level (k, s); returns t = (p * K + k) * S + s.  The order is
+// fixed, so every sum over a slice's samples is deterministic.
+__device__ __forceinline__ int slice_sample(const KArgs& a, int x, int m, int j) {
+    const int p = j / m;
+    const int l = a.lv.slice_level[x][j - p * m];
+    const int k = l / a.S;
+    const int s = l - k * a.S;
+    return (p * a.K + k) * a.S + s;
+}
+
 // Launch-shape bookkeeping common to the per-anchor kernels: one workgroup per
 // (batch, anchor); row group rg = L consecutive lanes.
 struct AnchorCtx {

@@ -174,6 +174,151 @@ da_forward_kernel(KArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------------
+// forward by level slices
+// ------------------------------------------------------------------------------------
+// Workgroup (anchor, x) -- on XCD x -- sums the samples of the levels in slice
+// x only, in the fixed order of slice_sample(), and writes its partial output
+// row to fwd_part[x]; fwd_reduce_kernel then adds the 8 partials in slice
+// order.  Same staging, lane layout and two-deep pipeline as the per-anchor
+// kernel above.
+template <typename T, int VEC, int NV>
+__global__ void __launch_bounds__(kWave * kMaxWaves)
+da_forward_sliced_kernel(KArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int x = (int)(blockIdx.x % (uint32_t)kSlices);
+    const int64_t ba = blockIdx.x / (uint32_t)kSlices;
+    const int64_t b = ba / a.A;
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int L = a.L;
+    const int spw = kWave >> a.log2L;
+    const int rg = wave * spw + (lane >> a.log2L);
+    const int n_rg = (nthreads / kWave) * spw;
+    const int li = lane & (L - 1);
+    constexpr int kElem = (int)sizeof(T);
+
+    const int ns_max = a.sample_chunk;           // desc[ns_max] is the null descriptor
+    FwdDesc* desc = reinterpret_cast<FwdDesc*>(smem);
+    float* wts = reinterpret_cast<float*>(smem + (size_t)(ns_max + 1) * sizeof(FwdDesc));
+    float* red = wts + (size_t)ns_max * a.G;
+
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(
+        static_cast<const unsigned char*>(a.feat) + b * a.feat_batch_bytes, a.feat_image_bytes);
+
+    const int v0 = blockIdx.y * NV;
+    const uint32_t lane_off = (uint32_t)(li * VEC * kElem);
+    uint32_t soff[NV];
+    int gi[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        soff[i] = (uint32_t)(L * (v0 + i) * VEC * kElem);
+        gi[i] = (li + L * (v0 + i)) * VEC / a.D;
+    }
+    float acc[NV][VEC];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[i][e] = 0.0f;
+
+    if (tid == 0) desc[ns_max] = null_fwd_desc(a.feat_image_bytes);
+    const int m = a.lv.slice_nlev[x];
+    const int n = a.P * m;
+    const int64_t wbase = ba * (int64_t)a.npk * a.S * a.G;
+    for (int j0 = 0; j0 < n; j0 += ns_max) {
+        const int nsc = min(ns_max, n - j0);
+        for (int jj = tid; jj < nsc; jj += nthreads) {
+            const Stencil st = make_stencil(a, ba, slice_sample(a, x, m, j0 + jj));
+            FwdDesc d;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                d.off[i] = st.row[i] >= 0 ? (uint32_t)st.row[i] * (uint32_t)a.row_bytes
+                                          : a.feat_image_bytes;
+                d.cw[i] = st.cw[i];
+            }
+            desc[jj] = d;
+        }
+        for (int i = tid; i < nsc * a.G; i += nthreads) {
+            const int jj = i / a.G;
+            wts[i] = a.weights[wbase + (int64_t)slice_sample(a, x, m, j0 + jj) * a.G + (i - jj * a.G)];
+        }
+        __syncthreads();
+
+        int t = rg;
+        if (t < nsc) {
+            FwdDesc dA = desc[t], dB;
+            float vA[NV][4][VEC], vB[NV][4][VEC];
+            fwd_load<T, VEC, NV>(rsrc, dA, lane_off, soff, vA);
+            while (true) {
+                int tn = t + n_rg;
+                dB = desc[tn < nsc ? tn : ns_max];
+                fwd_load<T, VEC, NV>(rsrc, dB, lane_off, soff, vB);
+                fwd_accumulate<VEC, NV>(dA, wts + t * a.G, gi, vA, acc);
+                if (tn >= nsc) break;
+                t = tn;
+                tn = t + n_rg;
+                dA = desc[tn < nsc ? tn : ns_max];
+                fwd_load<T, VEC, NV>(rsrc, dA, lane_off, soff, vA);
+                fwd_accumulate<VEC, NV>(dB, wts + t * a.G, gi, vB, acc);
+                if (tn >= nsc) break;
+                t = tn;
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            for (int mk = L; mk < kWave; mk <<= 1) acc[i][e] += xor_shfl(acc[i][e], mk);
+    const int nch = NV * L * VEC;
+    if (lane < L) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) red[wave * nch + (li + L * i) * VEC + e] = acc[i][e];
+    }
+    __syncthreads();
+    const int nwaves = nthreads / kWave;
+    float* prow = a.fwd_part + ((int64_t)x * a.n_anchors + ba) * a.C + (int64_t)v0 * L * VEC;
+    for (int c = tid; c < nch; c += nthreads) {
+        float sum = 0.0f;
+        for (int w = 0; w < nwaves; ++w) sum += red[w * nch + c];
+        prow[c] = sum;
+    }
+}
+
+// out = sum of the 8 slice partials, added in slice order.
+__global__ void __launch_bounds__(256) fwd_reduce_kernel(KArgs a) {
+    const int64_t n = (int64_t)a.n_anchors * a.C;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float s = 0.0f;
+#pragma unroll
+        for (int x = 0; x < kSlices; ++x) s += a.fwd_part[x * n + i];
+        a.out[i] = s;
+    }
+}
+
+template <typename T, int VEC, int NV>
+hipError_t fwd_sliced_launch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((da_forward_sliced_kernel<T, VEC, NV>), grid, dim3(kWave * s.waves),
+                       s.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t fwd_sliced_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    switch (s.nvc) {
+        case 1: return fwd_sliced_launch<T, VEC, 1>(a, s, grid, st);
+        case 2: return fwd_sliced_launch<T, VEC, 2>(a, s, grid, st);
+        case 4: return fwd_sliced_launch<T, VEC, 4>(a, s, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, int VEC, int NV>
 hipError_t fwd_launch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((da_forward_kernel<T, VEC, NV>), grid, dim3(kWave * s.waves), s.lds_bytes,
@@ -197,6 +342,23 @@ hipError_t fwd_dispatch_nv(const KArgs& a, const LaunchShape& s, dim3 grid, hipS
 }
 
 }  // namespace
+
+hipError_t launch_forward_sliced(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
+                                 bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)(n_anchors_total * kSlices), (unsigned)s.chunks);
+    hipError_t e;
+    if (bf16)
+        e = s.vec == 8 ? fwd_sliced_dispatch<uint16_t, 8>(a, s, grid, stream)
+                       : fwd_sliced_dispatch<uint16_t, 1>(a, s, grid, stream);
+    else
+        e = s.vec == 4 ? fwd_sliced_dispatch<float, 4>(a, s, grid, stream)
+                       : fwd_sliced_dispatch<float, 1>(a, s, grid, stream);
+    if (e != hipSuccess) return e;
+    int64_t blocks = ((int64_t)a.n_anchors * a.C + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total, bool bf16,
                           hipStream_t stream) {

@@ -18,8 +18,10 @@ constexpr int kLdsBudget = 48 * 1024;
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr int kScanTile = kScanThreads * kScanItems;   // 4096
-// Levels with at most this many rows are counted in an LDS histogram first.
-constexpr int kCountLdsRows = 4096;
+// Levels with at most this many rows (no more than the corners one counting
+// workgroup takes) are counted in an LDS histogram first.
+constexpr int kCountThreads = 256;
+constexpr int kCountLdsRows = 4 * kCountThreads;
 // Entries covered by one wave of the feature-gradient gather, and the longest
 // row a single wave sums whole (longer rows are added range by range).
 constexpr int kGatherChunk = 64;
@@ -37,11 +39,21 @@ struct Entry {
 static_assert(sizeof(Entry) == 16, "Entry layout");
 constexpr uint32_t kEntryLongRow = 0x80000000u;
 
+// Level slices.  MI355X dispatches workgroup i to XCD i mod 8, and each XCD has
+// its own L2.  When the features outgrow one L2, the per-anchor kernels run 8
+// workgroups per anchor; workgroup (anchor, x) takes only the samples of the
+// levels in slice x, so each XCD's L2 serves only its slice's levels.
+constexpr int kSlices = 8;
+constexpr int kMaxSliceLevels = kMaxLevels / kSlices;   // 8
+
 // (H, W, first row) of every (camera, scale) level, camera-major.
 struct LevelTable {
     int32_t H[kMaxLevels];
     int32_t W[kMaxLevels];
     int32_t start[kMaxLevels];
+    // slice x holds levels slice_level[x][0 .. slice_nlev[x]) (used when sliced)
+    int8_t slice_level[kSlices][kMaxSliceLevels];
+    int8_t slice_nlev[kSlices];
 };
 
 // Everything a launch needs.  The per-anchor kernels run one workgroup per
@@ -59,11 +71,18 @@ struct KArgs {
     float* grad_loc;           // [bs, A, P, K, 2]
     float* grad_weights;       // [bs, A, P, K, S, G]
     // feature-gradient gather workspace
+    uint32_t* scan_done;       // tiles scanned so far (zeroed with cnt, which follows it)
     uint32_t* cnt;             // [n_rows] entries per row, then per-row rank source
     uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile
     uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
     uint32_t* rank;            // [4 * n_samples] rank of (sample, corner) inside its row
     Entry* entries;            // [4 * n_samples] row-sorted entries
+    // sliced per-anchor kernels
+    float* fwd_part;           // [kSlices, bs*A, C] forward partial sums, one per slice
+    float* loc_part;           // [n_samples, 2] location-gradient partial of every sample
+    int32_t sliced;            // 1: 8 workgroups per anchor, one per level slice
+    int32_t max_slice_samples; // P * max over slices of the slice's level count
+    int32_t sample_chunk;      // sliced kernels: samples staged in LDS at once
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
@@ -104,6 +123,10 @@ constexpr int kBwdDescBytes = 80;   // 4 feat offsets + 4 grad offsets + 3 x 4 c
 
 hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                           bool bf16, hipStream_t stream);
+// Forward by level slices: per-slice partials into a.fwd_part, then their sum
+// in fixed slice order into a.out.
+hipError_t launch_forward_sliced(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
+                                 bool bf16, hipStream_t stream);
 // Backward, scatter form: grad_feat must already hold zeros (or the sum to add to).
 hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                                    bool bf16, hipStream_t stream);
