@@ -71,8 +71,8 @@ def copy_calibration(nbytes):
 
 FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
 BWD_KERNELS = ("da_backward call: fill_zero_kernel, count_kernel, scan_tiles_kernel, "
-               "zero_empty_rows_kernel, da_backward_sliced_kernel, "
-               "loc_reduce_kernel, gather_kernel")
+               "da_backward_sliced_kernel (+ zeroing blocks), "
+               "gather_kernel (+ location-sum blocks)")
 
 
 def algorithmic_bytes(wl):

@@ -184,9 +184,48 @@ __device__ __forceinline__ void store_grad_weights(float (&gwp)[NV], const int (
     }
 }
 
+// Zero the feature-gradient rows r0 .. r0+63 (r0 = 64 w) that have no entry,
+// and the long rows that gather_kernel adds to range by range.
+template <int ZVEC>
+__device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int lane) {
+    const uint32_t r0 = w * (uint32_t)kWave;
+    if (r0 >= a.n_rows) return;
+    const uint32_t r = r0 + (uint32_t)lane;
+    const bool empty = r < a.n_rows && (a.cnt[r] == 0u || a.cnt[r] > (uint32_t)kGatherLong);
+    uint64_t m = __ballot(empty);
+    const int nvec = a.C / ZVEC;
+    while (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        float* row = a.grad_feat + (size_t)(r0 + (uint32_t)l) * a.C;
+        for (int v = lane; v < nvec; v += kWave) {
+            if constexpr (ZVEC == 4)
+                reinterpret_cast<float4*>(row)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+            else
+                row[v] = 0.0f;
+        }
+    }
+}
+
+// The zeroing role of the blocks past anchor_blocks: 64 rows per wave.
+__device__ __forceinline__ void zero_rows_role(const KArgs& a) {
+    const uint32_t w = (blockIdx.x - a.anchor_blocks) * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (a.gather_vec == 4)
+        zero_rows_wave<4>(a, w, lane);
+    else
+        zero_rows_wave<1>(a, w, lane);
+}
+
 template <typename T, int VEC, int NV, bool SCATTER>
 __global__ void __launch_bounds__(kWave * kMaxWaves)
 da_backward_anchor_kernel(KArgs a) {
+    if constexpr (!SCATTER) {
+        if (blockIdx.x >= a.anchor_blocks) {
+            zero_rows_role(a);
+            return;
+        }
+    }
     static_assert(!SCATTER || VEC == 1, "the scatter form uses one channel per lane");
     extern __shared__ __align__(16) unsigned char smem[];
     const AnchorCtx x = anchor_ctx(a);
@@ -307,11 +346,15 @@ da_backward_anchor_kernel(KArgs a) {
 // slice x only, in the order of slice_sample().  Everything but the location
 // gradient is per sample, as in the kernel above.  A point-camera pair's
 // scales are spread over slices, so each sample's location partial (summed
-// over the lanes of its row group) goes to loc_part[q], and loc_reduce_kernel
+// over the lanes of its row group) goes to loc_part[q], and loc_reduce_role
 // adds a pair's S partials in scale order.
 template <typename T, int VEC, int NV>
 __global__ void __launch_bounds__(kWave * kMaxWaves)
 da_backward_sliced_kernel(KArgs a) {
+    if (blockIdx.x >= a.anchor_blocks) {
+        zero_rows_role(a);
+        return;
+    }
     extern __shared__ __align__(16) unsigned char smem[];
     const int x = (int)(blockIdx.x % (uint32_t)kSlices);
     const int64_t ba = blockIdx.x / (uint32_t)kSlices;
@@ -406,20 +449,19 @@ da_backward_sliced_kernel(KArgs a) {
 }
 
 // grad_loc of each (anchor, point, camera) = sum of its S scale partials, in
-// scale order.
-__global__ void __launch_bounds__(256) loc_reduce_kernel(KArgs a) {
-    const int64_t n = (int64_t)a.n_anchors * a.npk;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+// scale order: the role of the gather launch's blocks past gather_blocks, one
+// thread per pair.
+__device__ __forceinline__ void loc_reduce_role(const KArgs& a) {
+    const int64_t i = (int64_t)(blockIdx.x - a.gather_blocks) * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)a.n_anchors * a.npk) return;
     const float2* part = reinterpret_cast<const float2*>(a.loc_part);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        float gx = 0.0f, gy = 0.0f;
-        for (int s = 0; s < a.S; ++s) {
-            const float2 v = part[i * a.S + s];
-            gx += v.x;
-            gy += v.y;
-        }
-        reinterpret_cast<float2*>(a.grad_loc)[i] = make_float2(gx, gy);
+    float gx = 0.0f, gy = 0.0f;
+    for (int s = 0; s < a.S; ++s) {
+        const float2 v = part[i * a.S + s];
+        gx += v.x;
+        gy += v.y;
     }
+    reinterpret_cast<float2*>(a.grad_loc)[i] = make_float2(gx, gy);
 }
 
 // ------------------------------------------------------------------------------------
@@ -605,6 +647,10 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 // batch ahead of the one being added up.
 template <int VEC, int NV>
 __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
+    if (blockIdx.x >= a.gather_blocks) {
+        loc_reduce_role(a);
+        return;
+    }
     constexpr int U = NV >= 8 ? 1 : 8 / NV;   // entries per batch, within the register budget
     constexpr uint32_t kNone = 0xffffffffu;
     static_assert(kGatherChunk == kWave && kGatherLong <= kGatherChunk, "window layout");
@@ -803,32 +849,6 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     flush(cur);
 }
 
-// Rows no sample touches, and the long rows that gather_kernel adds to piece
-// by piece: zero them (short rows are written whole by gather_kernel).  One
-// wave per 64 rows.
-template <int VEC>
-__global__ void __launch_bounds__(256) zero_empty_rows_kernel(KArgs a) {
-    const uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-    const int lane = threadIdx.x % kWave;
-    const uint32_t r0 = w * (uint32_t)kWave;
-    if (r0 >= a.n_rows) return;
-    const uint32_t r = r0 + (uint32_t)lane;
-    // rows with no entry, and the long rows gather_kernel adds to piece by piece
-    const bool empty = r < a.n_rows && (a.cnt[r] == 0u || a.cnt[r] > (uint32_t)kGatherLong);
-    uint64_t m = __ballot(empty);
-    const int nvec = a.C / VEC;
-    while (m) {
-        const int l = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        float* row = a.grad_feat + (size_t)(r0 + (uint32_t)l) * a.C;
-        for (int v = lane; v < nvec; v += kWave) {
-            if constexpr (VEC == 4)
-                reinterpret_cast<float4*>(row)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-            else
-                row[v] = 0.0f;
-        }
-    }
-}
 
 // ------------------------------------------------------------------------------------
 // launch helpers
@@ -954,9 +974,11 @@ hipError_t launch_fill_zero(void* p, int64_t n_words, hipStream_t stream) {
 
 hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                                    bool bf16, hipStream_t stream) {
+    KArgs k = a;
+    k.anchor_blocks = (uint32_t)n_anchors_total;
     const dim3 grid((unsigned)n_anchors_total, 1);
-    return bf16 ? anchor_dispatch_scalar<uint16_t, true>(a, s, grid, stream)
-                : anchor_dispatch_scalar<float, true>(a, s, grid, stream);
+    return bf16 ? anchor_dispatch_scalar<uint16_t, true>(k, s, grid, stream)
+                : anchor_dispatch_scalar<float, true>(k, s, grid, stream);
 }
 
 hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
@@ -970,44 +992,37 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (!a.accumulate) {
-        const int64_t zwaves = ((int64_t)a.n_rows + kWave - 1) / kWave;
-        const dim3 zgrid(blocks_for(zwaves, 256 / kWave));
-        if (a.gather_vec == 4)
-            hipLaunchKernelGGL((zero_empty_rows_kernel<4>), zgrid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((zero_empty_rows_kernel<1>), zgrid, dim3(256), 0, stream, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    // per-anchor kernel, followed (unless accumulating) by blocks that zero the
+    // rows the gather does not store whole
+    KArgs k = a;
+    k.anchor_blocks = (uint32_t)(a.sliced ? n_anchors_total * kSlices : n_anchors_total);
+    const int64_t zwaves = a.accumulate ? 0 : ((int64_t)a.n_rows + kWave - 1) / kWave;
+    const dim3 grid((unsigned)(k.anchor_blocks + blocks_for(zwaves, s.waves)), 1);
     if (a.sliced) {
-        const dim3 grid((unsigned)(n_anchors_total * kSlices), 1);
         if (bf16)
-            e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(a, s, grid, stream)
-                           : sliced_dispatch<uint16_t, 1>(a, s, grid, stream);
+            e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(k, s, grid, stream)
+                           : sliced_dispatch<uint16_t, 1>(k, s, grid, stream);
         else
-            e = s.vec == 4 ? sliced_dispatch<float, 4>(a, s, grid, stream)
-                           : sliced_dispatch<float, 1>(a, s, grid, stream);
-        if (e != hipSuccess) return e;
-        int64_t blocks = blocks_for((int64_t)a.n_anchors * a.npk, 256);
-        if (blocks > 65536) blocks = 65536;
-        hipLaunchKernelGGL(loc_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+            e = s.vec == 4 ? sliced_dispatch<float, 4>(k, s, grid, stream)
+                           : sliced_dispatch<float, 1>(k, s, grid, stream);
     } else {
-        const dim3 grid((unsigned)n_anchors_total, 1);
         if (bf16)
-            e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(a, s, grid, stream)
-                           : anchor_dispatch_scalar<uint16_t, false>(a, s, grid, stream);
+            e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(k, s, grid, stream)
+                           : anchor_dispatch_scalar<uint16_t, false>(k, s, grid, stream);
         else
-            e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(a, s, grid, stream)
-                           : anchor_dispatch_scalar<float, false>(a, s, grid, stream);
-        if (e != hipSuccess) return e;
+            e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(k, s, grid, stream)
+                           : anchor_dispatch_scalar<float, false>(k, s, grid, stream);
     }
-    // one wave per chunk of the largest possible entry count (4 per sample);
-    // waves past the real total return at once
+    if (e != hipSuccess) return e;
+    // gather: one wave per chunk of the largest possible entry count (4 per
+    // sample; waves past the real total return at once), followed in the
+    // sliced form by blocks that add up the location partials
     const int64_t waves = ((int64_t)a.n_samples * 4 + kGatherChunk - 1) / kGatherChunk;
-    const dim3 ggrid(blocks_for(waves, 256 / kWave));
-    return a.gather_vec == 4 ? gather_dispatch<4>(a, s, ggrid, stream)
-                             : gather_dispatch<1>(a, s, ggrid, stream);
+    k.gather_blocks = blocks_for(waves, 256 / kWave);
+    const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, 256) : 0;
+    const dim3 ggrid((unsigned)(k.gather_blocks + lr));
+    return a.gather_vec == 4 ? gather_dispatch<4>(k, s, ggrid, stream)
+                             : gather_dispatch<1>(k, s, ggrid, stream);
 }
 
 }  // namespace da

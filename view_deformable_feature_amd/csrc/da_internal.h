@@ -84,6 +84,11 @@ struct KArgs {
     int32_t sliced;            // 1: 8 workgroups per anchor, one per level slice
     int32_t max_slice_samples; // P * max over slices of the slice's level count
     int32_t sample_chunk;      // sliced kernels: samples staged in LDS at once
+    // Blocks past anchor_blocks of a gather-form per-anchor launch zero the
+    // feature-gradient rows that need it; blocks past gather_blocks of the
+    // gather launch add up the location partials (sliced form).
+    uint32_t anchor_blocks;
+    uint32_t gather_blocks;
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
