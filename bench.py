@@ -71,8 +71,8 @@ def copy_calibration(nbytes):
 
 FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
 BWD_KERNELS = ("da_backward call: fill_zero_kernel, count_kernel, scan_tiles_kernel, "
-               "da_backward_sliced_kernel (+ zeroing blocks), "
-               "gather_kernel (+ location-sum blocks)")
+               "bucket_kernel (+ zeroing blocks), gather_kernel (+ group dot products), "
+               "finalize_kernel")
 
 
 def algorithmic_bytes(wl):

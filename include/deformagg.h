@@ -87,6 +87,11 @@ typedef enum {
  */
 #define DA_FLAG_SLICES_ALWAYS 1  /* slice whatever the sizes (where the lane layout allows) */
 #define DA_FLAG_SLICES_NEVER 2   /* one workgroup per anchor                                */
+/* Backward form (see da_backward): by default the location and weight gradients
+ * come from dot products formed while the feature gradient is gathered in row
+ * order; this flag selects the per-anchor kernels that gather the corner rows
+ * again instead (always used where the row-ordered form does not apply). */
+#define DA_FLAG_BWD_REGATHER 4
 
 /* Problem sizes.  bs, num_anchors and num_pts may be 0 (then there is nothing to
  * sample: out and grad_feat are filled with zeros).  All other sizes are >= 1,
@@ -101,7 +106,7 @@ typedef struct {
     int64_t num_scale;    /* S                                             */
     int64_t num_groups;   /* G, weight groups over the channels            */
     int32_t feat_dtype;   /* da_dtype                                      */
-    int32_t flags;        /* 0 or one DA_FLAG_SLICES_* value               */
+    int32_t flags;        /* DA_FLAG_* bits (SLICES_ALWAYS and _NEVER exclusive) */
 } da_problem;
 
 /*

@@ -47,17 +47,19 @@ def gpu_forward(dev, slices=None, workspace=None):
     return out
 
 
-def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices=None):
+def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices=None,
+                 regather=False):
+    """regather: the per-anchor backward form instead of the row-ordered one."""
     import view_deformable_feature_amd as vdf
     args = (dev["feat"], dev["spatial_shape"], dev["scale_start_index"], dev["loc"],
             dev["weights"], dev["grad_out"])
     if atomic:
         r = vdf.da_backward_atomic(*args)
     elif accumulate_into is None:
-        r = vdf.da_backward(*args, workspace=workspace, slices=slices)
+        r = vdf.da_backward(*args, workspace=workspace, slices=slices, regather=regather)
     else:
         r = vdf.da_backward_accumulate(*args, accumulate_into, workspace=workspace,
-                                       slices=slices)
+                                       slices=slices, regather=regather)
     torch.cuda.synchronize()
     return r
 

@@ -87,7 +87,8 @@ def _msg(lib):
     (dict(num_pts=-1), 1, ">= 0"),
     (dict(feat_dtype=7), 1, "feat_dtype"),
     (dict(flags=3), 1, "flags"),
-    (dict(flags=4), 1, "flags"),
+    (dict(flags=7), 1, "flags"),
+    (dict(flags=8), 1, "flags"),
     (dict(flags=-1), 1, "flags"),
     (dict(num_feat=255), 1, "inside num_feat"),
     (dict(num_cams=9, num_scale=8), 1, "DA_MAX_LEVELS"),
@@ -200,9 +201,16 @@ def test_workspace_size_and_checks(lib):
     p = _prob()
     assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     # scan counter + counts + local prefix + tile prefix + ranks + 16-byte entries + location
-    # partials, each 256-aligned
+    # partials + per-corner group dot products (row-ordered form, G = 1), each 256-aligned
     n_rows, n_samples = 256, 8 * 4
-    expect = 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256
+    expect = 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256 + 512
+    assert lib.da_backward_workspace_size(ctypes.byref(_prob(flags=4)), ctypes.byref(n)) == 0
+    assert n.value == expect - 512                       # per-anchor form: no dot products
+    # C/G = 24 channels per group: 6 lanes per group, not a power of two -> per-anchor form
+    assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_embeds=48, num_groups=2)),
+                                          ctypes.byref(n)) == 0
+    assert n.value == 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256
+    assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value == expect
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_pts=0)), ctypes.byref(n)) == 0
     assert n.value == 0

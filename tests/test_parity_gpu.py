@@ -22,13 +22,20 @@ def _args(inp):
     return [inp[k] for k in KEYS]
 
 
-def _full_check(inp, tol_f, tol_b, label, slices=None):
+# (level slices, per-anchor backward): the library's choice, slices forced, and the
+# per-anchor backward form with and without slices
+MODES = {"auto": (None, False), "sliced": (True, False), "regather": (None, True),
+         "regather_sliced": (True, True), "regather_unsliced": (False, True),
+         "unsliced": (False, False)}
+
+
+def _full_check(inp, tol_f, tol_b, label, slices=None, regather=False):
     say(f"[parity] {label}: upload")
     dev = to_device(inp)
     say(f"[parity] {label}: forward (slices={slices})")
     out = gpu_forward(dev, slices=slices).cpu().numpy()
-    say(f"[parity] {label}: backward (slices={slices})")
-    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, slices=slices))
+    say(f"[parity] {label}: backward (slices={slices}, regather={regather})")
+    gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, slices=slices, regather=regather))
     say(f"[parity] {label}: oracle")
     r_out = oracle.forward(*_args(inp))
     r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
@@ -44,10 +51,10 @@ def _full_check(inp, tol_f, tol_b, label, slices=None):
 # the five workloads
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_tiny_full(slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather", "regather_sliced"])
+def test_tiny_full(mode):
     inp = W.make_inputs(W.WORKLOADS["tiny"])
-    _full_check(inp, TOL_FWD, TOL_BWD, "tiny", slices)
+    _full_check(inp, TOL_FWD, TOL_BWD, "tiny", *MODES[mode])
 
 
 # nuScenes-shaped workloads take level slices by default (92 MB of features, 24 levels)
@@ -63,13 +70,14 @@ def test_nuscenes_forward_full(slices):
     assert np.array_equal(out, out2), "forward is not deterministic"
 
 
-@pytest.mark.parametrize("slices", [None, False], ids=["auto", "unsliced"])
-def test_nuscenes_backward_full(slices):
+@pytest.mark.parametrize("mode", ["auto", "regather", "regather_unsliced"])
+def test_nuscenes_backward_full(mode):
+    slices, regather = MODES[mode]
     inp = W.make_inputs(W.WORKLOADS["nuscenes_bwd"])
     dev = to_device(inp)
-    say(f"[parity] nuscenes_bwd: backward x2 (slices={slices})")
-    r1 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices)]
-    r2 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices)]
+    say(f"[parity] nuscenes_bwd: backward x2 ({mode})")
+    r1 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices, regather=regather)]
+    r2 = [t.cpu().numpy() for t in gpu_backward(dev, slices=slices, regather=regather)]
     ref = oracle.backward(*_args(inp), inp["grad_out"])
     for run, r in (("run1", r1), ("run2", r2)):
         for name, g, rr in zip(("grad_feat", "grad_loc", "grad_weights"), r, ref):
@@ -80,13 +88,14 @@ def test_nuscenes_backward_full(slices):
         f"{np.abs(r1[0] - r2[0]).max():.3e}")
 
 
-def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=None):
+def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=None,
+                   regather=False):
     say(f"[parity] {wl.name}: generate")
     inp = W.make_inputs(wl)
     dev = to_device(inp)
-    say(f"[parity] {wl.name}: forward + backward (slices={slices})")
+    say(f"[parity] {wl.name}: forward + backward (slices={slices}, regather={regather})")
     out = gpu_forward(dev, slices=slices)
-    gf, gl, gw = gpu_backward(dev, slices=slices)
+    gf, gl, gw = gpu_backward(dev, slices=slices, regather=regather)
     rng = np.random.default_rng(seed)
     ids = rng.choice(wl.bs * wl.anchors, size=n_anchor, replace=False)
     ids.sort()
@@ -117,13 +126,17 @@ def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=Non
     say(f"[parity] {wl.name}: ok ({touched.size} touched rows)")
 
 
-@pytest.mark.parametrize("slices", [None, False], ids=["auto", "unsliced"])
-def test_large_sampled(slices):
-    _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD, slices=slices)
+@pytest.mark.parametrize("mode", ["auto", "regather", "regather_unsliced"])
+def test_large_sampled(mode):
+    slices, regather = MODES[mode]
+    _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD, slices=slices, regather=regather)
 
 
-def test_large_bf16_sampled():
-    _sampled_check(W.WORKLOADS["large_bf16"], TOL_BF16, TOL_BF16)
+@pytest.mark.parametrize("mode", ["auto", "regather"])
+def test_large_bf16_sampled(mode):
+    slices, regather = MODES[mode]
+    _sampled_check(W.WORKLOADS["large_bf16"], TOL_BF16, TOL_BF16, slices=slices,
+                   regather=regather)
 
 
 # ---------------------------------------------------------------------------------------
@@ -159,12 +172,12 @@ RAGGED = [
 
 @pytest.mark.parametrize("name, kw", RAGGED, ids=[r[0] for r in RAGGED])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_ragged_full(name, kw, dtype, slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather", "regather_sliced"])
+def test_ragged_full(name, kw, dtype, mode):
     wl = W.custom(f"{name}_{dtype}", feat_dtype=dtype, seed=zlib.crc32(name.encode()) % 1000, **kw)
     inp = W.make_inputs(wl)
     tol_f, tol_b = (TOL_BF16, TOL_BF16) if dtype == "bf16" else (TOL_FWD, TOL_BWD)
-    _full_check(inp, tol_f, tol_b, wl.name, slices)
+    _full_check(inp, tol_f, tol_b, wl.name, *MODES[mode])
 
 
 def test_per_camera_pyramids_and_permuted_level_order():
@@ -248,8 +261,8 @@ def test_no_points_and_empty_batches(slices):
         assert torch.count_nonzero(gf) == 0
 
 
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_nan_and_far_locations_contribute_nothing(slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+def test_nan_and_far_locations_contribute_nothing(mode):
     wl = W.custom("nanloc", bs=1, num_cams=2, levels=((8, 8), (4, 4)), C=32, groups=2,
                   anchors=10, pts=4, loc_lo=-0.1, loc_hi=1.1, seed=5)
     inp = W.make_inputs(wl)
@@ -258,7 +271,7 @@ def test_nan_and_far_locations_contribute_nothing(slices):
     loc[0, :, 1, :, 1] = np.inf
     loc[0, :, 2, :, :] = -3e38
     inp["loc"] = loc
-    _full_check(inp, TOL_FWD, TOL_BWD, "nanloc", slices)
+    _full_check(inp, TOL_FWD, TOL_BWD, "nanloc", *MODES[mode])
 
 
 def test_max_extent_levels():
@@ -273,14 +286,16 @@ def test_max_extent_levels():
     _full_check(W.make_inputs(wl), TOL_FWD, TOL_BWD, "maxext_w")
 
 
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_accumulate_adds_into_existing_gradient(slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+def test_accumulate_adds_into_existing_gradient(mode):
+    slices, regather = MODES[mode]
     inp = W.make_inputs(W.custom("acc", bs=1, num_cams=2, levels=((10, 12), (5, 6)), C=64,
                                  groups=4, anchors=17, pts=5, loc_lo=-0.1, loc_hi=1.1, seed=12))
     dev = to_device(inp)
     base = torch.randn(tuple(dev["feat"].shape), device="cuda", generator=None)
-    gf0, gl0, gw0 = gpu_backward(dev, slices=slices)
-    gf1, gl1, gw1 = gpu_backward(dev, accumulate_into=base.clone(), slices=slices)
+    gf0, gl0, gw0 = gpu_backward(dev, slices=slices, regather=regather)
+    gf1, gl1, gw1 = gpu_backward(dev, accumulate_into=base.clone(), slices=slices,
+                                 regather=regather)
     assert_close("accumulate", gf1.cpu().numpy(), (base + gf0).cpu().numpy(), 1e-6)
     assert torch.equal(gl0, gl1) and torch.equal(gw0, gw1)
 
@@ -346,18 +361,20 @@ def test_backward_atomic_form_ragged_bf16():
     assert_close("atomic bf16 grad_weights", gw, r_gw, TOL_BF16)
 
 
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_workspace_reused_across_calls(slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+def test_workspace_reused_across_calls(mode):
     """One caller-owned workspace serves two calls in a row, the second smaller; its
     stale contents from the first call must not leak into the second.  Same for the
     forward's workspace."""
     import view_deformable_feature_amd as vdf
+    slices, regather = MODES[mode]
     big = W.make_inputs(W.custom("ws_big", bs=2, num_cams=2, levels=((20, 30), (10, 15)), C=64,
                                  groups=4, anchors=40, pts=7, loc_lo=-0.1, loc_hi=1.1, seed=51))
     small = W.make_inputs(W.custom("ws_small", bs=1, num_cams=2, levels=((6, 9), (3, 5)), C=64,
                                    groups=4, anchors=9, pts=3, loc_lo=-0.1, loc_hi=1.1, seed=52))
     dev_b, dev_s = to_device(big), to_device(small)
-    n = vdf.workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"], dev_b["weights"])
+    n = vdf.workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"], dev_b["weights"],
+                           regather=regather)
     ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
     nf = vdf.forward_workspace_size(dev_b["feat"], dev_b["spatial_shape"], dev_b["loc"],
                                     dev_b["weights"], slices=slices)
@@ -365,19 +382,20 @@ def test_workspace_reused_across_calls(slices):
     for inp, dev in ((big, dev_b), (small, dev_s), (big, dev_b)):
         out = gpu_forward(dev, slices=slices, workspace=fws).cpu().numpy()
         assert_close("ws out", out, oracle.forward(*_args(inp)), TOL_FWD)
-        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, workspace=ws, slices=slices))
+        gf, gl, gw = (t.cpu().numpy() for t in gpu_backward(dev, workspace=ws, slices=slices,
+                                                             regather=regather))
         r_gf, r_gl, r_gw = oracle.backward(*_args(inp), inp["grad_out"])
         assert_close("ws grad_feat", gf, r_gf, TOL_BWD)
         assert_close("ws grad_loc", gl, r_gl, TOL_BWD)
         assert_close("ws grad_weights", gw, r_gw, TOL_BWD)
 
 
-@pytest.mark.parametrize("slices", [None, True], ids=["auto", "sliced"])
-def test_hot_rows_span_many_chunks(slices):
+@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+def test_hot_rows_span_many_chunks(mode):
     """A 2x3 level hit by 4000 samples: each of its rows collects thousands of
     feature-gradient terms, far more than one wave's chunk of the row-sorted list,
     next to a large level with a few terms per row."""
     wl = W.custom("hot_rows", bs=2, num_cams=2, levels=((2, 3), (40, 60)), C=64, groups=4,
                   anchors=250, pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)
     inp = W.make_inputs(wl)
-    _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows", slices)
+    _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows", *MODES[mode])

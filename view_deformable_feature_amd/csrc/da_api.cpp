@@ -51,7 +51,7 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
                        const int32_t* start, const float* loc, const float* weights,
                        Plan& plan) {
     if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
-    if ((p->flags & ~(DA_FLAG_SLICES_ALWAYS | DA_FLAG_SLICES_NEVER)) != 0 ||
+    if ((p->flags & ~(DA_FLAG_SLICES_ALWAYS | DA_FLAG_SLICES_NEVER | DA_FLAG_BWD_REGATHER)) != 0 ||
         (p->flags & DA_FLAG_SLICES_ALWAYS && p->flags & DA_FLAG_SLICES_NEVER))
         return fail(DA_ERR_INVALID_ARG, "problem.flags = %d is not a valid combination",
                     (int)p->flags);
@@ -345,14 +345,31 @@ da_status hip_status(hipError_t e, const char* what) {
     return fail(DA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The row-ordered backward applies when 4 channels per lane fit the groups
+// (C/G a multiple of 4 with C/G/4 a power of two, at most 1024 channels), there
+// are at most 16 weight groups, and all batch images together are addressable
+// by one 32-bit buffer range.  Only sizes and flags are read.
+bool fused_capable(const da_problem* p) {
+    if (p->flags & DA_FLAG_BWD_REGATHER) return false;
+    const int64_t C = p->num_embeds, G = p->num_groups;
+    if (G < 1 || C % G != 0) return false;
+    const int64_t D = C / G;
+    if (C % 4 != 0 || D % 4 != 0 || C > 1024 || G > 16) return false;
+    const int64_t seg = D / 4;
+    if (seg > 64 || (seg & (seg - 1)) != 0) return false;
+    const uint64_t elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    const uint64_t all = (uint64_t)p->bs * (uint64_t)p->num_feat * (uint64_t)C * elem;
+    return all + 2 * (uint64_t)C * elem <= kU32Max;
+}
+
 // Workspace of the gather form of the backward, each part 256-byte aligned.
 struct WsLayout {
-    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, total;
+    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, dots, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
+WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups) {
     WsLayout w;
     const uint64_t n_tiles = (n_rows + da::kScanTile - 1) / da::kScanTile;
     size_t off = 0;
@@ -370,6 +387,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples) {
     off += align256(n_samples * 4 * sizeof(da::Entry));
     w.loc_part = off;
     off += align256(n_samples * 8);
+    w.dots = off;
+    off += align256(n_samples * 4 * dot_groups * 4);
     w.total = off;
     return w;
 }
@@ -426,7 +445,8 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
         st = gather_sizes(p, n_rows, n_samples);
         if (st != DA_OK) return st;
         if (any_sample) {
-            const WsLayout w = ws_layout(n_rows, n_samples);
+            const bool fusable = fused_capable(p);
+            const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0);
             if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
             if (!aligned(workspace, 256))
                 return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -448,7 +468,16 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.num_feat = (int32_t)p->num_feat;
             ka.accumulate = mode == BwdMode::kGatherAccumulate ? 1 : 0;
             if (ka.gather_vec == 4 && !aligned(grad_feat, 16)) ka.gather_vec = 1;
-            plan_backward_sliced(p, plan);
+            if (fusable && ka.gather_vec == 4 && aligned(feat, 16)) {
+                ka.fused = 1;
+                ka.dots = reinterpret_cast<float*>(base + w.dots);
+                ka.feat_all_bytes =
+                    (uint32_t)((uint64_t)p->bs * p->num_feat * p->num_embeds * (plan.bf16 ? 2 : 4));
+                ka.w_vec4 = p->num_groups % 4 == 0 && aligned(weights, 16) &&
+                            aligned(grad_weights, 16);
+            } else {
+                plan_backward_sliced(p, plan);
+            }
         }
     }
     // the scatter form adds into zeros; the gather form zeroes only the rows no
@@ -525,7 +554,9 @@ da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
     uint64_t n_rows = 0, n_samples = 0;
     const da_status st = gather_sizes(p, n_rows, n_samples);
     if (st != DA_OK) return st;
-    *bytes = n_samples == 0 ? 0 : ws_layout(n_rows, n_samples).total;
+    *bytes = n_samples == 0
+                 ? 0
+                 : ws_layout(n_rows, n_samples, fused_capable(p) ? (uint64_t)p->num_groups : 0).total;
     return DA_OK;
 }
 

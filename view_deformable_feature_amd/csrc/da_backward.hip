@@ -77,9 +77,6 @@ __device__ __forceinline__ BwdDesc null_bwd_desc(uint32_t outside, uint32_t gout
     return d;
 }
 
-__device__ __forceinline__ uint32_t row_first_entry(const KArgs& a, uint32_t flat_row) {
-    return a.tile_prefix[flat_row / (uint32_t)kScanTile] + a.local_start[flat_row];
-}
 
 // LDS descriptor of one sample: corner offsets and the per-corner factors of
 // the location gradient (section 4.1).
@@ -127,7 +124,7 @@ __device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st,
         e.row = fr[i] | (cn[i] > (uint32_t)kGatherLong ? kEntryLongRow : 0u);
         e.w_off = q * (uint32_t)a.G * 4u;
         e.cw = st.cw[i];
-        e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u;
+        e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u + (uint32_t)i;
         const uint32_t pos = first[i] + rks[i];
         if (st.row[i] >= 0 && pos < 4u * a.n_samples) a.entries[pos] = e;
     }
@@ -448,6 +445,111 @@ da_backward_sliced_kernel(KArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------------
+// row-ordered backward: bucketing, then (after the gather) the per-sample gradients
+// ------------------------------------------------------------------------------------
+// One thread per sample: its stencil, and its inside corners into the row-sorted
+// entry list.  Blocks past anchor_blocks zero the rows the gather does not
+// store whole.
+__global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
+    if (blockIdx.x >= a.anchor_blocks) {
+        zero_rows_role(a);
+        return;
+    }
+    const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= a.n_samples) return;
+    const uint32_t per_anchor = (uint32_t)(a.npk * a.S);
+    const uint32_t ba = q / per_anchor;
+    const int t = (int)(q - ba * per_anchor);
+    const uint32_t b = ba / (uint32_t)a.A;
+    const Stencil st = make_stencil(a, (int64_t)ba, t);
+    bucket_sample(a, st, (int64_t)b, (int64_t)ba, q);
+}
+
+// One thread per sample q: from the per-corner group dot products
+// d[c][g] = sum over the channels of group g of grad_out * corner value c (formed
+// by the gather), section 4.1's gradients --
+//   grad_weights[q][g] = sum_c cw_c d[c][g]
+//   grad_loc of q's (point, camera) = sum over its S scales of
+//                                     sum_c (dx_c, dy_c) * sum_g w[q][g] d[c][g]
+// with (dx_c, dy_c) the derivatives of the corner weights: W (-hh, hh, -lh, lh)
+// and H (-hw, -lw, hw, lw).  Corners outside the level have no entry and count
+// 0.  The S samples of a (point, camera) are consecutive threads: with S a power
+// of two their location terms are summed across lanes (total in the last lane),
+// otherwise each sample's term goes to loc_part and loc_reduce_kernel adds them.
+__global__ void __launch_bounds__(256) finalize_kernel(KArgs a) {
+    const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool valid = q < a.n_samples;
+    const uint32_t qq = valid ? q : 0u;
+    const uint32_t per_anchor = (uint32_t)(a.npk * a.S);
+    const uint32_t ba = qq / per_anchor;
+    const int t = (int)(qq - ba * per_anchor);
+    const Stencil st = make_stencil(a, (int64_t)ba, t);
+    const int G = a.G;
+    const float* wrow = a.weights + (size_t)qq * G;
+    float* gwrow = a.grad_weights + (size_t)qq * G;
+    const float* drow = a.dots + (size_t)qq * 4 * G;
+    bool in[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) in[c] = st.row[c] >= 0;
+    float tc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.w_vec4) {
+        for (int g = 0; g < G; g += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(wrow + g);
+            float4 d[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float4 v = *reinterpret_cast<const float4*>(drow + c * G + g);
+                d[c] = in[c] ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+                tc[c] += w.x * d[c].x + w.y * d[c].y + w.z * d[c].z + w.w * d[c].w;
+            }
+            float4 gw;
+            gw.x = st.cw[0] * d[0].x + st.cw[1] * d[1].x + st.cw[2] * d[2].x + st.cw[3] * d[3].x;
+            gw.y = st.cw[0] * d[0].y + st.cw[1] * d[1].y + st.cw[2] * d[2].y + st.cw[3] * d[3].y;
+            gw.z = st.cw[0] * d[0].z + st.cw[1] * d[1].z + st.cw[2] * d[2].z + st.cw[3] * d[3].z;
+            gw.w = st.cw[0] * d[0].w + st.cw[1] * d[1].w + st.cw[2] * d[2].w + st.cw[3] * d[3].w;
+            if (valid) *reinterpret_cast<float4*>(gwrow + g) = gw;
+        }
+    } else {
+        for (int g = 0; g < G; ++g) {
+            float d[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) d[c] = in[c] ? drow[c * G + g] : 0.0f;
+            const float gw = st.cw[0] * d[0] + st.cw[1] * d[1] + st.cw[2] * d[2] + st.cw[3] * d[3];
+            if (valid) gwrow[g] = gw;
+            const float w = wrow[g];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) tc[c] += w * d[c];
+        }
+    }
+    const float m = st.inside ? 1.0f : 0.0f;
+    float gx = m * st.W * (st.hh * (tc[1] - tc[0]) + st.lh * (tc[3] - tc[2]));
+    float gy = m * st.H * (st.hw * (tc[2] - tc[0]) + st.lw * (tc[3] - tc[1]));
+    const int S = a.S;
+    if ((S & (S - 1)) == 0 && S <= kWave) {
+        gx = group_sum(gx, S);
+        gy = group_sum(gy, S);
+        if (valid && (t % S) == S - 1)
+            reinterpret_cast<float2*>(a.grad_loc)[(size_t)ba * a.npk + t / S] = make_float2(gx, gy);
+    } else if (valid) {
+        reinterpret_cast<float2*>(a.loc_part)[q] = make_float2(gx, gy);
+    }
+}
+
+// grad_loc of each (anchor, point, camera) = sum of its S partials, in scale order.
+__global__ void __launch_bounds__(256) loc_reduce_kernel(KArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)a.n_anchors * a.npk) return;
+    const float2* part = reinterpret_cast<const float2*>(a.loc_part);
+    float gx = 0.0f, gy = 0.0f;
+    for (int s = 0; s < a.S; ++s) {
+        const float2 v = part[i * a.S + s];
+        gx += v.x;
+        gy += v.y;
+    }
+    reinterpret_cast<float2*>(a.grad_loc)[i] = make_float2(gx, gy);
+}
+
 // grad_loc of each (anchor, point, camera) = sum of its S scale partials, in
 // scale order: the role of the gather launch's blocks past gather_blocks, one
 // thread per pair.
@@ -645,13 +747,24 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 // inside the range (only a row-change test each) and a tail (the rest of a
 // short row that crosses the range end).  Batches of U entries are issued one
 // batch ahead of the one being added up.
-template <int VEC, int NV>
+//
+// Row-ordered backward (FUSED): every entry also loads its feature row (a
+// repeat of the previous entry's row is an L1 hit) and, per weight group, the
+// dot product of that row with the entry's grad_out row is summed over the
+// group's lanes and stored for finalize_kernel.
+template <typename T, int VEC, int NV, bool FUSED>
 __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
         return;
     }
-    constexpr int U = NV >= 8 ? 1 : 8 / NV;   // entries per batch, within the register budget
+    // entries per batch, within the register budget
+    constexpr int U = FUSED ? (NV >= 4 ? 1 : 4 / NV) : (NV >= 8 ? 1 : 8 / NV);
+    // FUSED: the feature row of the entry being added; a batch loads an entry's
+    // row only where it differs from the previous entry's (else the load points
+    // past the buffer: no memory request, zeros, and the row is kept here)
+    float fcur[NV][VEC];
+    static_assert(!FUSED || VEC == 4, "the row-ordered backward reads 4 channels per lane");
     constexpr uint32_t kNone = 0xffffffffu;
     static_assert(kGatherChunk == kWave && kGatherLong <= kGatherChunk, "window layout");
     static_assert(kWave % U == 0, "batches tile a window");
@@ -683,6 +796,7 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     };
     const uint4 win0 = load_window(e0);
     const uint4 win1 = load_window(e0 + (uint32_t)kWave);
+    const uint32_t last0 = (uint32_t)__builtin_amdgcn_readlane((int)win0.x, kWave - 1);
     const uint32_t before = (e0 == 0) ? kNone : uni(a.entries[e0 - 1].row);
 
     // where this wave starts: at e0, unless the row there began earlier and is
@@ -712,6 +826,17 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     }
     const __amdgpu_buffer_rsrc_t r_go = make_rsrc(a.grad_out, go_bytes);
     const __amdgpu_buffer_rsrc_t r_w = make_rsrc(a.weights, w_bytes);
+    // FUSED: feature rows of every batch image, by flat row
+    const __amdgpu_buffer_rsrc_t r_f = make_rsrc(a.feat, FUSED ? a.feat_all_bytes : 0u);
+    const int G = a.G;
+    const int seg = FUSED ? a.D / VEC : 1;    // lanes per weight group (a power of two)
+    uint32_t lo_f[NV];
+    bool dvalid[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        lo_f[i] = (uint32_t)(vv[i] * VEC * (int)sizeof(T));
+        dvalid[i] = lane + kWave * i < nvec && (lane & (seg - 1)) == seg - 1;
+    }
 
     float acc[NV][VEC];
 #pragma unroll
@@ -763,20 +888,42 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
         float cw[U];
         float go[U][NV][VEC];
         float wt[U][NV];
+        float f[U][NV][VEC];   // FUSED: the entry's feature row, where it starts a new row
+        bool fnew[U];          // FUSED: the entry's row differs from the previous entry's
+        uint32_t dof[U];       // FUSED: float index of the entry's dot products
     };
-    // entries at positions p0 .. p0+U-1 of window `win` (p0 a multiple of U)
-    auto issue = [&](const uint4& win, int p0, Batch& B) {
+    // entries at positions p0 .. p0+U-1 of window `win` (p0 a multiple of U);
+    // row_before: the row of the entry before the window (kNone for the first
+    // window, so that the first entry a wave takes always loads its row)
+    auto issue = [&](const uint4& win, uint32_t row_before, int p0, Batch& B) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = p0 + u;
             B.row[u] = (uint32_t)__builtin_amdgcn_readlane((int)win.x, idx);
             const uint32_t wo = (uint32_t)__builtin_amdgcn_readlane((int)win.y, idx);
             B.cw[u] = __int_as_float(__builtin_amdgcn_readlane((int)win.z, idx));
-            const uint32_t go = (uint32_t)__builtin_amdgcn_readlane((int)win.w, idx);
+            const uint32_t gow = (uint32_t)__builtin_amdgcn_readlane((int)win.w, idx);
+            const uint32_t go = gow & ~3u;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 VecLoad<float, VEC>::run(r_go, lo_go[i], go, B.go[u][i]);
                 B.wt[u][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_w, lo_w[i], wo, 0));
+            }
+            if constexpr (FUSED) {
+                // previous entry's row: in this batch, the window before p0, or
+                // none (the first entry a wave takes always loads its row)
+                const uint32_t prev =
+                    u > 0 ? B.row[u > 0 ? u - 1 : 0]
+                          : (p0 > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)win.x, p0 > 0 ? p0 - 1 : 0)
+                                    : row_before);
+                B.fnew[u] = B.row[u] != prev;
+                if (B.fnew[u]) {
+                    const uint32_t rb = (B.row[u] & ~kEntryLongRow) * (uint32_t)a.row_bytes;
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) VecLoad<T, VEC>::run(r_f, lo_f[i], rb, B.f[u][i]);
+                }
+                // (4 q + corner) * G with wo = 4 q G
+                B.dof[u] = wo + (gow & 3u) * (uint32_t)G;
             }
         }
     };
@@ -787,6 +934,22 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[i][k] += sc * B.go[u][i][k];
         }
+        if constexpr (FUSED) {
+            if (B.fnew[u]) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) fcur[i][k] = B.f[u][i][k];
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float d = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) d += B.go[u][i][k] * fcur[i][k];
+                d = group_sum(d, seg);
+                if (dvalid[i]) a.dots[B.dof[u] + (uint32_t)(lo_w[i] >> 2)] = d;
+            }
+        }
     };
 
     // phase 1: positions sp .. n1-1 of win0; a row change flushes the finished row
@@ -794,10 +957,10 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     {
         const int first = sp - sp % U;
         int p = first;
-        issue(win0, p, A);
+        issue(win0, kNone, p, A);
         while (true) {
             const int pn = min(p + U, kWave - U);
-            issue(win0, pn, B);
+            issue(win0, kNone, pn, B);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pos = p + u;
@@ -812,7 +975,7 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
             p += U;
             if (p >= n1) break;
             const int pn2 = min(p + U, kWave - U);
-            issue(win0, pn2, A);
+            issue(win0, kNone, pn2, A);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pos = p + u;
@@ -833,7 +996,7 @@ __global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
     if (n1 == kWave && !(cur & kEntryLongRow)) {
         bool done = false;
         for (int p = 0; p < kWave && !done; p += U) {
-            issue(win1, p, A);
+            issue(win1, last0, p, A);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!done) {
@@ -931,22 +1094,22 @@ hipError_t sliced_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipS
     }
 }
 
-template <int VEC>
+template <typename T, int VEC, bool FUSED>
 hipError_t gather_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
     // C <= 1024 in the backward: 16-byte vectors need at most 4 per lane
     switch (s.gather_nv) {
-        case 1: hipLaunchKernelGGL((gather_kernel<VEC, 1>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gather_kernel<VEC, 2>), grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gather_kernel<VEC, 4>), grid, dim3(256), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED>), grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED>), grid, dim3(256), 0, st, a); break;
         case 8:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<1, 8>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 8, false>), grid, dim3(256), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
         case 16:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<1, 16>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 16, false>), grid, dim3(256), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
@@ -992,11 +1155,34 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    KArgs k = a;
+    const int64_t zwaves = a.accumulate ? 0 : ((int64_t)a.n_rows + kWave - 1) / kWave;
+    const int64_t waves = ((int64_t)a.n_samples * 4 + kGatherChunk - 1) / kGatherChunk;
+    if (a.fused) {
+        // bucketing (+ zeroing blocks), the gather with the dot products, then
+        // the per-sample gradients
+        k.anchor_blocks = blocks_for((int64_t)a.n_samples, 256);
+        hipLaunchKernelGGL(bucket_kernel, dim3((unsigned)(k.anchor_blocks + blocks_for(zwaves, 256 / kWave))),
+                           dim3(256), 0, stream, k);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k.gather_blocks = blocks_for(waves, 256 / kWave);
+        const dim3 ggrid(k.gather_blocks);
+        e = bf16 ? gather_dispatch<uint16_t, 4, true>(k, s, ggrid, stream)
+                 : gather_dispatch<float, 4, true>(k, s, ggrid, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for((int64_t)a.n_samples, 256)), dim3(256),
+                           0, stream, k);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((a.S & (a.S - 1)) != 0 || a.S > kWave) {
+            hipLaunchKernelGGL(loc_reduce_kernel, dim3(blocks_for((int64_t)a.n_anchors * a.npk, 256)),
+                               dim3(256), 0, stream, k);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
     // per-anchor kernel, followed (unless accumulating) by blocks that zero the
     // rows the gather does not store whole
-    KArgs k = a;
     k.anchor_blocks = (uint32_t)(a.sliced ? n_anchors_total * kSlices : n_anchors_total);
-    const int64_t zwaves = a.accumulate ? 0 : ((int64_t)a.n_rows + kWave - 1) / kWave;
     const dim3 grid((unsigned)(k.anchor_blocks + blocks_for(zwaves, s.waves)), 1);
     if (a.sliced) {
         if (bf16)
@@ -1017,12 +1203,11 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     // gather: one wave per chunk of the largest possible entry count (4 per
     // sample; waves past the real total return at once), followed in the
     // sliced form by blocks that add up the location partials
-    const int64_t waves = ((int64_t)a.n_samples * 4 + kGatherChunk - 1) / kGatherChunk;
     k.gather_blocks = blocks_for(waves, 256 / kWave);
     const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, 256) : 0;
     const dim3 ggrid((unsigned)(k.gather_blocks + lr));
-    return a.gather_vec == 4 ? gather_dispatch<4>(k, s, ggrid, stream)
-                             : gather_dispatch<1>(k, s, ggrid, stream);
+    return a.gather_vec == 4 ? gather_dispatch<float, 4, false>(k, s, ggrid, stream)
+                             : gather_dispatch<float, 1, false>(k, s, ggrid, stream);
 }
 
 }  // namespace da

@@ -62,6 +62,18 @@ struct VecLoad<uint16_t, 1> {
 };
 
 template <>
+struct VecLoad<uint16_t, 4> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[4]) {
+        auto q = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        v[0] = bf16_lo(q[0]);
+        v[1] = bf16_hi(q[0]);
+        v[2] = bf16_lo(q[1]);
+        v[3] = bf16_hi(q[1]);
+    }
+};
+
+template <>
 struct VecLoad<uint16_t, 8> {
     static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff, float (&v)[8]) {

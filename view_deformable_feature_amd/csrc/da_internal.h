@@ -35,7 +35,8 @@ struct Entry {
                        // (more than kGatherLong entries: summed range by range)
     uint32_t w_off;    // byte offset of the sample's weight row: sample * G * 4
     float cw;          // bilinear corner weight
-    uint32_t go_off;   // byte offset of the anchor's grad_out row: (b*A + a) * C * 4
+    uint32_t go_off;   // byte offset of the anchor's grad_out row, (b*A + a) * C * 4,
+                       // plus the corner index 0..3 in the two low bits
 };
 static_assert(sizeof(Entry) == 16, "Entry layout");
 constexpr uint32_t kEntryLongRow = 0x80000000u;
@@ -89,6 +90,13 @@ struct KArgs {
     // gather launch add up the location partials (sliced form).
     uint32_t anchor_blocks;
     uint32_t gather_blocks;
+    // Row-ordered backward: the gather also forms, for every entry, the dot
+    // products of its grad_out row with its feature row per weight group;
+    // finalize_kernel turns them into grad_weights and grad_loc.
+    int32_t fused;
+    uint32_t feat_all_bytes;   // bs * num_feat * C * elem (< 2^32 on this path)
+    float* dots;               // [n_samples, 4, G]: entry (q, corner) at (4q + corner) * G
+    int32_t w_vec4;            // weights / grad_weights rows readable as float4
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
