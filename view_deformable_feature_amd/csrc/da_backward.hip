@@ -456,13 +456,15 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
         zero_rows_role(a);
         return;
     }
+    __shared__ int32_t lvl_lds[3 * kMaxLevels];
+    const LevelsLds lv = stage_levels(a, lvl_lds);
     const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= a.n_samples) return;
     const uint32_t per_anchor = (uint32_t)(a.npk * a.S);
     const uint32_t ba = q / per_anchor;
     const int t = (int)(q - ba * per_anchor);
     const uint32_t b = ba / (uint32_t)a.A;
-    const Stencil st = make_stencil(a, (int64_t)ba, t);
+    const Stencil st = make_stencil(a, (int64_t)ba, t, lv);
     bucket_sample(a, st, (int64_t)b, (int64_t)ba, q);
 }
 
@@ -478,13 +480,15 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
 // of two their location terms are summed across lanes (total in the last lane),
 // otherwise each sample's term goes to loc_part and loc_reduce_kernel adds them.
 __global__ void __launch_bounds__(256) finalize_kernel(KArgs a) {
+    __shared__ int32_t lvl_lds[3 * kMaxLevels];
+    const LevelsLds lv = stage_levels(a, lvl_lds);
     const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
     const bool valid = q < a.n_samples;
     const uint32_t qq = valid ? q : 0u;
     const uint32_t per_anchor = (uint32_t)(a.npk * a.S);
     const uint32_t ba = qq / per_anchor;
     const int t = (int)(qq - ba * per_anchor);
-    const Stencil st = make_stencil(a, (int64_t)ba, t);
+    const Stencil st = make_stencil(a, (int64_t)ba, t, lv);
     const int G = a.G;
     const float* wrow = a.weights + (size_t)qq * G;
     float* gwrow = a.grad_weights + (size_t)qq * G;
@@ -752,8 +756,11 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 // repeat of the previous entry's row is an L1 hit) and, per weight group, the
 // dot product of that row with the entry's grad_out row is summed over the
 // group's lanes and stored for finalize_kernel.
+// The walk is latency-bound: the occupancy hint (5 waves per SIMD for one
+// vector per lane, measured faster despite a few spilled registers) keeps more
+// waves in flight.
 template <typename T, int VEC, int NV, bool FUSED>
-__global__ void __launch_bounds__(256) gather_kernel(KArgs a) {
+__global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
         return;

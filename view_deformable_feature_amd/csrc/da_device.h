@@ -112,14 +112,48 @@ struct Stencil {
     float H, W;
 };
 
-__device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int t) {
+// The level table as read by one sample: straight from the kernel arguments
+// (fine where the level is the same across a wave), or from a copy in LDS
+// (where every lane may sit on a different level).
+struct LevelsArg {
+    const KArgs& a;
+    __device__ __forceinline__ void get(int l, int32_t& H, int32_t& W, int32_t& st) const {
+        H = a.lv.H[l];
+        W = a.lv.W[l];
+        st = a.lv.start[l];
+    }
+};
+struct LevelsLds {
+    const int32_t* hws;   // [3][kMaxLevels]: H, W, start
+    __device__ __forceinline__ void get(int l, int32_t& H, int32_t& W, int32_t& st) const {
+        H = hws[l];
+        W = hws[kMaxLevels + l];
+        st = hws[2 * kMaxLevels + l];
+    }
+};
+
+// Copy the level table to LDS (every thread of the block must call this).
+__device__ __forceinline__ LevelsLds stage_levels(const KArgs& a, int32_t* lds) {
+    const int nlev = a.K * a.S;
+    for (int i = threadIdx.x; i < nlev; i += blockDim.x) {
+        lds[i] = a.lv.H[i];
+        lds[kMaxLevels + i] = a.lv.W[i];
+        lds[2 * kMaxLevels + i] = a.lv.start[i];
+    }
+    __syncthreads();
+    return LevelsLds{lds};
+}
+
+template <typename Levels>
+__device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int t, const Levels& lv) {
     // t < P*K*S and ba < 2^23 are guaranteed by the host checks
     Stencil st;
     const int pk = t / a.S;
     const int s = t - pk * a.S;
     const int k = pk % a.K;
     const int lvl = k * a.S + s;
-    const int32_t H = a.lv.H[lvl], W = a.lv.W[lvl], start = a.lv.start[lvl];
+    int32_t H, W, start;
+    lv.get(lvl, H, W, start);
     const float2 xy = *reinterpret_cast<const float2*>(a.loc + (ba * a.npk + pk) * 2);
     float w_im, h_im;
     {
@@ -152,6 +186,10 @@ __device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int 
     st.cw[2] = m * st.lh * st.hw;
     st.cw[3] = m * st.lh * st.lw;
     return st;
+}
+
+__device__ __forceinline__ Stencil make_stencil(const KArgs& a, int64_t ba, int t) {
+    return make_stencil(a, ba, t, LevelsArg{a});
 }
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, kWave); }
@@ -189,6 +227,15 @@ __device__ __forceinline__ float group_sum(float v, int n) {
 __device__ __forceinline__ int slice_sample(const KArgs& a, int x, int m, int j) {
     const int p = j / m;
     const int l = a.lv.slice_level[x][j - p * m];
+    const int k = l / a.S;
+    const int s = l - k * a.S;
+    return (p * a.K + k) * a.S + s;
+}
+
+// The same, with slice x's level list copied to LDS (`levels`, m entries).
+__device__ __forceinline__ int slice_sample(const KArgs& a, const int32_t* levels, int m, int j) {
+    const int p = j / m;
+    const int l = levels[j - p * m];
     const int k = l / a.S;
     const int s = l - k * a.S;
     return (p * a.K + k) * a.S + s;

@@ -225,11 +225,17 @@ da_forward_sliced_kernel(KArgs a) {
     if (tid == 0) desc[ns_max] = null_fwd_desc(a.feat_image_bytes);
     const int m = a.lv.slice_nlev[x];
     const int n = a.P * m;
+    // level table and this slice's level list in LDS: every lane of the
+    // staging loops looks up its own level
+    __shared__ int32_t lvl_lds[3 * kMaxLevels + kMaxSliceLevels];
+    int32_t* slice_lv = lvl_lds + 3 * kMaxLevels;
+    if (tid < m) slice_lv[tid] = a.lv.slice_level[x][tid];
+    const LevelsLds lv = stage_levels(a, lvl_lds);
     const int64_t wbase = ba * (int64_t)a.npk * a.S * a.G;
     for (int j0 = 0; j0 < n; j0 += ns_max) {
         const int nsc = min(ns_max, n - j0);
         for (int jj = tid; jj < nsc; jj += nthreads) {
-            const Stencil st = make_stencil(a, ba, slice_sample(a, x, m, j0 + jj));
+            const Stencil st = make_stencil(a, ba, slice_sample(a, slice_lv, m, j0 + jj), lv);
             FwdDesc d;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -241,7 +247,7 @@ da_forward_sliced_kernel(KArgs a) {
         }
         for (int i = tid; i < nsc * a.G; i += nthreads) {
             const int jj = i / a.G;
-            wts[i] = a.weights[wbase + (int64_t)slice_sample(a, x, m, j0 + jj) * a.G + (i - jj * a.G)];
+            wts[i] = a.weights[wbase + (int64_t)slice_sample(a, slice_lv, m, j0 + jj) * a.G + (i - jj * a.G)];
         }
         __syncthreads();
 
