@@ -87,11 +87,14 @@ typedef enum {
  */
 #define DA_FLAG_SLICES_ALWAYS 1  /* slice whatever the sizes (where the lane layout allows) */
 #define DA_FLAG_SLICES_NEVER 2   /* one workgroup per anchor                                */
-/* Backward form (see da_backward): by default the location and weight gradients
- * come from dot products formed while the feature gradient is gathered in row
- * order; this flag selects the per-anchor kernels that gather the corner rows
- * again instead (always used where the row-ordered form does not apply). */
+/* Backward form (see da_backward): where feature rows are shared by several
+ * corners (on the largest level, 4 * num_anchors * num_pts / (H * W) >= 2) the
+ * location and weight gradients come from dot products formed while the feature
+ * gradient is gathered in row order; elsewhere, where the lane layout does not
+ * allow that form, or with this flag, per-anchor kernels gather the corner rows
+ * again instead. */
 #define DA_FLAG_BWD_REGATHER 4
+#define DA_FLAG_BWD_ROW_ORDER 8  /* the row-ordered backward wherever the lane layout allows */
 
 /* Problem sizes.  bs, num_anchors and num_pts may be 0 (then there is nothing to
  * sample: out and grad_feat are filled with zeros).  All other sizes are >= 1,
@@ -106,7 +109,8 @@ typedef struct {
     int64_t num_scale;    /* S                                             */
     int64_t num_groups;   /* G, weight groups over the channels            */
     int32_t feat_dtype;   /* da_dtype                                      */
-    int32_t flags;        /* DA_FLAG_* bits (SLICES_ALWAYS and _NEVER exclusive) */
+    int32_t flags;        /* DA_FLAG_* bits (SLICES_ALWAYS / _NEVER exclusive, and so are
+                             BWD_REGATHER / BWD_ROW_ORDER) */
 } da_problem;
 
 /*
@@ -157,7 +161,9 @@ da_status da_forward(const da_problem* problem,
 /*
  * da_backward_workspace_size -- bytes of device workspace da_backward and
  * da_backward_accumulate need for `problem` (0 when there is no sample): about
- * 8 * bs * num_feat + 88 * bs*A*P*K*S.  Only the sizes in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
+ * 8 * bs * num_feat + (88 + 16 * G) * bs*A*P*K*S where the row-ordered backward
+ * may apply, else 8 * bs * num_feat + 88 * bs*A*P*K*S.  Only the sizes and flags
+ * in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */

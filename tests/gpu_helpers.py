@@ -48,8 +48,9 @@ def gpu_forward(dev, slices=None, workspace=None):
 
 
 def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices=None,
-                 regather=False):
-    """regather: the per-anchor backward form instead of the row-ordered one."""
+                 regather=None):
+    """regather: None = the library's choice of backward form, True = per-anchor,
+    False = row-ordered."""
     import view_deformable_feature_amd as vdf
     args = (dev["feat"], dev["spatial_shape"], dev["scale_start_index"], dev["loc"],
             dev["weights"], dev["grad_out"])

@@ -88,7 +88,8 @@ def _msg(lib):
     (dict(feat_dtype=7), 1, "feat_dtype"),
     (dict(flags=3), 1, "flags"),
     (dict(flags=7), 1, "flags"),
-    (dict(flags=8), 1, "flags"),
+    (dict(flags=12), 1, "flags"),
+    (dict(flags=16), 1, "flags"),
     (dict(flags=-1), 1, "flags"),
     (dict(num_feat=255), 1, "inside num_feat"),
     (dict(num_cams=9, num_scale=8), 1, "DA_MAX_LEVELS"),

@@ -22,14 +22,14 @@ def _args(inp):
     return [inp[k] for k in KEYS]
 
 
-# (level slices, per-anchor backward): the library's choice, slices forced, and the
-# per-anchor backward form with and without slices
-MODES = {"auto": (None, False), "sliced": (True, False), "regather": (None, True),
-         "regather_sliced": (True, True), "regather_unsliced": (False, True),
-         "unsliced": (False, False)}
+# (level slices, backward form): the library's choice of both; slices forced on; the
+# row-ordered backward forced; the per-anchor backward forced, with and without slices
+MODES = {"auto": (None, None), "sliced": (True, None), "roworder": (None, False),
+         "regather": (None, True), "regather_sliced": (True, True),
+         "regather_unsliced": (False, True), "unsliced": (False, None)}
 
 
-def _full_check(inp, tol_f, tol_b, label, slices=None, regather=False):
+def _full_check(inp, tol_f, tol_b, label, slices=None, regather=None):
     say(f"[parity] {label}: upload")
     dev = to_device(inp)
     say(f"[parity] {label}: forward (slices={slices})")
@@ -51,7 +51,7 @@ def _full_check(inp, tol_f, tol_b, label, slices=None, regather=False):
 # the five workloads
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather", "regather_sliced"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather", "regather_sliced"])
 def test_tiny_full(mode):
     inp = W.make_inputs(W.WORKLOADS["tiny"])
     _full_check(inp, TOL_FWD, TOL_BWD, "tiny", *MODES[mode])
@@ -89,7 +89,7 @@ def test_nuscenes_backward_full(mode):
 
 
 def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=None,
-                   regather=False):
+                   regather=None):
     say(f"[parity] {wl.name}: generate")
     inp = W.make_inputs(wl)
     dev = to_device(inp)
@@ -126,13 +126,13 @@ def _sampled_check(wl, tol_f, tol_b, n_anchor=48, n_rows=160, seed=0, slices=Non
     say(f"[parity] {wl.name}: ok ({touched.size} touched rows)")
 
 
-@pytest.mark.parametrize("mode", ["auto", "regather", "regather_unsliced"])
+@pytest.mark.parametrize("mode", ["auto", "roworder", "regather_unsliced"])
 def test_large_sampled(mode):
     slices, regather = MODES[mode]
     _sampled_check(W.WORKLOADS["large"], TOL_FWD, TOL_BWD, slices=slices, regather=regather)
 
 
-@pytest.mark.parametrize("mode", ["auto", "regather"])
+@pytest.mark.parametrize("mode", ["auto", "roworder"])
 def test_large_bf16_sampled(mode):
     slices, regather = MODES[mode]
     _sampled_check(W.WORKLOADS["large_bf16"], TOL_BF16, TOL_BF16, slices=slices,
@@ -172,7 +172,7 @@ RAGGED = [
 
 @pytest.mark.parametrize("name, kw", RAGGED, ids=[r[0] for r in RAGGED])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather", "regather_sliced"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather_sliced"])
 def test_ragged_full(name, kw, dtype, mode):
     wl = W.custom(f"{name}_{dtype}", feat_dtype=dtype, seed=zlib.crc32(name.encode()) % 1000, **kw)
     inp = W.make_inputs(wl)
@@ -261,7 +261,7 @@ def test_no_points_and_empty_batches(slices):
         assert torch.count_nonzero(gf) == 0
 
 
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather"])
 def test_nan_and_far_locations_contribute_nothing(mode):
     wl = W.custom("nanloc", bs=1, num_cams=2, levels=((8, 8), (4, 4)), C=32, groups=2,
                   anchors=10, pts=4, loc_lo=-0.1, loc_hi=1.1, seed=5)
@@ -286,7 +286,7 @@ def test_max_extent_levels():
     _full_check(W.make_inputs(wl), TOL_FWD, TOL_BWD, "maxext_w")
 
 
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather"])
 def test_accumulate_adds_into_existing_gradient(mode):
     slices, regather = MODES[mode]
     inp = W.make_inputs(W.custom("acc", bs=1, num_cams=2, levels=((10, 12), (5, 6)), C=64,
@@ -361,7 +361,7 @@ def test_backward_atomic_form_ragged_bf16():
     assert_close("atomic bf16 grad_weights", gw, r_gw, TOL_BF16)
 
 
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather"])
 def test_workspace_reused_across_calls(mode):
     """One caller-owned workspace serves two calls in a row, the second smaller; its
     stale contents from the first call must not leak into the second.  Same for the
@@ -390,7 +390,7 @@ def test_workspace_reused_across_calls(mode):
         assert_close("ws grad_weights", gw, r_gw, TOL_BWD)
 
 
-@pytest.mark.parametrize("mode", ["auto", "sliced", "regather"])
+@pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather"])
 def test_hot_rows_span_many_chunks(mode):
     """A 2x3 level hit by 4000 samples: each of its rows collects thousands of
     feature-gradient terms, far more than one wave's chunk of the row-sorted list,

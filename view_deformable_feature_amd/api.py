@@ -54,21 +54,22 @@ def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _flags(slices: Optional[bool], regather: bool = False) -> int:
+def _flags(slices: Optional[bool], regather: Optional[bool] = None) -> int:
     """slices: None lets the library choose level slices, True / False force them on /
-    off.  regather: the backward takes the per-anchor form that gathers the corner
-    rows again (default: the row-ordered form where it applies)."""
+    off.  regather: None lets the library choose the backward form; True takes the
+    per-anchor form that gathers the corner rows again, False the row-ordered form
+    (where the lane layout allows it)."""
     f = 0
     if slices is not None:
         f |= _lib.DA_FLAG_SLICES_ALWAYS if slices else _lib.DA_FLAG_SLICES_NEVER
-    if regather:
-        f |= _lib.DA_FLAG_BWD_REGATHER
+    if regather is not None:
+        f |= _lib.DA_FLAG_BWD_REGATHER if regather else _lib.DA_FLAG_BWD_ROW_ORDER
     return f
 
 
 def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
                sampling_location: torch.Tensor, weights: torch.Tensor,
-               slices: Optional[bool] = None, regather: bool = False) -> _lib.DAProblem:
+               slices: Optional[bool] = None, regather: Optional[bool] = None) -> _lib.DAProblem:
     if mc_ms_feat.dim() != 3:
         raise ValueError("mc_ms_feat must be [bs, num_feat, C]")
     if sampling_location.dim() != 5 or sampling_location.shape[-1] != 2:
@@ -87,7 +88,7 @@ def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
 
 
 def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
-             slices=None, regather=False):
+             slices=None, regather=None):
     shape = _host_i32(spatial_shape)
     start = _host_i32(scale_start_index)
     dev = mc_ms_feat.device
@@ -162,7 +163,7 @@ def forward_workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights
 
 
 def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
-                   regather: bool = False) -> int:
+                   regather: Optional[bool] = None) -> int:
     """Bytes of workspace da_backward / da_backward_accumulate need for these shapes."""
     lib = _lib.load()
     prob = problem_of(mc_ms_feat, _host_i32(spatial_shape), sampling_location, weights,
@@ -175,7 +176,7 @@ def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
 
 def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
               weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None,
-              workspace=None, slices=None, regather=False):
+              workspace=None, slices=None, regather=None):
     lib = _lib.load()
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
                                   sampling_location, weights, slices, regather)
@@ -208,7 +209,7 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
 
 def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
                 grad_out, grad_feat=None, grad_loc=None, grad_weights=None, workspace=None,
-                slices=None, regather=False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                slices=None, regather=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
     return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
@@ -217,7 +218,7 @@ def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
 
 def da_backward_accumulate(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
                            weights, grad_out, grad_feat, grad_loc=None, grad_weights=None,
-                           workspace=None, slices=None, regather=False):
+                           workspace=None, slices=None, regather=None):
     """As da_backward, adding the feature gradient into the existing ``grad_feat``."""
     return _backward("da_backward_accumulate", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
