@@ -106,6 +106,59 @@ def cpu_baseline(wl, inp, min_seconds=10.0):
                        f"(fp64 C loop, one thread)")
 
 
+def bench_pack(args):
+    """Level packing (section 6, feature_maps_format) of the workload's per-scale
+    camera maps [B, N, C, H_s, W_s] into [B, num_feat, C], and back.  Each direction
+    reads and writes the whole tensor once: algorithmic bytes = 2 x tensor bytes."""
+    import torch
+    import view_deformable_feature_amd as vdf
+    from view_deformable_feature_amd import workloads as W
+    wl = W.WORKLOADS[args.workload]
+    dt = torch.bfloat16 if wl.feat_dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    maps = [torch.randn((wl.bs, wl.num_cams, wl.C, h, w), device="cuda", generator=gen).to(dt)
+            for h, w in wl.levels]
+    _, _, nf = vdf.pack_layout(list(wl.levels), wl.num_cams, wl.C, dt)
+    packed = torch.empty((wl.bs, nf, wl.C), device="cuda", dtype=dt)
+    outs = [torch.empty_like(m) for m in maps]
+    nbytes = packed.numel() * packed.element_size()
+    res = {}
+    for name, fn in (("pack", lambda: vdf.da_pack_levels(maps, out=packed)),
+                     ("unpack", lambda: vdf.da_unpack_levels(packed, list(wl.levels), wl.num_cams,
+                                                             out=outs))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e-3 / args.steps
+    t = res["pack"] + res["unpack"]
+    a = 2 * nbytes / res["pack"] / 1e9
+    rec = {"metric": "level packing: bytes read + written per second (pack then unpack)",
+           "value": 4 * nbytes / t, "unit": "B/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32" if dt == torch.float32 else "bf16", "data": "synthetic",
+           "config": {"workload": f"{wl.name} feature maps: {wl.num_cams} cameras, scales "
+                                  + "/".join(f"{h}x{w_}" for h, w_ in wl.levels)
+                                  + f", C={wl.C}, bs={wl.bs}", "tensor_bytes": nbytes},
+           "pack_us": res["pack"] * 1e6, "unpack_us": res["unpack"] * 1e6,
+           "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "pack_kernel (pack direction)",
+                        "algorithmic_bytes": 2 * nbytes,
+                        "avg_launch_us": round(res["pack"] * 1e6, 2)},
+           "roofline_unpack": {"bound": "hbm",
+                               "achieved": round(2 * nbytes / res["unpack"] / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(2 * nbytes / res["unpack"] / 1e9 / HBM_PEAK_GBS, 4)}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +170,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack"),
+                    help="aggregate: forward + backward step (the headline); pack: level "
+                         "packing and unpacking of the workload's feature maps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -128,6 +184,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.op == "pack":
+        bench_pack(args)
         return
 
     import view_deformable_feature_amd as vdf

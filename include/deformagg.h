@@ -245,6 +245,55 @@ da_status da_backward_atomic(const da_problem* problem,
                              float* grad_weights,
                              void* stream);
 
+/*
+ * Level packing -- section 6 of the walkthrough: feature_maps_format turns the list of
+ * per-scale camera feature maps into the flattened tensor the aggregation reads (plus
+ * its level table), and back.  The page prints this step only in garbled form; the
+ * library takes the layout of section 3.1: each level HWC, levels camera-major, scales
+ * in order inside a camera.  Level (k, s) starts at row
+ *     k * sum_s' H_s' W_s'  +  sum_{s' < s} H_s' W_s'.
+ * Packing is a pure rearrangement: values are copied bit for bit.
+ */
+typedef struct {
+    int64_t bs;           /* B                                               */
+    int64_t num_cams;     /* N, cameras; num_cams * num_scale <= DA_MAX_LEVELS */
+    int64_t num_scale;    /* S                                               */
+    int64_t num_embeds;   /* C                                               */
+    int32_t dtype;        /* da_dtype of the maps and of the packed tensor   */
+    int32_t reserved;     /* must be 0                                       */
+} da_pack_problem;
+
+/*
+ * da_pack_layout -- host only.  scale_hw: HOST int32 [S, 2], (H_s, W_s) of scale s
+ * (the same for every camera).  Writes spatial_shape HOST int32 [N, S, 2],
+ * scale_start_index HOST int32 [N, S] and *num_feat (rows of one packed batch image)
+ * -- the level table da_forward / da_backward take.  Errors: DA_ERR_INVALID_ARG for
+ * NULL pointers or malformed sizes, DA_ERR_UNSUPPORTED when num_feat >= 2^31 or
+ * bs * num_cams > 65535.
+ */
+da_status da_pack_layout(const da_pack_problem* problem, const int32_t* scale_hw,
+                         int32_t* spatial_shape, int32_t* scale_start_index, int64_t* num_feat);
+
+/*
+ * da_pack_levels -- packed[b, row(k, s) + i*W_s + j, c] = maps[s][b, k, c, i, j].
+ *   maps     HOST array of S device pointers; maps[s] is [B, N, C, H_s, W_s], contiguous,
+ *            element aligned.
+ *   packed   device [B, num_feat, C], fully overwritten; element aligned.
+ * Asynchronous on `stream`.  Same errors as da_pack_layout, plus DA_ERR_INVALID_ARG for
+ * NULL or misaligned tensors and DA_ERR_HIP.
+ */
+da_status da_pack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
+                         const void* const* maps, void* packed, void* stream);
+
+/*
+ * da_unpack_levels -- the inverse: maps[s][b, k, c, i, j] = packed[b, row(k, s) + i*W_s + j, c]
+ * (every element of every map overwritten).  Used for the gradient of the packing:
+ * it carries d loss / d packed back to the per-scale maps.  Arguments and errors as
+ * da_pack_levels.
+ */
+da_status da_unpack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
+                           const void* packed, void* const* maps, void* stream);
+
 /* Static description of a status code. */
 const char* da_status_string(da_status status);
 

@@ -23,7 +23,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "forward", "backward", "backward_anchors", "grad_feat_rows"]
+__all__ = ["build", "forward", "backward", "backward_anchors", "grad_feat_rows",
+           "pack_levels", "unpack_levels"]
 
 
 def build(force: bool = True) -> str:
@@ -151,3 +152,41 @@ def run_inputs(inp: Dict[str, np.ndarray], backward_too: bool = True):
     if not backward_too:
         return out
     return (out,) + backward(*(inp[k] for k in keys), inp["grad_out"])
+
+
+# ---------------------------------------------------------------------------------------
+# level packing (section 6: feature_maps_format), written out with numpy
+# ---------------------------------------------------------------------------------------
+# Layout (section 3.1 and the reading taken where section 6 is garbled): each
+# (camera k, scale s) level is stored HWC -- pixel (i, j) of the level is row
+# i*W + j of its block, C channels per row -- and the blocks follow camera by
+# camera, scales in order inside a camera.  Pure rearrangement, no arithmetic.
+
+def pack_levels(maps: Sequence[np.ndarray]):
+    """maps[s]: [B, N, C, H_s, W_s] -> (packed [B, num_feat, C], spatial_shape [N, S, 2]
+    int32, scale_start_index [N, S] int32)."""
+    B, N, C = maps[0].shape[:3]
+    S = len(maps)
+    blocks, shape, start, row = [], np.zeros((N, S, 2), np.int32), np.zeros((N, S), np.int32), 0
+    for k in range(N):
+        for s, m in enumerate(maps):
+            H, W = m.shape[3], m.shape[4]
+            # [B, C, H, W] -> [B, H, W, C] -> [B, H*W, C]
+            blocks.append(np.transpose(m[:, k], (0, 2, 3, 1)).reshape(B, H * W, C))
+            shape[k, s] = (H, W)
+            start[k, s] = row
+            row += H * W
+    return np.ascontiguousarray(np.concatenate(blocks, axis=1)), shape, start
+
+
+def unpack_levels(packed: np.ndarray, scale_hw: Sequence[Tuple[int, int]], num_cams: int):
+    """The inverse of pack_levels: packed [B, num_feat, C] -> list of [B, N, C, H_s, W_s]."""
+    B, _, C = packed.shape
+    maps = [np.empty((B, num_cams, C, h, w), packed.dtype) for h, w in scale_hw]
+    row = 0
+    for k in range(num_cams):
+        for s, (h, w) in enumerate(scale_hw):
+            block = packed[:, row:row + h * w, :].reshape(B, h, w, C)
+            maps[s][:, k] = np.transpose(block, (0, 3, 1, 2))
+            row += h * w
+    return maps

@@ -8,4 +8,7 @@ from .api import (DeformableAggregationFunction, da_backward, da_backward_accumu
                   da_backward_atomic, da_forward, deformable_aggregation, forward_workspace_size,
                   workspace_size)
 
+from .pack import (PackLevelsFunction, da_pack_levels, da_unpack_levels,  # noqa: F401
+                   feature_maps_format, pack_layout, pack_levels)
+
 __version__ = "1.1.0"

@@ -35,6 +35,17 @@ class DAProblem(ctypes.Structure):
     ]
 
 
+class DAPackProblem(ctypes.Structure):
+    _fields_ = [
+        ("bs", ctypes.c_int64),
+        ("num_cams", ctypes.c_int64),
+        ("num_scale", ctypes.c_int64),
+        ("num_embeds", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class DAError(RuntimeError):
     def __init__(self, status: int, func: str, detail: str):
         self.status = status
@@ -68,6 +79,14 @@ def load() -> ctypes.CDLL:
     lib.da_backward_atomic.restype = ctypes.c_int
     lib.da_backward_workspace_size.argtypes = [prob, ctypes.POINTER(ctypes.c_size_t)]
     lib.da_backward_workspace_size.restype = ctypes.c_int
+    pprob = ctypes.POINTER(DAPackProblem)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.da_pack_layout.argtypes = [pprob, i32p, i32p, i32p, ctypes.POINTER(ctypes.c_int64)]
+    lib.da_pack_layout.restype = ctypes.c_int
+    lib.da_pack_levels.argtypes = [pprob, i32p, vpp, vp, vp]
+    lib.da_pack_levels.restype = ctypes.c_int
+    lib.da_unpack_levels.argtypes = [pprob, i32p, vp, vpp, vp]
+    lib.da_unpack_levels.restype = ctypes.c_int
     lib.da_status_string.argtypes = [ctypes.c_int]
     lib.da_status_string.restype = ctypes.c_char_p
     lib.da_last_error.argtypes = []

@@ -14,9 +14,10 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("da_forward.hip", "da_backward.hip", "da_api.cpp")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("da_forward.hip", "da_backward.hip", "da_pack.hip", "da_api.cpp")]
 HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(CSRC, "da_internal.h"),
-           os.path.join(CSRC, "da_device.h")]
+           os.path.join(CSRC, "da_device.h"), os.path.join(CSRC, "da_pack.h")]
 ARCH = "gfx950"
 
 
@@ -36,21 +37,32 @@ def compile_flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libdeformagg.so (always recompiles)."""
-    hipcc = _hipcc()
-    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *compile_flags(), "-shared", *SOURCES, "-o", tmp,
-           f"-Wl,-rpath,{rocm_lib}", "-Wl,--no-undefined"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed building {LIB_PATH}")
+        raise RuntimeError(f"hipcc failed: {' '.join(cmd[-3:])}")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link libdeformagg.so; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = _hipcc()
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc, *compile_flags(), "-c", so[0], "-o", so[1]], verbose),
+                    zip(SOURCES, objs)))
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp,
+          f"-Wl,-rpath,{rocm_lib}", "-Wl,--no-undefined"], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "da_internal.h"
+#include "da_pack.h"
 #include "deformagg.h"
 
 namespace {
@@ -511,9 +512,126 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                       "backward kernel launch");
 }
 
+// Checks and layout shared by the packing entry points.
+da_status pack_plan(const da_pack_problem* p, const int32_t* scale_hw, da::PackArgs& pa,
+                    int& elem) {
+    if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->reserved != 0) return fail(DA_ERR_INVALID_ARG, "problem.reserved must be 0");
+    if (p->bs < 0) return fail(DA_ERR_INVALID_ARG, "bs must be >= 0");
+    if (p->num_cams < 1 || p->num_scale < 1 || p->num_embeds < 1)
+        return fail(DA_ERR_INVALID_ARG, "num_cams, num_scale and num_embeds must be >= 1");
+    if (p->num_cams * p->num_scale > DA_MAX_LEVELS)
+        return fail(DA_ERR_INVALID_ARG, "num_cams * num_scale = %lld exceeds DA_MAX_LEVELS (%d)",
+                    (long long)(p->num_cams * p->num_scale), DA_MAX_LEVELS);
+    if (p->dtype != DA_F32 && p->dtype != DA_BF16)
+        return fail(DA_ERR_INVALID_ARG, "dtype %d is neither DA_F32 nor DA_BF16", (int)p->dtype);
+    if (!scale_hw) return fail(DA_ERR_INVALID_ARG, "scale_hw is NULL");
+    if (p->bs * p->num_cams > 65535)
+        return fail(DA_ERR_UNSUPPORTED, "bs * num_cams = %lld exceeds 65535",
+                    (long long)(p->bs * p->num_cams));
+    memset(&pa, 0, sizeof pa);
+    elem = p->dtype == DA_BF16 ? 2 : 4;
+    const int64_t C = p->num_embeds;
+    const int64_t c_tiles = (C + 63) / 64;
+    int64_t rows = 0, tiles = 0;
+    for (int64_t s = 0; s < p->num_scale; ++s) {
+        const int64_t H = scale_hw[2 * s], W = scale_hw[2 * s + 1];
+        if (H < 1 || W < 1 || H > DA_MAX_EXTENT || W > DA_MAX_EXTENT)
+            return fail(DA_ERR_INVALID_ARG, "scale %lld: (H, W) = (%lld, %lld) outside [1, %d]",
+                        (long long)s, (long long)H, (long long)W, DA_MAX_EXTENT);
+        pa.hw[s] = H * W;
+        pa.start_in_cam[s] = rows;
+        pa.tile_base[s] = tiles;
+        rows += H * W;
+        tiles += (H * W + 63) / 64 * c_tiles;
+    }
+    pa.tile_base[p->num_scale] = tiles;
+    if (tiles > INT32_MAX) return fail(DA_ERR_UNSUPPORTED, "too many tiles per camera map");
+    pa.rows_per_cam = rows;
+    pa.num_feat = rows * p->num_cams;
+    if (pa.num_feat > INT32_MAX)
+        return fail(DA_ERR_UNSUPPORTED, "num_feat = %lld exceeds 2^31 - 1", (long long)pa.num_feat);
+    pa.c_tiles = c_tiles;
+    pa.B = (int32_t)p->bs;
+    pa.N = (int32_t)p->num_cams;
+    pa.S = (int32_t)p->num_scale;
+    if (C > INT32_MAX) return fail(DA_ERR_UNSUPPORTED, "num_embeds too large");
+    pa.C = (int32_t)C;
+    // 16-bit elements go two at a time when every row of both layouts has an even
+    // length (then every pair is 4-byte aligned, given 4-byte aligned tensors)
+    bool even = C % 2 == 0;
+    for (int64_t s = 0; s < p->num_scale; ++s) even = even && pa.hw[s] % 2 == 0;
+    pa.pairs = elem == 2 && even ? 1 : 0;
+    return DA_OK;
+}
+
+da_status pack_pointers(const da_pack_problem* p, const void* const* maps, const void* packed,
+                        int elem, da::PackArgs& pa) {
+    if (p->bs == 0) return DA_OK;
+    if (!maps) return fail(DA_ERR_INVALID_ARG, "maps is NULL");
+    if (!packed) return fail(DA_ERR_INVALID_ARG, "packed is NULL");
+    if (!aligned(packed, elem)) return fail(DA_ERR_INVALID_ARG, "packed is not element aligned");
+    for (int64_t s = 0; s < p->num_scale; ++s) {
+        if (!maps[s]) return fail(DA_ERR_INVALID_ARG, "maps[%lld] is NULL", (long long)s);
+        if (!aligned(maps[s], elem))
+            return fail(DA_ERR_INVALID_ARG, "maps[%lld] is not element aligned", (long long)s);
+        pa.maps[s] = const_cast<void*>(maps[s]);
+    }
+    pa.packed = const_cast<void*>(packed);
+    if (pa.pairs) {
+        bool al = aligned(packed, 4);
+        for (int64_t s = 0; s < p->num_scale; ++s) al = al && aligned(maps[s], 4);
+        if (!al) pa.pairs = 0;
+    }
+    return DA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+da_status da_pack_layout(const da_pack_problem* p, const int32_t* scale_hw, int32_t* spatial_shape,
+                         int32_t* scale_start_index, int64_t* num_feat) {
+    da::PackArgs pa;
+    int elem = 0;
+    const da_status st = pack_plan(p, scale_hw, pa, elem);
+    if (st != DA_OK) return st;
+    if (!spatial_shape || !scale_start_index || !num_feat)
+        return fail(DA_ERR_INVALID_ARG, "spatial_shape / scale_start_index / num_feat is NULL");
+    for (int64_t k = 0; k < p->num_cams; ++k)
+        for (int64_t s = 0; s < p->num_scale; ++s) {
+            const int64_t l = k * p->num_scale + s;
+            spatial_shape[2 * l] = scale_hw[2 * s];
+            spatial_shape[2 * l + 1] = scale_hw[2 * s + 1];
+            scale_start_index[l] = (int32_t)(k * pa.rows_per_cam + pa.start_in_cam[s]);
+        }
+    *num_feat = pa.num_feat;
+    return DA_OK;
+}
+
+da_status da_pack_levels(const da_pack_problem* p, const int32_t* scale_hw, const void* const* maps,
+                         void* packed, void* stream) {
+    da::PackArgs pa;
+    int elem = 0;
+    da_status st = pack_plan(p, scale_hw, pa, elem);
+    if (st != DA_OK) return st;
+    st = pack_pointers(p, maps, packed, elem, pa);
+    if (st != DA_OK || p->bs == 0) return st;
+    return hip_status(da::launch_pack(pa, elem, true, static_cast<hipStream_t>(stream)),
+                      "pack kernel launch");
+}
+
+da_status da_unpack_levels(const da_pack_problem* p, const int32_t* scale_hw, const void* packed,
+                           void* const* maps, void* stream) {
+    da::PackArgs pa;
+    int elem = 0;
+    da_status st = pack_plan(p, scale_hw, pa, elem);
+    if (st != DA_OK) return st;
+    st = pack_pointers(p, const_cast<const void* const*>(maps), packed, elem, pa);
+    if (st != DA_OK || p->bs == 0) return st;
+    return hip_status(da::launch_pack(pa, elem, false, static_cast<hipStream_t>(stream)),
+                      "unpack kernel launch");
+}
 
 da_status da_forward_workspace_size(const da_problem* p, size_t* bytes) {
     if (!bytes) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
