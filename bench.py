@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="run the backward in its deterministic (64-bit fixed-point) form")
     ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack"),
                     help="aggregate: forward + backward step (the headline); pack: level "
                          "packing and unpacking of the workload's feature maps")
@@ -227,7 +229,9 @@ def main():
     # caller-owned workspaces, allocated once, as a training loop would hold them
     fws_n = vdf.forward_workspace_size(feat, shape, loc, w)
     fws = torch.empty(fws_n, device=dev, dtype=torch.uint8) if fws_n else None
-    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w), device=dev, dtype=torch.uint8)
+    det = args.deterministic
+    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w, deterministic=det), device=dev,
+                      dtype=torch.uint8)
 
     def step(ev=None):
         if ev is not None:
@@ -236,7 +240,7 @@ def main():
         if ev is not None:
             ev[1].record()
         vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
-                        grad_weights=gw, workspace=bws)
+                        grad_weights=gw, workspace=bws, deterministic=det)
         if ev is not None:
             ev[2].record()
 
@@ -294,7 +298,8 @@ def main():
                                + "/".join(f"{h}x{w_}" for h, w_ in wl.levels)
                                + f", C={wl.C}, groups={wl.groups}, anchors={wl.anchors}, "
                                  f"points={wl.pts}",
-                   "sample_channels_per_step": sc},
+                   "sample_channels_per_step": sc,
+                   "backward_form": "deterministic" if det else "default"},
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
         "roofline": roof(b_bwd, bwd_s, BWD_KERNELS, "backward")

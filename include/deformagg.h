@@ -95,6 +95,14 @@ typedef enum {
  * again instead. */
 #define DA_FLAG_BWD_REGATHER 4
 #define DA_FLAG_BWD_ROW_ORDER 8  /* the row-ordered backward wherever the lane layout allows */
+/* Deterministic backward (da_backward, da_backward_accumulate): every feature-gradient
+ * term is rounded once to a multiple of 2^-E and the terms of a row are summed as 64-bit
+ * integers, which makes grad_feat independent of the order the terms arrive in: bit for
+ * bit the same across runs, backward forms and level slices.  E is derived on the GPU
+ * from max|grad_out| * max|weights| * (most terms of any row), leaving ~2^-60 of that
+ * bound as the resolution.  grad_out and weights must be finite.  Costs the workspace
+ * a 64-bit row per long row (see da_backward_workspace_size). */
+#define DA_FLAG_DETERMINISTIC 16
 
 /* Problem sizes.  bs, num_anchors and num_pts may be 0 (then there is nothing to
  * sample: out and grad_feat are filled with zeros).  All other sizes are >= 1,
@@ -162,8 +170,9 @@ da_status da_forward(const da_problem* problem,
  * da_backward_workspace_size -- bytes of device workspace da_backward and
  * da_backward_accumulate need for `problem` (0 when there is no sample): about
  * 8 * bs * num_feat + (88 + 16 * G) * bs*A*P*K*S where the row-ordered backward
- * may apply, else 8 * bs * num_feat + 88 * bs*A*P*K*S.  Only the sizes and flags
- * in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
+ * may apply, else 8 * bs * num_feat + 88 * bs*A*P*K*S; with DA_FLAG_DETERMINISTIC
+ * another 8 * C * (4 * bs*A*P*K*S / 65 + 1).  Only the sizes and flags in `problem`
+ * are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */
@@ -231,7 +240,8 @@ da_status da_backward_accumulate(const da_problem* problem,
  * workspace: grad_feat is zero-filled, then every (sample, corner, channel) term is
  * added with a binary32 atomic (section 4.1 adds them the same way).  Results equal
  * da_backward's up to rounding; it is slower wherever atomics are the bottleneck.
- * Arguments as da_backward without the workspace; same errors as da_forward.
+ * Arguments as da_backward without the workspace; same errors as da_forward, and
+ * DA_ERR_UNSUPPORTED with DA_FLAG_DETERMINISTIC.
  */
 da_status da_backward_atomic(const da_problem* problem,
                              const void* mc_ms_feat,

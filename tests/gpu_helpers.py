@@ -48,7 +48,7 @@ def gpu_forward(dev, slices=None, workspace=None):
 
 
 def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices=None,
-                 regather=None):
+                 regather=None, deterministic=False):
     """regather: None = the library's choice of backward form, True = per-anchor,
     False = row-ordered."""
     import view_deformable_feature_amd as vdf
@@ -57,10 +57,12 @@ def gpu_backward(dev, accumulate_into=None, atomic=False, workspace=None, slices
     if atomic:
         r = vdf.da_backward_atomic(*args)
     elif accumulate_into is None:
-        r = vdf.da_backward(*args, workspace=workspace, slices=slices, regather=regather)
+        r = vdf.da_backward(*args, workspace=workspace, slices=slices, regather=regather,
+                            deterministic=deterministic)
     else:
         r = vdf.da_backward_accumulate(*args, accumulate_into, workspace=workspace,
-                                       slices=slices, regather=regather)
+                                       slices=slices, regather=regather,
+                                       deterministic=deterministic)
     torch.cuda.synchronize()
     return r
 

@@ -89,7 +89,7 @@ def _msg(lib):
     (dict(flags=3), 1, "flags"),
     (dict(flags=7), 1, "flags"),
     (dict(flags=12), 1, "flags"),
-    (dict(flags=16), 1, "flags"),
+    (dict(flags=32), 1, "flags"),
     (dict(flags=-1), 1, "flags"),
     (dict(num_feat=255), 1, "inside num_feat"),
     (dict(num_cams=9, num_scale=8), 1, "DA_MAX_LEVELS"),
@@ -211,6 +211,10 @@ def test_workspace_size_and_checks(lib):
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_embeds=48, num_groups=2)),
                                           ctypes.byref(n)) == 0
     assert n.value == 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256
+    # deterministic form: + one 64-bit row of C per possible long row (4 * 32 // 65 + 1 = 2)
+    assert lib.da_backward_workspace_size(ctypes.byref(_prob(flags=16)), ctypes.byref(n)) == 0
+    assert n.value == expect + 2 * 32 * 8
+    assert _bwd(lib, _prob(flags=16), "da_backward_atomic") == 2 and "deterministic" in _msg(lib)
     assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value == expect
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_pts=0)), ctypes.byref(n)) == 0

@@ -399,3 +399,49 @@ def test_hot_rows_span_many_chunks(mode):
                   anchors=250, pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)
     inp = W.make_inputs(wl)
     _full_check(inp, TOL_FWD, TOL_BWD, "hot_rows", *MODES[mode])
+
+
+# ---------------------------------------------------------------------------------------
+# deterministic backward
+# ---------------------------------------------------------------------------------------
+
+DET_CASES = [
+    ("nuscenes_bwd", None),
+    ("hot_rows", dict(bs=2, num_cams=2, levels=((2, 3), (40, 60)), C=64, groups=4, anchors=250,
+                      pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)),
+    ("c96_g3_bf16", dict(bs=2, num_cams=3, levels=((13, 29), (7, 15), (3, 8)), C=96, groups=3,
+                         anchors=37, pts=5, loc_lo=-0.1, loc_hi=1.1, feat_dtype="bf16", seed=7)),
+]
+
+
+@pytest.mark.parametrize("name, kw", DET_CASES, ids=[c[0] for c in DET_CASES])
+def test_deterministic_backward_is_bit_identical(name, kw):
+    """grad_feat is the same bit for bit across runs, backward forms and level slices
+    (64-bit fixed-point row sums), and within the tolerance of the oracle."""
+    wl = W.WORKLOADS[name] if kw is None else W.custom(name, **kw)
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    say(f"[det] {name}")
+    runs = []
+    for slices, regather in ((None, None), (None, None), (None, True), (True, True), (False, False),
+                             (True, False)):
+        gf, gl, gw = gpu_backward(dev, slices=slices, regather=regather, deterministic=True)
+        runs.append((gf.cpu().numpy(), gl.cpu().numpy(), gw.cpu().numpy()))
+    for r in runs[1:]:
+        assert np.array_equal(r[0], runs[0][0]), "deterministic grad_feat differs"
+    ref = oracle.backward(*_args(inp), inp["grad_out"])
+    tol = TOL_BF16 if wl.feat_dtype == "bf16" else TOL_BWD
+    for gname, g, rr in zip(("grad_feat", "grad_loc", "grad_weights"), runs[0], ref):
+        assert_close(f"det {name} {gname}", g, rr, tol)
+
+
+def test_deterministic_accumulate():
+    inp = W.make_inputs(W.custom("detacc", bs=1, num_cams=2, levels=((3, 4), (20, 30)), C=64,
+                                 groups=4, anchors=120, pts=6, loc_lo=0.0, loc_hi=1.0, seed=71))
+    dev = to_device(inp)
+    base = torch.randn(tuple(dev["feat"].shape), device="cuda")
+    gf0, _, _ = gpu_backward(dev, deterministic=True)
+    outs = [gpu_backward(dev, accumulate_into=base.clone(), deterministic=True, regather=rg)[0]
+            for rg in (None, True)]
+    assert torch.equal(outs[0], outs[1])
+    assert_close("det accumulate", outs[0].cpu().numpy(), (base + gf0).cpu().numpy(), 1e-6)

@@ -18,6 +18,7 @@ DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
 DA_F32, DA_BF16 = 0, 1
 DA_FLAG_SLICES_ALWAYS, DA_FLAG_SLICES_NEVER, DA_FLAG_BWD_REGATHER, DA_FLAG_BWD_ROW_ORDER = \
     1, 2, 4, 8
+DA_FLAG_DETERMINISTIC = 16
 
 
 class DAProblem(ctypes.Structure):

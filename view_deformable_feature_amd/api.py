@@ -54,7 +54,8 @@ def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _flags(slices: Optional[bool], regather: Optional[bool] = None) -> int:
+def _flags(slices: Optional[bool], regather: Optional[bool] = None,
+           deterministic: bool = False) -> int:
     """slices: None lets the library choose level slices, True / False force them on /
     off.  regather: None lets the library choose the backward form; True takes the
     per-anchor form that gathers the corner rows again, False the row-ordered form
@@ -64,12 +65,15 @@ def _flags(slices: Optional[bool], regather: Optional[bool] = None) -> int:
         f |= _lib.DA_FLAG_SLICES_ALWAYS if slices else _lib.DA_FLAG_SLICES_NEVER
     if regather is not None:
         f |= _lib.DA_FLAG_BWD_REGATHER if regather else _lib.DA_FLAG_BWD_ROW_ORDER
+    if deterministic:
+        f |= _lib.DA_FLAG_DETERMINISTIC
     return f
 
 
 def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
                sampling_location: torch.Tensor, weights: torch.Tensor,
-               slices: Optional[bool] = None, regather: Optional[bool] = None) -> _lib.DAProblem:
+               slices: Optional[bool] = None, regather: Optional[bool] = None,
+               deterministic: bool = False) -> _lib.DAProblem:
     if mc_ms_feat.dim() != 3:
         raise ValueError("mc_ms_feat must be [bs, num_feat, C]")
     if sampling_location.dim() != 5 or sampling_location.shape[-1] != 2:
@@ -84,18 +88,20 @@ def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
     if spatial_shape.shape[:2] != (K, S):
         raise ValueError(f"spatial_shape is {spatial_shape.shape}, expected ({K}, {S}, 2)")
     dt = _lib.DA_BF16 if mc_ms_feat.dtype == torch.bfloat16 else _lib.DA_F32
-    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt, _flags(slices, regather))
+    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt,
+                          _flags(slices, regather, deterministic))
 
 
 def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
-             slices=None, regather=None):
+             slices=None, regather=None, deterministic=False):
     shape = _host_i32(spatial_shape)
     start = _host_i32(scale_start_index)
     dev = mc_ms_feat.device
     _need(mc_ms_feat, "mc_ms_feat", (torch.float32, torch.bfloat16), dev)
     _need(sampling_location, "sampling_location", torch.float32, dev)
     _need(weights, "weights", torch.float32, dev)
-    prob = problem_of(mc_ms_feat, shape, sampling_location, weights, slices, regather)
+    prob = problem_of(mc_ms_feat, shape, sampling_location, weights, slices, regather,
+                      deterministic)
     bs, A, P, K = (sampling_location.shape[i] for i in range(4))
     if tuple(weights.shape[:4]) != (bs, A, P, K) or mc_ms_feat.shape[0] != bs:
         raise ValueError("batch / anchor / point / camera sizes disagree between inputs")
@@ -163,11 +169,11 @@ def forward_workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights
 
 
 def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
-                   regather: Optional[bool] = None) -> int:
+                   regather: Optional[bool] = None, deterministic: bool = False) -> int:
     """Bytes of workspace da_backward / da_backward_accumulate need for these shapes."""
     lib = _lib.load()
     prob = problem_of(mc_ms_feat, _host_i32(spatial_shape), sampling_location, weights,
-                      regather=regather)
+                      regather=regather, deterministic=deterministic)
     n = ctypes.c_size_t(0)
     _lib.check(lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
                "da_backward_workspace_size")
@@ -176,10 +182,10 @@ def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
 
 def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
               weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None,
-              workspace=None, slices=None, regather=None):
+              workspace=None, slices=None, regather=None, deterministic=False):
     lib = _lib.load()
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
-                                  sampling_location, weights, slices, regather)
+                                  sampling_location, weights, slices, regather, deterministic)
     dev = mc_ms_feat.device
     _need(grad_out, "grad_out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
     if grad_feat is None:
@@ -209,20 +215,24 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
 
 def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
                 grad_out, grad_feat=None, grad_loc=None, grad_weights=None, workspace=None,
-                slices=None, regather=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
+                slices=None, regather=None, deterministic=False
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G]).
+
+    deterministic=True: grad_feat bit for bit independent of run, backward form and
+    level slices (64-bit fixed-point sums; needs finite grad_out and weights)."""
     return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
-                     workspace, slices, regather)
+                     workspace, slices, regather, deterministic)
 
 
 def da_backward_accumulate(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
                            weights, grad_out, grad_feat, grad_loc=None, grad_weights=None,
-                           workspace=None, slices=None, regather=None):
+                           workspace=None, slices=None, regather=None, deterministic=False):
     """As da_backward, adding the feature gradient into the existing ``grad_feat``."""
     return _backward("da_backward_accumulate", mc_ms_feat, spatial_shape, scale_start_index,
                      sampling_location, weights, grad_out, grad_feat, grad_loc, grad_weights,
-                     workspace, slices, regather)
+                     workspace, slices, regather, deterministic)
 
 
 def da_backward_atomic(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,

@@ -53,7 +53,7 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
                        Plan& plan) {
     if (!p) return fail(DA_ERR_INVALID_ARG, "problem is NULL");
     if ((p->flags & ~(DA_FLAG_SLICES_ALWAYS | DA_FLAG_SLICES_NEVER | DA_FLAG_BWD_REGATHER |
-                      DA_FLAG_BWD_ROW_ORDER)) != 0 ||
+                      DA_FLAG_BWD_ROW_ORDER | DA_FLAG_DETERMINISTIC)) != 0 ||
         (p->flags & DA_FLAG_SLICES_ALWAYS && p->flags & DA_FLAG_SLICES_NEVER) ||
         (p->flags & DA_FLAG_BWD_REGATHER && p->flags & DA_FLAG_BWD_ROW_ORDER))
         return fail(DA_ERR_INVALID_ARG, "problem.flags = %d is not a valid combination",
@@ -380,12 +380,15 @@ bool rows_reused(const da_problem* p, const da::KArgs& ka) {
 
 // Workspace of the gather form of the backward, each part 256-byte aligned.
 struct WsLayout {
-    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, dots, total;
+    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, dots, slots, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups) {
+// Accumulation rows of the deterministic form: one per possible long row.
+uint64_t det_slots(uint64_t n_samples) { return 4 * n_samples / (uint64_t)da::kSlotStride + 1; }
+
+WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uint64_t slot_bytes) {
     WsLayout w;
     const uint64_t n_tiles = (n_rows + da::kScanTile - 1) / da::kScanTile;
     size_t off = 0;
@@ -405,6 +408,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups) {
     off += align256(n_samples * 8);
     w.dots = off;
     off += align256(n_samples * 4 * dot_groups * 4);
+    w.slots = off;
+    off += align256(slot_bytes);
     w.total = off;
     return w;
 }
@@ -447,6 +452,9 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
     if (!aligned(grad_out, 4) || !aligned(grad_feat, 4) || !aligned(grad_weights, 4))
         return fail(DA_ERR_INVALID_ARG, "grad_out / grad_feat / grad_weights not 4-byte aligned");
     if (!aligned(grad_loc, 8)) return fail(DA_ERR_INVALID_ARG, "grad_loc is not 8-byte aligned");
+    if (mode == BwdMode::kScatter && (p->flags & DA_FLAG_DETERMINISTIC))
+        return fail(DA_ERR_UNSUPPORTED,
+                    "da_backward_atomic has no deterministic form (use da_backward)");
     st = plan_backward(p, plan, mode != BwdMode::kScatter);
     if (st != DA_OK) return st;
     da::KArgs& ka = plan.ka;
@@ -462,7 +470,9 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
         if (st != DA_OK) return st;
         if (any_sample) {
             const bool fusable = fused_capable(p);
-            const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0);
+            const bool det = p->flags & DA_FLAG_DETERMINISTIC;
+            const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0,
+                                         det ? det_slots(n_samples) * p->num_embeds * 8 : 0);
             if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
             if (!aligned(workspace, 256))
                 return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -477,6 +487,8 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.rank = reinterpret_cast<uint32_t*>(base + w.rank);
             ka.entries = reinterpret_cast<da::Entry*>(base + w.entries);
             ka.loc_part = reinterpret_cast<float*>(base + w.loc_part);
+            ka.det = det ? 1 : 0;
+            ka.slots = reinterpret_cast<long long*>(base + w.slots);
             ka.n_rows = (uint32_t)n_rows;
             ka.n_samples = (uint32_t)n_samples;
             ka.n_anchors = (uint32_t)plan.n_anchors;
@@ -687,9 +699,11 @@ da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
     uint64_t n_rows = 0, n_samples = 0;
     const da_status st = gather_sizes(p, n_rows, n_samples);
     if (st != DA_OK) return st;
+    const bool det = p->flags & DA_FLAG_DETERMINISTIC;
     *bytes = n_samples == 0
                  ? 0
-                 : ws_layout(n_rows, n_samples, fused_capable(p) ? (uint64_t)p->num_groups : 0).total;
+                 : ws_layout(n_rows, n_samples, fused_capable(p) ? (uint64_t)p->num_groups : 0,
+                             det ? det_slots(n_samples) * p->num_embeds * 8 : 0).total;
     return DA_OK;
 }
 

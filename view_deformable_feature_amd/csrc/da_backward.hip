@@ -32,6 +32,9 @@
 
 #include "da_device.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace da {
 namespace {
 
@@ -181,6 +184,11 @@ __device__ __forceinline__ void store_grad_weights(float (&gwp)[NV], const int (
     }
 }
 
+// First entry of a row in the row-sorted list.
+__device__ __forceinline__ uint32_t first_entry(const KArgs& a, uint32_t row) {
+    return a.tile_prefix[row / (uint32_t)kScanTile] + a.local_start[row];
+}
+
 // Zero the feature-gradient rows r0 .. r0+63 (r0 = 64 w) that have no entry,
 // and the long rows that gather_kernel adds to range by range.
 template <int ZVEC>
@@ -188,8 +196,13 @@ __device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int l
     const uint32_t r0 = w * (uint32_t)kWave;
     if (r0 >= a.n_rows) return;
     const uint32_t r = r0 + (uint32_t)lane;
-    const bool empty = r < a.n_rows && (a.cnt[r] == 0u || a.cnt[r] > (uint32_t)kGatherLong);
-    uint64_t m = __ballot(empty);
+    const uint32_t c = r < a.n_rows ? a.cnt[r] : 1u;
+    // rows the gather does not store whole: no entry (unless accumulating), or
+    // long (summed range by range: onto the zeroed row, or in the deterministic
+    // form onto its zeroed 64-bit accumulation row)
+    const bool empty = c == 0u && !a.accumulate;
+    const bool long_row = c > (uint32_t)kGatherLong;
+    uint64_t m = __ballot(empty || (long_row && !a.det && !a.accumulate));
     const int nvec = a.C / ZVEC;
     while (m) {
         const int l = __ffsll((unsigned long long)m) - 1;
@@ -200,6 +213,16 @@ __device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int l
                 reinterpret_cast<float4*>(row)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
             else
                 row[v] = 0.0f;
+        }
+    }
+    if (a.det) {
+        m = __ballot(long_row);
+        while (m) {
+            const int l = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            const uint32_t row = r0 + (uint32_t)l;
+            long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
+            for (int v = lane; v < a.C; v += kWave) slot[v] = 0;
         }
     }
 }
@@ -680,12 +703,18 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j) v[j] = (base + j < n) ? a.cnt[base + j] : 0u;
     }
-    uint32_t tot = 0;
+    uint32_t tot = 0, vmax = 0;
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
         const uint32_t c = v[j];
         v[j] = tot;
         tot += c;
+        vmax = max(vmax, c);
+    }
+    if (a.det) {   // the longest row bounds every row sum of the deterministic form
+        for (int m = 1; m < kWave; m <<= 1)
+            vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, m, kWave));
+        if (threadIdx.x % kWave == 0) atomicMax(a.scan_done + kCtrlMaxCnt, vmax);
     }
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const uint32_t incl = wave_inclusive_scan(tot, lane);
@@ -732,6 +761,84 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
     if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry;
 }
 
+// ------------------------------------------------------------------------------------
+// deterministic backward: 64-bit fixed point
+// ------------------------------------------------------------------------------------
+// Every feature-gradient term cw * w * grad_out is rounded once to a multiple
+// of 2^-E and summed as a 64-bit integer, so a row's sum does not depend on the
+// order its terms are added in (nor on how a long row is split).  E is chosen
+// from bound = max|grad_out| * max|w| * (longest row) -- cw <= 1 -- so that
+// |sum| * 2^E < 2^61; the rounding error of a term is at most 2^-(E+1).
+__device__ __forceinline__ int det_exponent(const KArgs& a) {
+    const double bound = (double)__uint_as_float(a.scan_done[kCtrlMaxGo]) *
+                         (double)__uint_as_float(a.scan_done[kCtrlMaxW]) *
+                         (double)a.scan_done[kCtrlMaxCnt];
+    if (!(bound > 0.0) || !(bound < 1e300)) return 0;
+    int e;
+    frexp(bound, &e);                      // bound < 2^e
+    return 61 - e;
+}
+__device__ __forceinline__ long long to_fixed(float x, int E) {
+    return __double2ll_rn(ldexp((double)x, E));
+}
+__device__ __forceinline__ float from_fixed(long long v, int E) {
+    return (float)ldexp((double)v, -E);
+}
+
+// max |grad_out| and max |weight| (float bits compare as unsigned for values >= 0)
+__global__ void __launch_bounds__(256) bound_kernel(KArgs a) {
+    __shared__ uint32_t red[2][256 / kWave];
+    const int64_t ngo = (int64_t)a.n_anchors * a.C;
+    const int64_t nw = (int64_t)a.n_samples * a.G;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t mg = 0, mw = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ngo; i += stride)
+        mg = max(mg, __float_as_uint(fabsf(a.grad_out[i])));
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nw; i += stride)
+        mw = max(mw, __float_as_uint(fabsf(a.weights[i])));
+    for (int m = 1; m < kWave; m <<= 1) {
+        mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
+        mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
+    }
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        red[0][wave] = mg;
+        red[1][wave] = mw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) {
+            mg = max(mg, red[0][w]);
+            mw = max(mw, red[1][w]);
+        }
+        atomicMax(a.scan_done + kCtrlMaxGo, mg);
+        atomicMax(a.scan_done + kCtrlMaxW, mw);
+    }
+}
+
+// After the gather: each long row's fixed-point sum to binary32, stored (or added,
+// when accumulating) into grad_feat.  One wave per 64 rows.
+__global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
+    const uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int lane = threadIdx.x % kWave;
+    const uint32_t r0 = w * (uint32_t)kWave;
+    if (r0 >= a.n_rows) return;
+    const int E = det_exponent(a);
+    const uint32_t r = r0 + (uint32_t)lane;
+    uint64_t m = __ballot(r < a.n_rows && a.cnt[r] > (uint32_t)kGatherLong);
+    while (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const uint32_t row = r0 + (uint32_t)l;
+        const long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
+        float* out = a.grad_feat + (size_t)row * a.C;
+        for (int c = lane; c < a.C; c += kWave) {
+            const float v = from_fixed(slot[c], E);
+            out[c] = a.accumulate ? out[c] + v : v;
+        }
+    }
+}
+
 // Each wave covers the range [e0, e0 + kGatherChunk) of the row-sorted entry
 // list.  A row with at most kGatherLong entries is owned by the wave whose
 // range holds its first entry: that wave follows it past the range end and
@@ -759,7 +866,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 // The walk is latency-bound: the occupancy hint (5 waves per SIMD for one
 // vector per lane, measured faster despite a few spilled registers) keeps more
 // waves in flight.
-template <typename T, int VEC, int NV, bool FUSED>
+template <typename T, int VEC, int NV, bool FUSED, bool DET>
 __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
@@ -845,11 +952,14 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
         dvalid[i] = lane + kWave * i < nvec && (lane & (seg - 1)) == seg - 1;
     }
 
-    float acc[NV][VEC];
+    // DET: 64-bit fixed-point sums (multiples of 2^-E), else binary32
+    using Acc = typename std::conditional<DET, long long, float>::type;
+    const int E = DET ? det_exponent(a) : 0;
+    Acc acc[NV][VEC];
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[i][k] = 0.0f;
+        for (int k = 0; k < VEC; ++k) acc[i][k] = 0;
 
     // Write (or add) the row's sum through a buffer resource that spans exactly
     // that row: lanes past its last vector fall outside the range and their
@@ -859,17 +969,39 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
     auto flush = [&](uint32_t row_bits) {
         const uint32_t row = row_bits & ~kEntryLongRow;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(a.grad_feat + (size_t)row * C, (uint32_t)C * 4u);
+        long long* slot = nullptr;
+        if constexpr (DET) {
+            if (row_bits & kEntryLongRow)
+                slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * C;
+        }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const uint32_t off = (uint32_t)((lane + kWave * i) * VEC * 4);
             if (row_bits & kEntryLongRow) {
+                if constexpr (DET) {
+                    // 64-bit integer additions: exact, so their order does not matter
+                    const int c0 = (lane + kWave * i) * VEC;
+                    if (c0 < C) {
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][k], r, off + 4u * k, 0, 0);
+                        for (int k = 0; k < VEC; ++k)
+                            atomicAdd(reinterpret_cast<unsigned long long*>(slot + c0 + k),
+                                      (unsigned long long)acc[i][k]);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k)
+                        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][k], r, off + 4u * k,
+                                                                        0, 0);
+                }
             } else {
                 float o[VEC];
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) o[k] = acc[i][k];
+                for (int k = 0; k < VEC; ++k) {
+                    if constexpr (DET)
+                        o[k] = from_fixed(acc[i][k], E);
+                    else
+                        o[k] = acc[i][k];
+                }
                 if (a.accumulate) {
                     float old[VEC];
                     VecLoad<float, VEC>::run(r, off, 0u, old);
@@ -886,7 +1018,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
                 }
             }
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[i][k] = 0.0f;
+            for (int k = 0; k < VEC; ++k) acc[i][k] = 0;
         }
     };
 
@@ -939,7 +1071,12 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
         for (int i = 0; i < NV; ++i) {
             const float sc = B.cw[u] * B.wt[u][i];
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[i][k] += sc * B.go[u][i][k];
+            for (int k = 0; k < VEC; ++k) {
+                if constexpr (DET)
+                    acc[i][k] += to_fixed(sc * B.go[u][i][k], E);
+                else
+                    acc[i][k] += sc * B.go[u][i][k];
+            }
         }
         if constexpr (FUSED) {
             if (B.fnew[u]) {
@@ -1101,28 +1238,34 @@ hipError_t sliced_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipS
     }
 }
 
-template <typename T, int VEC, bool FUSED>
-hipError_t gather_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+template <typename T, int VEC, bool FUSED, bool DET>
+hipError_t gather_dispatch_det(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
     // C <= 1024 in the backward: 16-byte vectors need at most 4 per lane
     switch (s.gather_nv) {
-        case 1: hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED>), grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED>), grid, dim3(256), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED, DET>), grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED, DET>), grid, dim3(256), 0, st, a); break;
         case 8:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<T, 1, 8, false>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 8, false, DET>), grid, dim3(256), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
         case 16:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<T, 1, 16, false>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 16, false, DET>), grid, dim3(256), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T, int VEC, bool FUSED>
+hipError_t gather_dispatch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
+    return a.det ? gather_dispatch_det<T, VEC, FUSED, true>(a, s, grid, st)
+                 : gather_dispatch_det<T, VEC, FUSED, false>(a, s, grid, st);
 }
 
 unsigned blocks_for(int64_t n, int per_block) {
@@ -1153,9 +1296,15 @@ hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t
 
 hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
                                   bool bf16, hipStream_t stream) {
-    // the scan counter and the row counts are one zeroed range
+    // the control words and the row counts are one zeroed range
     hipError_t e = launch_fill_zero(a.scan_done, (int64_t)(a.cnt - a.scan_done) + a.n_rows, stream);
     if (e != hipSuccess) return e;
+    if (a.det) {
+        const int64_t n = std::max<int64_t>((int64_t)a.n_anchors * a.C, (int64_t)a.n_samples * a.G);
+        hipLaunchKernelGGL(bound_kernel, dim3((unsigned)std::min<int64_t>(1024, blocks_for(n, 256))),
+                           dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
     hipLaunchKernelGGL(count_kernel, cgrid, dim3(kCountThreads), 0, stream, a);
@@ -1163,7 +1312,10 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     KArgs k = a;
-    const int64_t zwaves = a.accumulate ? 0 : ((int64_t)a.n_rows + kWave - 1) / kWave;
+    const int64_t row_waves = ((int64_t)a.n_rows + kWave - 1) / kWave;
+    // rows to zero before the gather: none when accumulating, unless long rows
+    // need their 64-bit accumulation rows zeroed
+    const int64_t zwaves = (a.accumulate && !a.det) ? 0 : row_waves;
     const int64_t waves = ((int64_t)a.n_samples * 4 + kGatherChunk - 1) / kGatherChunk;
     if (a.fused) {
         // bucketing (+ zeroing blocks), the gather with the dot products, then
@@ -1183,38 +1335,45 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         if ((a.S & (a.S - 1)) != 0 || a.S > kWave) {
             hipLaunchKernelGGL(loc_reduce_kernel, dim3(blocks_for((int64_t)a.n_anchors * a.npk, 256)),
                                dim3(256), 0, stream, k);
-            return hipGetLastError();
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        return hipSuccess;
-    }
-    // per-anchor kernel, followed (unless accumulating) by blocks that zero the
-    // rows the gather does not store whole
-    k.anchor_blocks = (uint32_t)(a.sliced ? n_anchors_total * kSlices : n_anchors_total);
-    const dim3 grid((unsigned)(k.anchor_blocks + blocks_for(zwaves, s.waves)), 1);
-    if (a.sliced) {
-        if (bf16)
-            e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(k, s, grid, stream)
-                           : sliced_dispatch<uint16_t, 1>(k, s, grid, stream);
-        else
-            e = s.vec == 4 ? sliced_dispatch<float, 4>(k, s, grid, stream)
-                           : sliced_dispatch<float, 1>(k, s, grid, stream);
     } else {
-        if (bf16)
-            e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(k, s, grid, stream)
-                           : anchor_dispatch_scalar<uint16_t, false>(k, s, grid, stream);
-        else
-            e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(k, s, grid, stream)
-                           : anchor_dispatch_scalar<float, false>(k, s, grid, stream);
+        // per-anchor kernel, followed by blocks that zero the rows the gather
+        // does not store whole
+        k.anchor_blocks = (uint32_t)(a.sliced ? n_anchors_total * kSlices : n_anchors_total);
+        const dim3 grid((unsigned)(k.anchor_blocks + blocks_for(zwaves, s.waves)), 1);
+        if (a.sliced) {
+            if (bf16)
+                e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(k, s, grid, stream)
+                               : sliced_dispatch<uint16_t, 1>(k, s, grid, stream);
+            else
+                e = s.vec == 4 ? sliced_dispatch<float, 4>(k, s, grid, stream)
+                               : sliced_dispatch<float, 1>(k, s, grid, stream);
+        } else {
+            if (bf16)
+                e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(k, s, grid, stream)
+                               : anchor_dispatch_scalar<uint16_t, false>(k, s, grid, stream);
+            else
+                e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(k, s, grid, stream)
+                               : anchor_dispatch_scalar<float, false>(k, s, grid, stream);
+        }
+        if (e != hipSuccess) return e;
+        // gather: one wave per chunk of the largest possible entry count (4 per
+        // sample; waves past the real total return at once), followed in the
+        // sliced form by blocks that add up the location partials
+        k.gather_blocks = blocks_for(waves, 256 / kWave);
+        const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, 256) : 0;
+        const dim3 ggrid((unsigned)(k.gather_blocks + lr));
+        e = a.gather_vec == 4 ? gather_dispatch<float, 4, false>(k, s, ggrid, stream)
+                              : gather_dispatch<float, 1, false>(k, s, ggrid, stream);
+        if (e != hipSuccess) return e;
     }
-    if (e != hipSuccess) return e;
-    // gather: one wave per chunk of the largest possible entry count (4 per
-    // sample; waves past the real total return at once), followed in the
-    // sliced form by blocks that add up the location partials
-    k.gather_blocks = blocks_for(waves, 256 / kWave);
-    const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, 256) : 0;
-    const dim3 ggrid((unsigned)(k.gather_blocks + lr));
-    return a.gather_vec == 4 ? gather_dispatch<float, 4, false>(k, s, ggrid, stream)
-                             : gather_dispatch<float, 1, false>(k, s, ggrid, stream);
+    if (a.det) {
+        hipLaunchKernelGGL(long_rows_kernel, dim3(blocks_for(row_waves, 256 / kWave)), dim3(256), 0,
+                           stream, k);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace da

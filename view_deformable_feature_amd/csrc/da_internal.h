@@ -27,6 +27,15 @@ constexpr int kCountLdsRows = 16 * kCountThreads;
 // row a single wave sums whole (longer rows are added range by range).
 constexpr int kGatherChunk = 64;
 constexpr int kGatherLong = 64;
+// Deterministic backward: a long row (> kGatherLong entries) starting at entry
+// `first` owns the int64 accumulation row first / kSlotStride -- unique, since
+// the next long row starts at least kSlotStride entries later.
+constexpr int kSlotStride = kGatherLong + 1;
+// Words of the control block at the start of the backward workspace.
+constexpr int kCtrlScanDone = 0;   // scan workgroups finished
+constexpr int kCtrlMaxGo = 1;      // max |grad_out| (float bits)
+constexpr int kCtrlMaxW = 2;       // max |weight| (float bits)
+constexpr int kCtrlMaxCnt = 3;     // max entries of one row
 
 // One (sample, corner) contribution to the feature gradient, bucketed by row.
 // Offsets are stored in bytes so that the gather does no index arithmetic.
@@ -73,7 +82,7 @@ struct KArgs {
     float* grad_loc;           // [bs, A, P, K, 2]
     float* grad_weights;       // [bs, A, P, K, S, G]
     // feature-gradient gather workspace
-    uint32_t* scan_done;       // tiles scanned so far (zeroed with cnt, which follows it)
+    uint32_t* scan_done;       // control words (kCtrl*), zeroed with cnt, which follows them
     uint32_t* cnt;             // [n_rows] entries per row, then per-row rank source
     uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile
     uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
@@ -97,6 +106,9 @@ struct KArgs {
     uint32_t feat_all_bytes;   // bs * num_feat * C * elem (< 2^32 on this path)
     float* dots;               // [n_samples, 4, G]: entry (q, corner) at (4q + corner) * G
     int32_t w_vec4;            // weights / grad_weights rows readable as float4
+    // Deterministic backward: feature-gradient sums in 64-bit fixed point
+    int32_t det;
+    long long* slots;          // [n_slots, C] accumulation rows of the long rows
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
