@@ -99,7 +99,7 @@ typedef enum {
  * term is rounded once to a multiple of 2^-E and the terms of a row are summed as 64-bit
  * integers, which makes grad_feat independent of the order the terms arrive in: bit for
  * bit the same across runs, backward forms and level slices.  E is derived on the GPU
- * from max|grad_out| * max|weights| * (most terms of any row), leaving ~2^-60 of that
+ * from max|grad_out| * max|weights| * (most terms of any row), leaving ~2^-50 of that
  * bound as the resolution.  grad_out and weights must be finite.  Costs the workspace
  * a 64-bit row per long row (see da_backward_workspace_size). */
 #define DA_FLAG_DETERMINISTIC 16
@@ -171,8 +171,8 @@ da_status da_forward(const da_problem* problem,
  * da_backward_accumulate need for `problem` (0 when there is no sample): about
  * 8 * bs * num_feat + (88 + 16 * G) * bs*A*P*K*S where the row-ordered backward
  * may apply, else 8 * bs * num_feat + 88 * bs*A*P*K*S; with DA_FLAG_DETERMINISTIC
- * another 8 * C * (4 * bs*A*P*K*S / 65 + 1).  Only the sizes and flags in `problem`
- * are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
+ * another (8 * C + 4) * (4 * bs*A*P*K*S / 65 + 1) + 8 * bs*K*S * ceil(A*P / 256).
+ * Only the sizes and flags in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */

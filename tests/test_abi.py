@@ -211,9 +211,10 @@ def test_workspace_size_and_checks(lib):
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_embeds=48, num_groups=2)),
                                           ctypes.byref(n)) == 0
     assert n.value == 256 + 2 * 4 * n_rows + 256 + n_samples * 16 + n_samples * 4 * 16 + 256
-    # deterministic form: + one 64-bit row of C per possible long row (4 * 32 // 65 + 1 = 2)
+    # deterministic form: + one 64-bit row of C and a row index per possible long row
+    # (4 * 32 // 65 + 1 = 2), + two words per counting block (one), 256-byte aligned
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(flags=16)), ctypes.byref(n)) == 0
-    assert n.value == expect + 2 * 32 * 8
+    assert n.value == expect + -(-(2 * (32 * 8 + 4) + 8) // 256) * 256
     assert _bwd(lib, _prob(flags=16), "da_backward_atomic") == 2 and "deterministic" in _msg(lib)
     assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value == expect

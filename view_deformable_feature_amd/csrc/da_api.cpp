@@ -387,6 +387,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Accumulation rows of the deterministic form: one per possible long row.
 uint64_t det_slots(uint64_t n_samples) { return 4 * n_samples / (uint64_t)da::kSlotStride + 1; }
+// Blocks of count_kernel: 256 (anchor, point) pairs at one level of one batch image.
+uint64_t count_blocks(const da_problem* p) {
+    return (uint64_t)((p->num_anchors * p->num_pts + 255) / 256) * p->num_cams * p->num_scale *
+           p->bs;
+}
+// the accumulation rows, the list of long rows, then the count blocks' maxima
+uint64_t det_bytes(const da_problem* p, uint64_t n_samples) {
+    return det_slots(n_samples) * ((uint64_t)p->num_embeds * 8 + 4) + 8 * count_blocks(p);
+}
 
 WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uint64_t slot_bytes) {
     WsLayout w;
@@ -472,7 +481,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             const bool fusable = fused_capable(p);
             const bool det = p->flags & DA_FLAG_DETERMINISTIC;
             const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0,
-                                         det ? det_slots(n_samples) * p->num_embeds * 8 : 0);
+                                         det ? det_bytes(p, n_samples) : 0);
             if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
             if (!aligned(workspace, 256))
                 return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -489,6 +498,10 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.loc_part = reinterpret_cast<float*>(base + w.loc_part);
             ka.det = det ? 1 : 0;
             ka.slots = reinterpret_cast<long long*>(base + w.slots);
+            ka.n_slots = (uint32_t)det_slots(n_samples);
+            ka.long_rows = reinterpret_cast<uint32_t*>(ka.slots + (size_t)ka.n_slots * p->num_embeds);
+            ka.bound_part = ka.long_rows + ka.n_slots;
+            ka.count_blocks = (uint32_t)count_blocks(p);
             ka.n_rows = (uint32_t)n_rows;
             ka.n_samples = (uint32_t)n_samples;
             ka.n_anchors = (uint32_t)plan.n_anchors;
@@ -703,7 +716,7 @@ da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
     *bytes = n_samples == 0
                  ? 0
                  : ws_layout(n_rows, n_samples, fused_capable(p) ? (uint64_t)p->num_groups : 0,
-                             det ? det_slots(n_samples) * p->num_embeds * 8 : 0).total;
+                             det ? det_bytes(p, n_samples) : 0).total;
     return DA_OK;
 }
 

@@ -217,12 +217,27 @@ __device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int l
     }
     if (a.det) {
         m = __ballot(long_row);
+        if (m != 0) {
+            // list this wave's long rows for long_rows_kernel
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(a.scan_done + kCtrlLongRows, (uint32_t)__popcll(m));
+            base = (uint32_t)__shfl((int)base, 0, kWave);
+            const uint32_t rank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+            if (long_row && base + rank < a.n_slots) a.long_rows[base + rank] = r;
+        }
+        // every lane looks up its own long row's slot before the loop
+        const uint32_t slot_id = long_row ? first_entry(a, r) / kSlotStride : 0u;
         while (m) {
             const int l = __ffsll((unsigned long long)m) - 1;
             m &= m - 1;
-            const uint32_t row = r0 + (uint32_t)l;
-            long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
-            for (int v = lane; v < a.C; v += kWave) slot[v] = 0;
+            long long* slot =
+                a.slots + (size_t)(uint32_t)__builtin_amdgcn_readlane((int)slot_id, l) * a.C;
+            if ((a.C & 1) == 0) {      // rows start 16-byte aligned
+                for (int v = lane; v < a.C / 2; v += kWave)
+                    reinterpret_cast<longlong2*>(slot)[v] = make_longlong2(0, 0);
+            } else {
+                for (int v = lane; v < a.C; v += kWave) slot[v] = 0;
+            }
         }
     }
 }
@@ -596,6 +611,37 @@ __device__ __forceinline__ void loc_reduce_role(const KArgs& a) {
 // ------------------------------------------------------------------------------------
 // gather form: count, scan, gather
 // ------------------------------------------------------------------------------------
+// max |p[i]| over i = i0, i0 + stride, ... below n, as float bits (which order
+// like the values for values >= 0)
+__device__ __forceinline__ uint32_t abs_max_bits(const float* p, int64_t n, int64_t i0,
+                                                 int64_t stride) {
+    uint32_t m = 0;
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {      // 16-byte loads, then the tail
+        const int64_t n4 = n / 4;
+        const float4* p4 = reinterpret_cast<const float4*>(p);
+        int64_t i = i0;
+        for (; i + 3 * stride < n4; i += 4 * stride) {      // four loads in flight
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = p4[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                m = max(m, max(max(__float_as_uint(fabsf(v[u].x)), __float_as_uint(fabsf(v[u].y))),
+                               max(__float_as_uint(fabsf(v[u].z)), __float_as_uint(fabsf(v[u].w)))));
+        }
+        for (; i < n4; i += stride) {
+            const float4 v = p4[i];
+            m = max(m, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
+                           max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
+        }
+        for (int64_t i = n4 * 4 + i0; i < n; i += stride) m = max(m, __float_as_uint(fabsf(p[i])));
+    } else {
+        for (int64_t i = i0; i < n; i += stride) m = max(m, __float_as_uint(fabsf(p[i])));
+    }
+    return m;
+}
+
+
 // Level-major counting.  Workgroup (x, level, b) takes 256 consecutive
 // (anchor, point) pairs of batch b at one (camera, scale) level, one thread per
 // sample, and gives every inside corner the next slot of its feature row.
@@ -603,7 +649,8 @@ __device__ __forceinline__ void loc_reduce_role(const KArgs& a) {
 // global atomics would serialise -- are first counted in an LDS histogram of
 // the level; one global atomic per touched row then reserves the workgroup's
 // block of slots.  Large levels count straight into global memory.  The slot
-// order inside a row is whatever order the atomics retire in.
+// order inside a row is whatever order the atomics retire in.  The
+// deterministic form also takes the maxima of |weights| and |grad_out| here.
 __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     __shared__ uint32_t hist[kCountLdsRows];
     const int lvl = blockIdx.y;
@@ -665,6 +712,36 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     }
     if (valid)
         *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
+    if (a.det) {
+        // bounds for the fixed point: this sample's weights and a share of
+        // grad_out; the block's maxima go to bound_part (reduced by the scan)
+        __shared__ uint32_t red[2][kCountThreads / kWave];
+        const uint32_t fb = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        const uint32_t nb = gridDim.x * gridDim.y * gridDim.z;
+        uint32_t mw = 0;
+        if (valid) mw = abs_max_bits(a.weights + (size_t)q * a.G, a.G, 0, 1);
+        uint32_t mg = abs_max_bits(a.grad_out, (int64_t)a.n_anchors * a.C,
+                                   (int64_t)fb * kCountThreads + threadIdx.x,
+                                   (int64_t)nb * kCountThreads);
+        for (int m = 1; m < kWave; m <<= 1) {
+            mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
+            mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
+        }
+        const int wave = threadIdx.x / kWave;
+        if (threadIdx.x % kWave == 0) {
+            red[0][wave] = mg;
+            red[1][wave] = mw;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kCountThreads / kWave; ++w) {
+                mg = max(mg, red[0][w]);
+                mw = max(mw, red[1][w]);
+            }
+            a.bound_part[2 * fb] = mg;
+            a.bound_part[2 * fb + 1] = mw;
+        }
+    }
 }
 
 // Inclusive prefix sum of v over the 64 lanes of a wave.
@@ -684,7 +761,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
 // device scope before the counter increment; acquire: the last workgroup
 // fences after seeing the count, before reading the totals.)
 __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
-    __shared__ uint32_t wave_tot[kScanThreads / kWave];
+    __shared__ uint32_t wave_tot[kScanThreads / kWave], wave_tot2[kScanThreads / kWave];
     __shared__ uint32_t is_last;
     const uint32_t n = a.n_rows;
     const uint32_t base = blockIdx.x * (uint32_t)kScanTile + threadIdx.x * (uint32_t)kScanItems;
@@ -759,6 +836,31 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
         carry += all;
     }
     if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry;
+    if (a.det) {   // the count blocks' maxima of |grad_out| and |w|
+        uint32_t mg = 0, mw = 0;
+        for (uint32_t i = threadIdx.x; i < a.count_blocks; i += kScanThreads) {
+            mg = max(mg, a.bound_part[2 * i]);
+            mw = max(mw, a.bound_part[2 * i + 1]);
+        }
+        for (int m = 1; m < kWave; m <<= 1) {
+            mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
+            mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
+        }
+        __syncthreads();                       // wave_tot is reused
+        if (lane == 0) {
+            wave_tot[wave] = mg;
+            wave_tot2[wave] = mw;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w2 = 1; w2 < kScanThreads / kWave; ++w2) {
+                mg = max(mg, wave_tot[w2]);
+                mw = max(mw, wave_tot2[w2]);
+            }
+            a.scan_done[kCtrlMaxGo] = mg;
+            a.scan_done[kCtrlMaxW] = mw;
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -768,7 +870,8 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 // of 2^-E and summed as a 64-bit integer, so a row's sum does not depend on the
 // order its terms are added in (nor on how a long row is split).  E is chosen
 // from bound = max|grad_out| * max|w| * (longest row) -- cw <= 1 -- so that
-// |sum| * 2^E < 2^61; the rounding error of a term is at most 2^-(E+1).
+// |sum| * 2^E < 2^50 (one bit spare for the rounding of a term's product); the
+// rounding error of a term is at most 2^-(E+1).
 __device__ __forceinline__ int det_exponent(const KArgs& a) {
     const double bound = (double)__uint_as_float(a.scan_done[kCtrlMaxGo]) *
                          (double)__uint_as_float(a.scan_done[kCtrlMaxW]) *
@@ -776,66 +879,39 @@ __device__ __forceinline__ int det_exponent(const KArgs& a) {
     if (!(bound > 0.0) || !(bound < 1e300)) return 0;
     int e;
     frexp(bound, &e);                      // bound < 2^e
-    return 61 - e;
+    return 50 - e;
 }
-__device__ __forceinline__ long long to_fixed(float x, int E) {
-    return __double2ll_rn(ldexp((double)x, E));
+// Rounding a term t to the integer RNE(t 2^E) in three instructions: with
+// |t 2^E| < 2^51, t 2^E + 1.5 * 2^52 lies in [2^52, 2^53), where binary64 spacing
+// is 1 (so the fma rounds t 2^E to an integer, ties to even: the constant is
+// even) and the encoding of an integer is that integer plus a fixed offset.
+// Encodings are summed as 64-bit words (wrapping); fixed_value() removes the
+// offset once per term summed.
+constexpr double kFixMagic = 6755399441055744.0;            // 1.5 * 2^52
+__device__ __forceinline__ unsigned long long fixed_code(float t, double scale) {
+    return (unsigned long long)__double_as_longlong(fma((double)t, scale, kFixMagic));
+}
+__device__ __forceinline__ long long fixed_value(unsigned long long code_sum, uint32_t terms) {
+    return (long long)(code_sum -
+                       (unsigned long long)terms * (unsigned long long)__double_as_longlong(kFixMagic));
 }
 __device__ __forceinline__ float from_fixed(long long v, int E) {
     return (float)ldexp((double)v, -E);
 }
 
-// max |grad_out| and max |weight| (float bits compare as unsigned for values >= 0)
-__global__ void __launch_bounds__(256) bound_kernel(KArgs a) {
-    __shared__ uint32_t red[2][256 / kWave];
-    const int64_t ngo = (int64_t)a.n_anchors * a.C;
-    const int64_t nw = (int64_t)a.n_samples * a.G;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    uint32_t mg = 0, mw = 0;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ngo; i += stride)
-        mg = max(mg, __float_as_uint(fabsf(a.grad_out[i])));
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nw; i += stride)
-        mw = max(mw, __float_as_uint(fabsf(a.weights[i])));
-    for (int m = 1; m < kWave; m <<= 1) {
-        mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
-        mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
-    }
-    const int wave = threadIdx.x / kWave;
-    if (threadIdx.x % kWave == 0) {
-        red[0][wave] = mg;
-        red[1][wave] = mw;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) {
-            mg = max(mg, red[0][w]);
-            mw = max(mw, red[1][w]);
-        }
-        atomicMax(a.scan_done + kCtrlMaxGo, mg);
-        atomicMax(a.scan_done + kCtrlMaxW, mw);
-    }
-}
-
 // After the gather: each long row's fixed-point sum to binary32, stored (or added,
-// when accumulating) into grad_feat.  One wave per 64 rows.
+// when accumulating) into grad_feat.  One wave per listed long row.
 __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
     const uint32_t w = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
     const int lane = threadIdx.x % kWave;
-    const uint32_t r0 = w * (uint32_t)kWave;
-    if (r0 >= a.n_rows) return;
+    if (w >= min(a.scan_done[kCtrlLongRows], a.n_slots)) return;
     const int E = det_exponent(a);
-    const uint32_t r = r0 + (uint32_t)lane;
-    uint64_t m = __ballot(r < a.n_rows && a.cnt[r] > (uint32_t)kGatherLong);
-    while (m) {
-        const int l = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const uint32_t row = r0 + (uint32_t)l;
-        const long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
-        float* out = a.grad_feat + (size_t)row * a.C;
-        for (int c = lane; c < a.C; c += kWave) {
-            const float v = from_fixed(slot[c], E);
-            out[c] = a.accumulate ? out[c] + v : v;
-        }
+    const uint32_t row = a.long_rows[w];
+    const long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
+    float* out = a.grad_feat + (size_t)row * a.C;
+    for (int c = lane; c < a.C; c += kWave) {
+        const float v = from_fixed(slot[c], E);
+        out[c] = a.accumulate ? out[c] + v : v;
     }
 }
 
@@ -867,7 +943,7 @@ __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
 // vector per lane, measured faster despite a few spilled registers) keeps more
 // waves in flight.
 template <typename T, int VEC, int NV, bool FUSED, bool DET>
-__global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
+__global__ void __launch_bounds__(256, NV == 1 ? (DET ? 4 : 5) : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
         return;
@@ -952,9 +1028,12 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
         dvalid[i] = lane + kWave * i < nvec && (lane & (seg - 1)) == seg - 1;
     }
 
-    // DET: 64-bit fixed-point sums (multiples of 2^-E), else binary32
-    using Acc = typename std::conditional<DET, long long, float>::type;
+    // DET: 64-bit fixed-point sums (multiples of 2^-E) kept as sums of the
+    // terms' codes (fixed_code), `terms` of them; else binary32
+    using Acc = typename std::conditional<DET, unsigned long long, float>::type;
     const int E = DET ? det_exponent(a) : 0;
+    const double scale = DET ? ldexp(1.0, E) : 0.0;
+    uint32_t terms = 0;
     Acc acc[NV][VEC];
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -985,7 +1064,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
 #pragma unroll
                         for (int k = 0; k < VEC; ++k)
                             atomicAdd(reinterpret_cast<unsigned long long*>(slot + c0 + k),
-                                      (unsigned long long)acc[i][k]);
+                                      (unsigned long long)fixed_value(acc[i][k], terms));
                     }
                 } else {
 #pragma unroll
@@ -998,7 +1077,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     if constexpr (DET)
-                        o[k] = from_fixed(acc[i][k], E);
+                        o[k] = from_fixed(fixed_value(acc[i][k], terms), E);
                     else
                         o[k] = acc[i][k];
                 }
@@ -1020,6 +1099,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[i][k] = 0;
         }
+        terms = 0;
     };
 
     struct Batch {
@@ -1073,11 +1153,12 @@ __global__ void __launch_bounds__(256, NV == 1 ? 5 : (NV == 2 ? 4 : 1)) gather_k
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 if constexpr (DET)
-                    acc[i][k] += to_fixed(sc * B.go[u][i][k], E);
+                    acc[i][k] += fixed_code(sc * B.go[u][i][k], scale);
                 else
                     acc[i][k] += sc * B.go[u][i][k];
             }
         }
+        if constexpr (DET) ++terms;
         if constexpr (FUSED) {
             if (B.fnew[u]) {
 #pragma unroll
@@ -1299,14 +1380,9 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     // the control words and the row counts are one zeroed range
     hipError_t e = launch_fill_zero(a.scan_done, (int64_t)(a.cnt - a.scan_done) + a.n_rows, stream);
     if (e != hipSuccess) return e;
-    if (a.det) {
-        const int64_t n = std::max<int64_t>((int64_t)a.n_anchors * a.C, (int64_t)a.n_samples * a.G);
-        hipLaunchKernelGGL(bound_kernel, dim3((unsigned)std::min<int64_t>(1024, blocks_for(n, 256))),
-                           dim3(256), 0, stream, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
+    if (a.det && (uint64_t)cgrid.x * cgrid.y * cgrid.z != a.count_blocks) return hipErrorInvalidValue;
     hipLaunchKernelGGL(count_kernel, cgrid, dim3(kCountThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
@@ -1369,7 +1445,7 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         if (e != hipSuccess) return e;
     }
     if (a.det) {
-        hipLaunchKernelGGL(long_rows_kernel, dim3(blocks_for(row_waves, 256 / kWave)), dim3(256), 0,
+        hipLaunchKernelGGL(long_rows_kernel, dim3(blocks_for(a.n_slots, 256 / kWave)), dim3(256), 0,
                            stream, k);
         return hipGetLastError();
     }

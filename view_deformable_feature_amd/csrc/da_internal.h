@@ -36,6 +36,7 @@ constexpr int kCtrlScanDone = 0;   // scan workgroups finished
 constexpr int kCtrlMaxGo = 1;      // max |grad_out| (float bits)
 constexpr int kCtrlMaxW = 2;       // max |weight| (float bits)
 constexpr int kCtrlMaxCnt = 3;     // max entries of one row
+constexpr int kCtrlLongRows = 4;   // long rows listed in long_rows (deterministic form)
 
 // One (sample, corner) contribution to the feature gradient, bucketed by row.
 // Offsets are stored in bytes so that the gather does no index arithmetic.
@@ -109,6 +110,10 @@ struct KArgs {
     // Deterministic backward: feature-gradient sums in 64-bit fixed point
     int32_t det;
     long long* slots;          // [n_slots, C] accumulation rows of the long rows
+    uint32_t* long_rows;       // [n_slots] the long rows, in no particular order
+    uint32_t n_slots;
+    uint32_t* bound_part;      // [count_kernel blocks][2] each block's max |grad_out|, max |w|
+    uint32_t count_blocks;
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
