@@ -34,12 +34,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nuscenes.json")
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources: counter-derived traffic is reported only for the
-    kernels it was measured on."""
+    """Hash of the kernel and launch sources (not the public header, which only
+    declares): counter-derived traffic is reported only for the code it was
+    measured on."""
     import hashlib
     from view_deformable_feature_amd.build import HEADERS, SOURCES
     h = hashlib.sha256()
-    for f in sorted(SOURCES + HEADERS):
+    for f in sorted(SOURCES + [x for x in HEADERS if not x.endswith("deformagg.h")]):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -70,19 +71,20 @@ def copy_calibration(nbytes):
 
 
 FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
-BWD_KERNELS = ("da_backward call: fill_zero_kernel, count_kernel, scan_tiles_kernel, "
+BWD_KERNELS = ("da_backward call: prep_kernel, count_kernel, scan_tiles_kernel, "
                "bucket_kernel (+ zeroing blocks), gather_kernel (+ group dot products), "
                "finalize_kernel")
 
 
-def algorithmic_bytes(wl):
-    """Bytes each direction must move ("Byte accounting")."""
+def algorithmic_bytes(wl, out_bytes=4):
+    """Bytes each direction must move: corner rows, locations, weights and out (or
+    grad_out) of out_bytes per element, plus the backward's gradients."""
     n_s = wl.num_samples
     n_pk = wl.bs * wl.anchors * wl.pts * wl.num_cams
     e = wl.feat_elem_bytes
     C, G = wl.C, wl.groups
-    b_fwd = 4 * C * e * n_s + 8 * n_pk + 4 * G * n_s + 4 * wl.bs * wl.anchors * C
-    b_bwd = (4 * wl.bs * wl.anchors * C + 4 * C * e * n_s + 16 * C * n_s + 16 * n_pk
+    b_fwd = 4 * C * e * n_s + 8 * n_pk + 4 * G * n_s + out_bytes * wl.bs * wl.anchors * C
+    b_bwd = (out_bytes * wl.bs * wl.anchors * C + 4 * C * e * n_s + 16 * C * n_s + 16 * n_pk
              + 8 * G * n_s)
     return b_fwd, b_bwd
 
@@ -114,7 +116,7 @@ def bench_pack(args):
     import view_deformable_feature_amd as vdf
     from view_deformable_feature_amd import workloads as W
     wl = W.WORKLOADS[args.workload]
-    dt = torch.bfloat16 if wl.feat_dtype == "bf16" else torch.float32
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.feat_dtype]
     gen = torch.Generator(device="cuda").manual_seed(wl.seed)
     maps = [torch.randn((wl.bs, wl.num_cams, wl.C, h, w), device="cuda", generator=gen).to(dt)
             for h, w in wl.levels]
@@ -158,7 +160,7 @@ def bench_pack(args):
            "value": 4 * nbytes / t, "unit": "B/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32" if dt == torch.float32 else "bf16", "data": "synthetic",
+           "dtype": wl.feat_dtype, "data": "synthetic",
            "config": {"workload": f"{wl.name} feature maps: {wl.num_cams} cameras, scales "
                                   + "/".join(f"{h}x{w_}" for h, w_ in wl.levels)
                                   + f", C={wl.C}, bs={wl.bs}", "tensor_bytes": nbytes},
@@ -186,6 +188,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--out-dtype", default="f32", choices=("f32", "bf16", "f16"),
+                    help="element type of out and grad_out (binary32 arithmetic throughout)")
     ap.add_argument("--deterministic", action="store_true",
                     help="run the backward in its deterministic (64-bit fixed-point) form")
     ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack"),
@@ -217,12 +221,13 @@ def main():
     if inp["feat"].dtype == np.uint16:
         feat = torch.from_numpy(inp["feat"].view(np.int16)).to(dev).view(torch.bfloat16)
     else:
-        feat = torch.from_numpy(inp["feat"]).to(dev)
+        feat = torch.from_numpy(inp["feat"]).to(dev)           # float32 or float16
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.out_dtype]
     loc = torch.from_numpy(inp["loc"]).to(dev)
     w = torch.from_numpy(inp["weights"]).to(dev)
-    go = torch.from_numpy(inp["grad_out"]).to(dev)
+    go = torch.from_numpy(inp["grad_out"]).to(dev).to(odt)
     shape, start = inp["spatial_shape"], inp["scale_start_index"]
-    out = torch.empty((wl.bs, wl.anchors, wl.C), device=dev, dtype=torch.float32)
+    out = torch.empty((wl.bs, wl.anchors, wl.C), device=dev, dtype=odt)
     gf = torch.empty(tuple(feat.shape), device=dev, dtype=torch.float32)
     gl = torch.empty(tuple(loc.shape), device=dev, dtype=torch.float32)
     gw = torch.empty(tuple(w.shape), device=dev, dtype=torch.float32)
@@ -230,8 +235,8 @@ def main():
     fws_n = vdf.forward_workspace_size(feat, shape, loc, w)
     fws = torch.empty(fws_n, device=dev, dtype=torch.uint8) if fws_n else None
     det = args.deterministic
-    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w, deterministic=det), device=dev,
-                      dtype=torch.uint8)
+    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w, deterministic=det,
+                                         grad_out_dtype=odt), device=dev, dtype=torch.uint8)
 
     def step(ev=None):
         if ev is not None:
@@ -259,12 +264,13 @@ def main():
     t_fwd = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_bwd = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     t_step = wall / args.steps
-    b_fwd, b_bwd = algorithmic_bytes(wl)
+    b_fwd, b_bwd = algorithmic_bytes(wl, out.element_size())
     sc = wl.sample_channels
     fwd_s, bwd_s = float(t_fwd.mean()), float(t_bwd.mean())
     dominant = "backward" if bwd_s >= fwd_s else "forward"
 
-    traffic = measured_traffic(wl.name)
+    # counter totals are taken on the binary32-out configuration only
+    traffic = measured_traffic(wl.name) if args.out_dtype == "f32" else None
 
     def roof(bytes_, secs, kernel, direction):
         a = bytes_ / secs / 1e9
@@ -292,17 +298,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.feat_dtype == "f32" else "bf16-features/f32",
+        "dtype": ("f32" if wl.feat_dtype == "f32" and args.out_dtype == "f32"
+                  else f"{wl.feat_dtype}-features/{args.out_dtype}-out/f32"),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: bs={wl.bs}, {wl.num_cams} cameras, scales "
                                + "/".join(f"{h}x{w_}" for h, w_ in wl.levels)
                                + f", C={wl.C}, groups={wl.groups}, anchors={wl.anchors}, "
                                  f"points={wl.pts}",
-                   "sample_channels_per_step": sc,
+                   "sample_channels_per_step": sc, "out_dtype": args.out_dtype,
                    "backward_form": "deterministic" if det else "default"},
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
-        "roofline": roof(b_bwd, bwd_s, BWD_KERNELS, "backward")
+        "roofline": roof(b_bwd, bwd_s, BWD_KERNELS + (" (prep_kernel also converts grad_out)"
+                                                      if args.out_dtype != "f32" else ""),
+                         "backward")
         if dominant == "backward" else roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
         "roofline_forward": roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
     }

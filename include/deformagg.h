@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DA_VERSION 110         /* 1.1.0 */
+#define DA_VERSION 120         /* 1.2.0 */
 #define DA_MAX_LEVELS 64       /* num_cams * num_scale */
 #define DA_MAX_EXTENT 32768    /* H and W of every level */
 
@@ -70,9 +70,14 @@ typedef enum {
     DA_ERR_HIP = 3             /* the HIP runtime refused a launch */
 } da_status;
 
+/* Element types of mc_ms_feat (feat_dtype) and of out / grad_out (out_dtype).
+ * 16-bit types are raw 16-bit patterns.  Arithmetic is binary32 throughout: a
+ * 16-bit feature converts exactly, and out is rounded once (to nearest, ties to
+ * even) from the binary32 sum; a 16-bit grad_out converts exactly. */
 typedef enum {
-    DA_F32 = 0,                /* mc_ms_feat holds float */
-    DA_BF16 = 1                /* mc_ms_feat holds bfloat16 (raw 16-bit patterns) */
+    DA_F32 = 0,                /* binary32 */
+    DA_BF16 = 1,               /* bfloat16 */
+    DA_F16 = 2                 /* IEEE binary16 */
 } da_dtype;
 
 /*
@@ -116,9 +121,11 @@ typedef struct {
     int64_t num_cams;     /* K                                             */
     int64_t num_scale;    /* S                                             */
     int64_t num_groups;   /* G, weight groups over the channels            */
-    int32_t feat_dtype;   /* da_dtype                                      */
+    int32_t feat_dtype;   /* da_dtype of mc_ms_feat                        */
     int32_t flags;        /* DA_FLAG_* bits (SLICES_ALWAYS / _NEVER exclusive, and so are
                              BWD_REGATHER / BWD_ROW_ORDER) */
+    int32_t out_dtype;    /* da_dtype of out (forward) and grad_out (backward) */
+    int32_t reserved;     /* must be 0                                     */
 } da_problem;
 
 /*
@@ -140,7 +147,7 @@ da_status da_forward_workspace_size(const da_problem* problem, size_t* bytes);
  *   scale_start_index  HOST int32 [K, S]: first row of each level; start + H*W <= num_feat.
  *   sampling_location  device float [bs, A, P, K, 2], normalised (x, y); 8-byte aligned.
  *   weights            device float [bs, A, P, K, S, G]; 4-byte aligned.
- *   out                device float [bs, A, C], fully overwritten; 4-byte aligned.
+ *   out                device [bs, A, C] of out_dtype, fully overwritten; element aligned.
  *   workspace          NULL, or device scratch of at least da_forward_workspace_size()
  *                      bytes, 256-byte aligned, owned by the caller (contents on entry do
  *                      not matter; garbage on return).  With NULL the forward always runs
@@ -161,7 +168,7 @@ da_status da_forward(const da_problem* problem,
                      const int32_t* scale_start_index,
                      const float* sampling_location,
                      const float* weights,
-                     float* out,
+                     void* out,
                      void* workspace,
                      size_t workspace_bytes,
                      void* stream);
@@ -171,7 +178,8 @@ da_status da_forward(const da_problem* problem,
  * da_backward_accumulate need for `problem` (0 when there is no sample): about
  * 8 * bs * num_feat + (88 + 16 * G) * bs*A*P*K*S where the row-ordered backward
  * may apply, else 8 * bs * num_feat + 88 * bs*A*P*K*S; with DA_FLAG_DETERMINISTIC
- * another (8 * C + 4) * (4 * bs*A*P*K*S / 65 + 1) + 8 * bs*K*S * ceil(A*P / 256).
+ * another (8 * C + 4) * (4 * bs*A*P*K*S / 65 + 1) + 8 * bs*K*S * ceil(A*P / 256);
+ * with a 16-bit out_dtype another 4 * bs*A*C (grad_out converted to binary32).
  * Only the sizes and flags in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
@@ -181,8 +189,8 @@ da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
 /*
  * da_backward -- the backward pass (section 4.1).  Same inputs as da_forward, plus
  *
- *   grad_out           device float [bs, A, C]; 4-byte aligned.
- *   grad_feat          device float [bs, num_feat, C] (binary32 also for bf16 features):
+ *   grad_out           device [bs, A, C] of out_dtype; element aligned.
+ *   grad_feat          device float [bs, num_feat, C] (binary32 also for 16-bit features):
  *                      fully overwritten (rows no sample touches are zero); 4-byte aligned.
  *   grad_loc           device float [bs, A, P, K, 2], fully overwritten; 8-byte aligned.
  *   grad_weights       device float [bs, A, P, K, S, G], fully overwritten.
@@ -207,7 +215,7 @@ da_status da_backward(const da_problem* problem,
                       const int32_t* scale_start_index,
                       const float* sampling_location,
                       const float* weights,
-                      const float* grad_out,
+                      const void* grad_out,
                       float* grad_feat,
                       float* grad_loc,
                       float* grad_weights,
@@ -227,7 +235,7 @@ da_status da_backward_accumulate(const da_problem* problem,
                                  const int32_t* scale_start_index,
                                  const float* sampling_location,
                                  const float* weights,
-                                 const float* grad_out,
+                                 const void* grad_out,
                                  float* grad_feat,
                                  float* grad_loc,
                                  float* grad_weights,
@@ -249,7 +257,7 @@ da_status da_backward_atomic(const da_problem* problem,
                              const int32_t* scale_start_index,
                              const float* sampling_location,
                              const float* weights,
-                             const float* grad_out,
+                             const void* grad_out,
                              float* grad_feat,
                              float* grad_loc,
                              float* grad_weights,

@@ -65,12 +65,14 @@ def _problem(feat, spatial_shape, scale_start_index, loc, weights):
     spatial_shape = np.ascontiguousarray(spatial_shape, dtype=np.int32)
     scale_start_index = np.ascontiguousarray(scale_start_index, dtype=np.int32)
     K, S = scale_start_index.shape
+    if feat.dtype == np.float16:
+        feat = feat.astype(np.float32)          # exact: every binary16 value is a binary32 value
     if feat.dtype == np.uint16:
         is_bf16 = 1
     elif feat.dtype == np.float32:
         is_bf16 = 0
     else:
-        raise TypeError("feat must be float32 or uint16 bf16 bit patterns")
+        raise TypeError("feat must be float32, float16 or uint16 bf16 bit patterns")
     feat = np.ascontiguousarray(feat)
     loc = np.ascontiguousarray(loc, dtype=np.float32)
     weights = np.ascontiguousarray(weights, dtype=np.float32)
@@ -105,6 +107,8 @@ def backward(feat, spatial_shape, scale_start_index, loc, weights, grad_out,
              need_feat: bool = True) -> Tuple[Optional[np.ndarray], np.ndarray, np.ndarray]:
     """(grad_feat [bs,num_feat,C] or None, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G])."""
     args, keep, d = _problem(feat, spatial_shape, scale_start_index, loc, weights)
+    if grad_out.dtype == np.uint16:
+        raise TypeError("pass a bfloat16 grad_out as its float32 values")
     grad_out = np.ascontiguousarray(grad_out, dtype=np.float32)
     if grad_out.shape != (d["bs"], d["A"], d["C"]):
         raise ValueError("grad_out shape")

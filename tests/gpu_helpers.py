@@ -5,6 +5,9 @@ Tolerances (per element, |gpu - ref| <= tol * (1 + |ref|)):
   forward, binary32 features        1e-4
   backward (atomic sums), binary32  1e-3
   bfloat16 features                 1e-2
+  binary16 features                 as binary32 (they convert exactly)
+  out stored in bfloat16 / binary16 the forward bound plus the rounding of one
+                                    result: 2^-8 / 2^-11 of |ref|
 """
 import sys
 
@@ -14,6 +17,8 @@ import torch
 TOL_FWD = 1e-4
 TOL_BWD = 1e-3
 TOL_BF16 = 1e-2
+TOL_OUT_BF16 = TOL_FWD + 2.0 ** -8
+TOL_OUT_F16 = TOL_FWD + 2.0 ** -11
 
 KEYS = ("feat", "spatial_shape", "scale_start_index", "loc", "weights")
 
@@ -38,11 +43,12 @@ def to_device(inp, device="cuda"):
     return d
 
 
-def gpu_forward(dev, slices=None, workspace=None):
+def gpu_forward(dev, slices=None, workspace=None, out_dtype=None):
     """slices: None = the library's choice, True / False = level slices forced on / off."""
     import view_deformable_feature_amd as vdf
     out = vdf.da_forward(dev["feat"], dev["spatial_shape"], dev["scale_start_index"],
-                         dev["loc"], dev["weights"], workspace=workspace, slices=slices)
+                         dev["loc"], dev["weights"], workspace=workspace, slices=slices,
+                         out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.da_version() == 110
+    assert lib.da_version() == 120
     for code in range(4):
         assert lib.da_status_string(code)
     assert b"unknown" in lib.da_status_string(99)
@@ -44,7 +44,7 @@ HOST_START = np.array([[0]], np.int32)
 
 def _prob(**kw):
     d = dict(bs=1, num_feat=256, num_embeds=32, num_anchors=8, num_pts=4, num_cams=1,
-             num_scale=1, num_groups=1, feat_dtype=0, flags=0)
+             num_scale=1, num_groups=1, feat_dtype=0, flags=0, out_dtype=0, reserved=0)
     d.update(kw)
     return _lib.DAProblem(**d)
 
@@ -86,6 +86,9 @@ def _msg(lib):
     (dict(num_anchors=-2), 1, ">= 0"),
     (dict(num_pts=-1), 1, ">= 0"),
     (dict(feat_dtype=7), 1, "feat_dtype"),
+    (dict(feat_dtype=-1), 1, "feat_dtype"),
+    (dict(out_dtype=3), 1, "out_dtype"),
+    (dict(reserved=1), 1, "reserved"),
     (dict(flags=3), 1, "flags"),
     (dict(flags=7), 1, "flags"),
     (dict(flags=12), 1, "flags"),
@@ -146,9 +149,12 @@ def test_rejects_misaligned_pointers(lib):
     assert _fwd(lib, p, out=FAKE + 2) == 1
     assert _bwd(lib, p, gl=FAKE + 4) == 1 and "grad_loc" in _msg(lib)
     assert _bwd(lib, p, gf=FAKE + 1) == 1
-    # bf16 features need 2-byte alignment only
-    pb = _prob(feat_dtype=1)
-    assert _fwd(lib, pb, feat=FAKE + 1) == 1
+    # 16-bit features, out and grad_out need 2-byte alignment only
+    for dt in (1, 2):
+        assert _fwd(lib, _prob(feat_dtype=dt), feat=FAKE + 1) == 1
+        assert _fwd(lib, _prob(out_dtype=dt), out=FAKE + 1) == 1 and "out" in _msg(lib)
+        assert _bwd(lib, _prob(out_dtype=dt), go=FAKE + 1) == 1 and "grad_out" in _msg(lib)
+        assert _bwd(lib, _prob(out_dtype=dt), "da_backward_atomic", go=FAKE + 1) == 1
 
 
 def test_rejects_unsupported_sizes(lib):
@@ -216,6 +222,14 @@ def test_workspace_size_and_checks(lib):
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(flags=16)), ctypes.byref(n)) == 0
     assert n.value == expect + -(-(2 * (32 * 8 + 4) + 8) // 256) * 256
     assert _bwd(lib, _prob(flags=16), "da_backward_atomic") == 2 and "deterministic" in _msg(lib)
+    # a 16-bit grad_out: + its binary32 copy, bs * A * C * 4 bytes
+    for dt in (1, 2):
+        assert lib.da_backward_workspace_size(ctypes.byref(_prob(out_dtype=dt)),
+                                              ctypes.byref(n)) == 0
+        assert n.value == expect + 8 * 32 * 4
+        assert _bwd(lib, _prob(out_dtype=dt), ws_bytes=expect + 8 * 32 * 4 - 1) == 1
+        assert "needed" in _msg(lib)
+    assert lib.da_backward_workspace_size(ctypes.byref(_prob(out_dtype=9)), ctypes.byref(n)) == 1
     assert lib.da_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value == expect
     assert lib.da_backward_workspace_size(ctypes.byref(_prob(num_pts=0)), ctypes.byref(n)) == 0

@@ -386,6 +386,27 @@ def test_bf16_features_read_exactly():
     assert np.array_equal(oracle.forward(*_args(inp)), oracle.forward(*_args(as_f32)))
 
 
+def test_f16_features_read_exactly():
+    # IEEE binary16 patterns and their values (sign, 5-bit exponent biased by 15,
+    # 10-bit fraction; subnormals below 2^-14)
+    golden = {0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14,
+              0x0001: 2.0 ** -24, 0x3555: 1365.0 / 4096.0, 0x8000: -0.0}
+    bits = np.array(list(golden), np.uint16)
+    assert np.array_equal(bits.view(np.float16).astype(np.float64), list(golden.values()))
+    wl = W.custom("th", bs=1, num_cams=1, levels=((16, 16),), C=32, groups=4, anchors=8,
+                  pts=4, feat_dtype="f16", loc_lo=-0.1, loc_hi=1.1, seed=32)
+    inp = W.make_inputs(wl)
+    assert inp["feat"].dtype == np.float16
+    as_f32 = dict(inp)
+    as_f32["feat"] = inp["feat"].astype(np.float32)
+    assert np.array_equal(oracle.forward(*_args(inp)), oracle.forward(*_args(as_f32)))
+    gf16 = oracle.backward(*_args(inp), inp["grad_out"])
+    gf32 = oracle.backward(*_args(as_f32), inp["grad_out"])
+    assert all(np.array_equal(a, b) for a, b in zip(gf16, gf32))
+    with pytest.raises(TypeError):      # bfloat16 grad_out must arrive as its values
+        oracle.backward(*_args(inp), W.bf16_bits_from_f32(inp["grad_out"]))
+
+
 def test_rejects_malformed_problem():
     wl = W.WORKLOADS["tiny"]
     inp = W.make_inputs(wl)

@@ -30,6 +30,8 @@ def _maps_np(name, B, N, C, hw, dtype):
     rng = np.random.default_rng(zlib.crc32(name.encode()) % 1000)
     if dtype == "f32":
         return [rng.standard_normal((B, N, C, h, w)).astype(np.float32) for h, w in hw]
+    if dtype == "f16":
+        return [rng.standard_normal((B, N, C, h, w)).astype(np.float16) for h, w in hw]
     return [W.bf16_bits_from_f32(rng.standard_normal((B, N, C, h, w)).astype(np.float32))
             for h, w in hw]
 
@@ -42,15 +44,17 @@ def _to_dev(a):
 
 def _bits(t):
     t = t.detach().cpu()
-    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).numpy()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy()
+    return t.view(torch.int32).numpy()
 
 
 def _obits(a):
-    return a.view(np.int16) if a.dtype == np.uint16 else a.view(np.int32)
+    return a.view(np.int16) if a.dtype in (np.uint16, np.float16) else a.view(np.int32)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_pack_and_unpack_bit_exact(case, dtype):
     import view_deformable_feature_amd as vdf
     name, B, N, C, hw = case

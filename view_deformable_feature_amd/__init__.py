@@ -11,4 +11,4 @@ from .api import (DeformableAggregationFunction, da_backward, da_backward_accumu
 from .pack import (PackLevelsFunction, da_pack_levels, da_unpack_levels,  # noqa: F401
                    feature_maps_format, pack_layout, pack_levels)
 
-__version__ = "1.1.0"
+__version__ = "1.2.0"

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "deformagg.h")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
-DA_F32, DA_BF16 = 0, 1
+DA_F32, DA_BF16, DA_F16 = 0, 1, 2
 DA_FLAG_SLICES_ALWAYS, DA_FLAG_SLICES_NEVER, DA_FLAG_BWD_REGATHER, DA_FLAG_BWD_ROW_ORDER = \
     1, 2, 4, 8
 DA_FLAG_DETERMINISTIC = 16
@@ -33,6 +33,8 @@ class DAProblem(ctypes.Structure):
         ("num_groups", ctypes.c_int64),
         ("feat_dtype", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

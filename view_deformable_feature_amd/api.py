@@ -27,6 +27,10 @@ __all__ = ["da_forward", "da_backward", "da_backward_accumulate", "da_backward_a
 
 IntTable = Union[torch.Tensor, np.ndarray, Sequence]
 
+# torch dtype -> da_dtype, for mc_ms_feat and for out / grad_out
+_DTYPES = {torch.float32: _lib.DA_F32, torch.bfloat16: _lib.DA_BF16, torch.float16: _lib.DA_F16}
+_FLOATS = tuple(_DTYPES)
+
 
 def _host_i32(x: IntTable) -> np.ndarray:
     """Level tables are read on the host; a device tensor is copied (synchronising)."""
@@ -73,7 +77,8 @@ def _flags(slices: Optional[bool], regather: Optional[bool] = None,
 def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
                sampling_location: torch.Tensor, weights: torch.Tensor,
                slices: Optional[bool] = None, regather: Optional[bool] = None,
-               deterministic: bool = False) -> _lib.DAProblem:
+               deterministic: bool = False,
+               out_dtype: torch.dtype = torch.float32) -> _lib.DAProblem:
     if mc_ms_feat.dim() != 3:
         raise ValueError("mc_ms_feat must be [bs, num_feat, C]")
     if sampling_location.dim() != 5 or sampling_location.shape[-1] != 2:
@@ -87,21 +92,22 @@ def problem_of(mc_ms_feat: torch.Tensor, spatial_shape: np.ndarray,
     S, G = weights.shape[4], weights.shape[5]
     if spatial_shape.shape[:2] != (K, S):
         raise ValueError(f"spatial_shape is {spatial_shape.shape}, expected ({K}, {S}, 2)")
-    dt = _lib.DA_BF16 if mc_ms_feat.dtype == torch.bfloat16 else _lib.DA_F32
-    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, dt,
-                          _flags(slices, regather, deterministic))
+    if mc_ms_feat.dtype not in _DTYPES or out_dtype not in _DTYPES:
+        raise TypeError(f"feature / output dtypes must be among {_FLOATS}")
+    return _lib.DAProblem(bs, num_feat, C, A, P, K, S, G, _DTYPES[mc_ms_feat.dtype],
+                          _flags(slices, regather, deterministic), _DTYPES[out_dtype], 0)
 
 
 def _prepare(mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
-             slices=None, regather=None, deterministic=False):
+             slices=None, regather=None, deterministic=False, out_dtype=torch.float32):
     shape = _host_i32(spatial_shape)
     start = _host_i32(scale_start_index)
     dev = mc_ms_feat.device
-    _need(mc_ms_feat, "mc_ms_feat", (torch.float32, torch.bfloat16), dev)
+    _need(mc_ms_feat, "mc_ms_feat", _FLOATS, dev)
     _need(sampling_location, "sampling_location", torch.float32, dev)
     _need(weights, "weights", torch.float32, dev)
     prob = problem_of(mc_ms_feat, shape, sampling_location, weights, slices, regather,
-                      deterministic)
+                      deterministic, out_dtype)
     bs, A, P, K = (sampling_location.shape[i] for i in range(4))
     if tuple(weights.shape[:4]) != (bs, A, P, K) or mc_ms_feat.shape[0] != bs:
         raise ValueError("batch / anchor / point / camera sizes disagree between inputs")
@@ -135,19 +141,25 @@ def _workspace(lib, size_fn: str, prob, dev, workspace):
 def da_forward(mc_ms_feat: torch.Tensor, spatial_shape: IntTable, scale_start_index: IntTable,
                sampling_location: torch.Tensor, weights: torch.Tensor,
                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-               slices: Optional[bool] = None) -> torch.Tensor:
-    """out[bs, A, C] (float32) on the current stream of mc_ms_feat's device.
+               slices: Optional[bool] = None,
+               out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """out[bs, A, C] on the current stream of mc_ms_feat's device.
+
+    The type of out is that of a given ``out`` tensor, else ``out_dtype`` (float32 by
+    default; bfloat16 / float16 round the binary32 sums once, to nearest even).
 
     slices=None lets the library choose level slices (given a workspace, allocated
     here when not passed), True forces them, False runs one workgroup per anchor."""
     lib = _lib.load()
+    if out is not None and out_dtype is not None and out.dtype != out_dtype:
+        raise TypeError(f"out has dtype {out.dtype}, out_dtype is {out_dtype}")
+    odt = out.dtype if out is not None else (out_dtype or torch.float32)
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
-                                  sampling_location, weights, slices)
+                                  sampling_location, weights, slices, out_dtype=odt)
     dev = mc_ms_feat.device
     if out is None:
-        out = torch.empty((prob.bs, prob.num_anchors, prob.num_embeds), device=dev,
-                          dtype=torch.float32)
-    _need(out, "out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
+        out = torch.empty((prob.bs, prob.num_anchors, prob.num_embeds), device=dev, dtype=odt)
+    _need(out, "out", _FLOATS, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
     workspace = _workspace(lib, "da_forward_workspace_size", prob, dev, workspace)
     with torch.cuda.device(dev):
         st = lib.da_forward(ctypes.byref(prob), _ptr(mc_ms_feat), _i32p(shape), _i32p(start),
@@ -169,11 +181,13 @@ def forward_workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights
 
 
 def workspace_size(mc_ms_feat, spatial_shape, sampling_location, weights,
-                   regather: Optional[bool] = None, deterministic: bool = False) -> int:
-    """Bytes of workspace da_backward / da_backward_accumulate need for these shapes."""
+                   regather: Optional[bool] = None, deterministic: bool = False,
+                   grad_out_dtype: torch.dtype = torch.float32) -> int:
+    """Bytes of workspace da_backward / da_backward_accumulate need for these shapes
+    (and a grad_out of grad_out_dtype)."""
     lib = _lib.load()
     prob = problem_of(mc_ms_feat, _host_i32(spatial_shape), sampling_location, weights,
-                      regather=regather, deterministic=deterministic)
+                      regather=regather, deterministic=deterministic, out_dtype=grad_out_dtype)
     n = ctypes.c_size_t(0)
     _lib.check(lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
                "da_backward_workspace_size")
@@ -184,10 +198,13 @@ def _backward(func: str, mc_ms_feat, spatial_shape, scale_start_index, sampling_
               weights, grad_out, grad_feat=None, grad_loc=None, grad_weights=None,
               workspace=None, slices=None, regather=None, deterministic=False):
     lib = _lib.load()
+    if not isinstance(grad_out, torch.Tensor) or grad_out.dtype not in _DTYPES:
+        raise TypeError(f"grad_out must be a tensor of one of {_FLOATS}")
     prob, shape, start = _prepare(mc_ms_feat, spatial_shape, scale_start_index,
-                                  sampling_location, weights, slices, regather, deterministic)
+                                  sampling_location, weights, slices, regather, deterministic,
+                                  grad_out.dtype)
     dev = mc_ms_feat.device
-    _need(grad_out, "grad_out", torch.float32, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
+    _need(grad_out, "grad_out", _FLOATS, dev, (prob.bs, prob.num_anchors, prob.num_embeds))
     if grad_feat is None:
         if func == "da_backward_accumulate":
             raise ValueError("da_backward_accumulate needs an existing grad_feat")
@@ -219,6 +236,8 @@ def da_backward(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(grad_feat [bs,num_feat,C] f32, grad_loc [bs,A,P,K,2], grad_weights [bs,A,P,K,S,G]).
 
+    grad_out may be float32, bfloat16 or float16 (the type the forward wrote out in).
+
     deterministic=True: grad_feat bit for bit independent of run, backward form and
     level slices (64-bit fixed-point sums; needs finite grad_out and weights)."""
     return _backward("da_backward", mc_ms_feat, spatial_shape, scale_start_index,
@@ -245,18 +264,21 @@ def da_backward_atomic(mc_ms_feat, spatial_shape, scale_start_index, sampling_lo
 class DeformableAggregationFunction(torch.autograd.Function):
     """Autograd wrapper: gradients for mc_ms_feat, sampling_location and weights.
 
-    The feature gradient is float32 (for bf16 features it is cast back to bf16
-    for autograd; use ``da_backward`` directly to keep the float32 values).
+    The feature gradient is float32 (for 16-bit features it is cast back to the
+    feature type for autograd; use ``da_backward`` directly to keep the float32
+    values).  ``out_dtype`` (after the page's five arguments) picks the output type.
     """
 
     @staticmethod
-    def forward(ctx, mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights):
+    def forward(ctx, mc_ms_feat, spatial_shape, scale_start_index, sampling_location, weights,
+                out_dtype=None):
         shape = _host_i32(spatial_shape)
         start = _host_i32(scale_start_index)
         mc_ms_feat = mc_ms_feat.contiguous()
         sampling_location = sampling_location.contiguous().float()
         weights = weights.contiguous().float()
-        out = da_forward(mc_ms_feat, shape, start, sampling_location, weights)
+        out = da_forward(mc_ms_feat, shape, start, sampling_location, weights,
+                         out_dtype=out_dtype)
         ctx.save_for_backward(mc_ms_feat, sampling_location, weights)
         ctx.tables = (shape, start)
         return out
@@ -265,14 +287,16 @@ class DeformableAggregationFunction(torch.autograd.Function):
     def backward(ctx, grad_out):
         mc_ms_feat, sampling_location, weights = ctx.saved_tensors
         shape, start = ctx.tables
+        if grad_out.dtype not in _DTYPES:
+            grad_out = grad_out.float()
         gf, gl, gw = da_backward(mc_ms_feat, shape, start, sampling_location, weights,
-                                 grad_out.contiguous().float())
+                                 grad_out.contiguous())
         if mc_ms_feat.dtype != torch.float32:
             gf = gf.to(mc_ms_feat.dtype)
-        return gf, None, None, gl, gw
+        return gf, None, None, gl, gw, None
 
 
 def deformable_aggregation(mc_ms_feat, spatial_shape, scale_start_index, sampling_location,
-                           weights):
+                           weights, out_dtype=None):
     return DeformableAggregationFunction.apply(mc_ms_feat, spatial_shape, scale_start_index,
-                                               sampling_location, weights)
+                                               sampling_location, weights, out_dtype)

@@ -39,11 +39,16 @@ int ilog2(int64_t x) {
 
 constexpr uint64_t kU32Max = 0xffffffffull;
 
+static_assert(da::kF32 == DA_F32 && da::kBF16 == DA_BF16 && da::kF16 == DA_F16, "da_dtype values");
+bool valid_dtype(int32_t t) { return t == DA_F32 || t == DA_BF16 || t == DA_F16; }
+int elem_bytes(int32_t t) { return t == DA_F32 ? 4 : 2; }
+
 struct Plan {
     da::KArgs ka;
     da::LaunchShape shape;
     int64_t n_anchors;   // bs * A
-    bool bf16;
+    int feat_dtype;
+    int elem;            // bytes per feature element
 };
 
 // Checks shared by both directions: problem sizes, the level table, the input
@@ -71,9 +76,11 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
     if (p->num_embeds % p->num_groups != 0)
         return fail(DA_ERR_INVALID_ARG, "num_embeds (%lld) is not a multiple of num_groups (%lld)",
                     (long long)p->num_embeds, (long long)p->num_groups);
-    if (p->feat_dtype != DA_F32 && p->feat_dtype != DA_BF16)
-        return fail(DA_ERR_INVALID_ARG, "feat_dtype %d is neither DA_F32 nor DA_BF16",
-                    (int)p->feat_dtype);
+    if (!valid_dtype(p->feat_dtype))
+        return fail(DA_ERR_INVALID_ARG, "feat_dtype %d is not a da_dtype", (int)p->feat_dtype);
+    if (!valid_dtype(p->out_dtype))
+        return fail(DA_ERR_INVALID_ARG, "out_dtype %d is not a da_dtype", (int)p->out_dtype);
+    if (p->reserved != 0) return fail(DA_ERR_INVALID_ARG, "problem.reserved must be 0");
     if (!shape || !start) return fail(DA_ERR_INVALID_ARG, "spatial_shape / scale_start_index is NULL");
     // sizes that must fit the kernels' 32-bit index arithmetic
     if (p->num_embeds > (1 << 20)) return fail(DA_ERR_UNSUPPORTED, "num_embeds > 2^20");
@@ -81,7 +88,7 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
         p->num_pts * p->num_cams > INT32_MAX / 64)
         return fail(DA_ERR_UNSUPPORTED, "num_anchors or num_pts * num_cams too large");
 
-    const int elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    const int elem = elem_bytes(p->feat_dtype);
     const int64_t C = p->num_embeds;
     const int64_t nlev = p->num_cams * p->num_scale;
     da::KArgs& ka = plan.ka;
@@ -134,8 +141,11 @@ da_status check_common(const da_problem* p, const void* feat, const int32_t* sha
     ka.feat_image_bytes = (uint32_t)feat_img;
     ka.row_bytes = (int32_t)(C * elem);
     ka.grow_bytes = (int32_t)(C * 4);
+    ka.out_dtype = p->out_dtype;
+    ka.go_dtype = p->out_dtype;
     plan.n_anchors = n_anchor;
-    plan.bf16 = p->feat_dtype == DA_BF16;
+    plan.feat_dtype = p->feat_dtype;
+    plan.elem = elem;
     return DA_OK;
 }
 
@@ -250,8 +260,8 @@ void plan_backward_sliced(const da_problem* p, Plan& plan) {
 da_status plan_forward(const da_problem* p, Plan& plan) {
     da::KArgs& ka = plan.ka;
     const int64_t C = ka.C, D = ka.D;
-    const int elem = plan.bf16 ? 2 : 4;
-    const int vwide = plan.bf16 ? 8 : 4;   // 16-byte vectors
+    const int elem = plan.elem;
+    const int vwide = 16 / elem;           // 16-byte vectors
     const int vec = (C % vwide == 0 && D % vwide == 0 && aligned(ka.feat, 16)) ? vwide : 1;
     const int64_t nvec = C / vec;                       // vectors per row
     const int64_t L = std::min<int64_t>(da::kWave, pow2_factor(nvec));
@@ -305,7 +315,7 @@ da_status plan_backward(const da_problem* p, Plan& plan, bool gather) {
     // the gather form only reads features: 16-byte vectors per lane when the
     // rows and groups allow; the scatter form keeps one channel per lane so that
     // each atomic instruction covers consecutive floats
-    const int64_t vw = plan.bf16 ? 8 : 4;
+    const int64_t vw = 16 / plan.elem;
     int64_t L = 0, seg = 0, nv = 0, vec = 1;
     if (gather && C % vw == 0 && D % vw == 0 && aligned(ka.feat, 16) &&
         bwd_layout(C, D, vw, 8, L, seg, nv)) {
@@ -380,7 +390,8 @@ bool rows_reused(const da_problem* p, const da::KArgs& ka) {
 
 // Workspace of the gather form of the backward, each part 256-byte aligned.
 struct WsLayout {
-    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, dots, slots, total;
+    size_t scan_done, cnt, local_start, tile_prefix, rank, entries, loc_part, dots, slots, go32,
+        total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -392,12 +403,17 @@ uint64_t count_blocks(const da_problem* p) {
     return (uint64_t)((p->num_anchors * p->num_pts + 255) / 256) * p->num_cams * p->num_scale *
            p->bs;
 }
+// grad_out as binary32, when it arrives in a 16-bit type
+uint64_t go32_bytes(const da_problem* p) {
+    return p->out_dtype == DA_F32 ? 0 : (uint64_t)p->bs * p->num_anchors * p->num_embeds * 4;
+}
 // the accumulation rows, the list of long rows, then the count blocks' maxima
 uint64_t det_bytes(const da_problem* p, uint64_t n_samples) {
     return det_slots(n_samples) * ((uint64_t)p->num_embeds * 8 + 4) + 8 * count_blocks(p);
 }
 
-WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uint64_t slot_bytes) {
+WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uint64_t slot_bytes,
+                   uint64_t go32_bytes) {
     WsLayout w;
     const uint64_t n_tiles = (n_rows + da::kScanTile - 1) / da::kScanTile;
     size_t off = 0;
@@ -419,6 +435,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uin
     off += align256(n_samples * 4 * dot_groups * 4);
     w.slots = off;
     off += align256(slot_bytes);
+    w.go32 = off;
+    off += align256(go32_bytes);
     w.total = off;
     return w;
 }
@@ -447,7 +465,7 @@ enum class BwdMode { kGather, kGatherAccumulate, kScatter };
 
 da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                         const int32_t* shape, const int32_t* start, const float* loc,
-                        const float* weights, const float* grad_out, float* grad_feat,
+                        const float* weights, const void* grad_out, float* grad_feat,
                         float* grad_loc, float* grad_weights, void* workspace,
                         size_t workspace_bytes, void* stream) {
     Plan plan;
@@ -458,8 +476,10 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
     if (plan.n_anchors > 0 && !grad_out) return fail(DA_ERR_INVALID_ARG, "grad_out is NULL");
     if (any_sample && (!grad_loc || !grad_weights))
         return fail(DA_ERR_INVALID_ARG, "grad_loc / grad_weights is NULL");
-    if (!aligned(grad_out, 4) || !aligned(grad_feat, 4) || !aligned(grad_weights, 4))
-        return fail(DA_ERR_INVALID_ARG, "grad_out / grad_feat / grad_weights not 4-byte aligned");
+    if (!aligned(grad_out, elem_bytes(p->out_dtype)))
+        return fail(DA_ERR_INVALID_ARG, "grad_out is not element aligned");
+    if (!aligned(grad_feat, 4) || !aligned(grad_weights, 4))
+        return fail(DA_ERR_INVALID_ARG, "grad_feat / grad_weights not 4-byte aligned");
     if (!aligned(grad_loc, 8)) return fail(DA_ERR_INVALID_ARG, "grad_loc is not 8-byte aligned");
     if (mode == BwdMode::kScatter && (p->flags & DA_FLAG_DETERMINISTIC))
         return fail(DA_ERR_UNSUPPORTED,
@@ -481,7 +501,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             const bool fusable = fused_capable(p);
             const bool det = p->flags & DA_FLAG_DETERMINISTIC;
             const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0,
-                                         det ? det_bytes(p, n_samples) : 0);
+                                         det ? det_bytes(p, n_samples) : 0, go32_bytes(p));
             if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
             if (!aligned(workspace, 256))
                 return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -502,6 +522,12 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.long_rows = reinterpret_cast<uint32_t*>(ka.slots + (size_t)ka.n_slots * p->num_embeds);
             ka.bound_part = ka.long_rows + ka.n_slots;
             ka.count_blocks = (uint32_t)count_blocks(p);
+            if (p->out_dtype != DA_F32) {   // the gather reads binary32 grad_out rows
+                ka.go_src = grad_out;
+                ka.go_src_dtype = p->out_dtype;
+                ka.grad_out = base + w.go32;
+                ka.go_dtype = DA_F32;
+            }
             ka.n_rows = (uint32_t)n_rows;
             ka.n_samples = (uint32_t)n_samples;
             ka.n_anchors = (uint32_t)plan.n_anchors;
@@ -513,7 +539,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                 ka.fused = 1;
                 ka.dots = reinterpret_cast<float*>(base + w.dots);
                 ka.feat_all_bytes =
-                    (uint32_t)((uint64_t)p->bs * p->num_feat * p->num_embeds * (plan.bf16 ? 2 : 4));
+                    (uint32_t)((uint64_t)p->bs * p->num_feat * p->num_embeds * plan.elem);
                 ka.w_vec4 = p->num_groups % 4 == 0 && aligned(weights, 16) &&
                             aligned(grad_weights, 16);
             } else {
@@ -531,9 +557,9 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
     }
     if (!any_sample) return DA_OK;
     if (mode == BwdMode::kScatter)
-        return hip_status(da::launch_backward_scatter(ka, plan.shape, plan.n_anchors, plan.bf16, s),
+        return hip_status(da::launch_backward_scatter(ka, plan.shape, plan.n_anchors, plan.feat_dtype, s),
                           "backward kernel launch");
-    return hip_status(da::launch_backward_gather(ka, plan.shape, plan.n_anchors, plan.bf16, s),
+    return hip_status(da::launch_backward_gather(ka, plan.shape, plan.n_anchors, plan.feat_dtype, s),
                       "backward kernel launch");
 }
 
@@ -548,14 +574,13 @@ da_status pack_plan(const da_pack_problem* p, const int32_t* scale_hw, da::PackA
     if (p->num_cams * p->num_scale > DA_MAX_LEVELS)
         return fail(DA_ERR_INVALID_ARG, "num_cams * num_scale = %lld exceeds DA_MAX_LEVELS (%d)",
                     (long long)(p->num_cams * p->num_scale), DA_MAX_LEVELS);
-    if (p->dtype != DA_F32 && p->dtype != DA_BF16)
-        return fail(DA_ERR_INVALID_ARG, "dtype %d is neither DA_F32 nor DA_BF16", (int)p->dtype);
+    if (!valid_dtype(p->dtype)) return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", (int)p->dtype);
     if (!scale_hw) return fail(DA_ERR_INVALID_ARG, "scale_hw is NULL");
     if (p->bs * p->num_cams > 65535)
         return fail(DA_ERR_UNSUPPORTED, "bs * num_cams = %lld exceeds 65535",
                     (long long)(p->bs * p->num_cams));
     memset(&pa, 0, sizeof pa);
-    elem = p->dtype == DA_BF16 ? 2 : 4;
+    elem = elem_bytes(p->dtype);
     const int64_t C = p->num_embeds;
     const int64_t c_tiles = (C + 63) / 64;
     int64_t rows = 0, tiles = 0;
@@ -669,13 +694,14 @@ da_status da_forward_workspace_size(const da_problem* p, size_t* bytes) {
 }
 
 da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape,
-                     const int32_t* start, const float* loc, const float* weights, float* out,
+                     const int32_t* start, const float* loc, const float* weights, void* out,
                      void* workspace, size_t workspace_bytes, void* stream) {
     Plan plan;
     da_status st = check_common(p, feat, shape, start, loc, weights, plan);
     if (st != DA_OK) return st;
     if (plan.n_anchors > 0 && !out) return fail(DA_ERR_INVALID_ARG, "out is NULL");
-    if (!aligned(out, 4)) return fail(DA_ERR_INVALID_ARG, "out is not 4-byte aligned");
+    if (!aligned(out, elem_bytes(p->out_dtype)))
+        return fail(DA_ERR_INVALID_ARG, "out is not element aligned");
     st = plan_forward(p, plan);
     if (st != DA_OK) return st;
     if (workspace) {
@@ -695,11 +721,11 @@ da_status da_forward(const da_problem* p, const void* feat, const int32_t* shape
         if (plan.ka.sliced) {
             plan.ka.fwd_part = static_cast<float*>(workspace);
             return hip_status(da::launch_forward_sliced(plan.ka, plan.shape, plan.n_anchors,
-                                                        plan.bf16, s),
+                                                        plan.feat_dtype, s),
                               "forward kernel launch");
         }
     }
-    return hip_status(da::launch_forward(plan.ka, plan.shape, plan.n_anchors, plan.bf16, s),
+    return hip_status(da::launch_forward(plan.ka, plan.shape, plan.n_anchors, plan.feat_dtype, s),
                       "forward kernel launch");
 }
 
@@ -709,6 +735,8 @@ da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
     if (p->bs < 0 || p->num_anchors < 0 || p->num_pts < 0 || p->num_feat < 1 ||
         p->num_cams < 1 || p->num_scale < 1)
         return fail(DA_ERR_INVALID_ARG, "malformed problem sizes");
+    if (!valid_dtype(p->out_dtype))
+        return fail(DA_ERR_INVALID_ARG, "out_dtype %d is not a da_dtype", (int)p->out_dtype);
     uint64_t n_rows = 0, n_samples = 0;
     const da_status st = gather_sizes(p, n_rows, n_samples);
     if (st != DA_OK) return st;
@@ -716,13 +744,14 @@ da_status da_backward_workspace_size(const da_problem* p, size_t* bytes) {
     *bytes = n_samples == 0
                  ? 0
                  : ws_layout(n_rows, n_samples, fused_capable(p) ? (uint64_t)p->num_groups : 0,
-                             det ? det_bytes(p, n_samples) : 0).total;
+                             det ? det_bytes(p, n_samples) : 0, go32_bytes(p))
+                       .total;
     return DA_OK;
 }
 
 da_status da_backward(const da_problem* p, const void* feat, const int32_t* shape,
                       const int32_t* start, const float* loc, const float* weights,
-                      const float* grad_out, float* grad_feat, float* grad_loc,
+                      const void* grad_out, float* grad_feat, float* grad_loc,
                       float* grad_weights, void* workspace, size_t workspace_bytes, void* stream) {
     return backward_impl(BwdMode::kGather, p, feat, shape, start, loc, weights, grad_out,
                          grad_feat, grad_loc, grad_weights, workspace, workspace_bytes, stream);
@@ -730,7 +759,7 @@ da_status da_backward(const da_problem* p, const void* feat, const int32_t* shap
 
 da_status da_backward_accumulate(const da_problem* p, const void* feat, const int32_t* shape,
                                  const int32_t* start, const float* loc, const float* weights,
-                                 const float* grad_out, float* grad_feat, float* grad_loc,
+                                 const void* grad_out, float* grad_feat, float* grad_loc,
                                  float* grad_weights, void* workspace, size_t workspace_bytes,
                                  void* stream) {
     return backward_impl(BwdMode::kGatherAccumulate, p, feat, shape, start, loc, weights,
@@ -740,7 +769,7 @@ da_status da_backward_accumulate(const da_problem* p, const void* feat, const in
 
 da_status da_backward_atomic(const da_problem* p, const void* feat, const int32_t* shape,
                              const int32_t* start, const float* loc, const float* weights,
-                             const float* grad_out, float* grad_feat, float* grad_loc,
+                             const void* grad_out, float* grad_feat, float* grad_loc,
                              float* grad_weights, void* stream) {
     return backward_impl(BwdMode::kScatter, p, feat, shape, start, loc, weights, grad_out,
                          grad_feat, grad_loc, grad_weights, nullptr, 0, stream);

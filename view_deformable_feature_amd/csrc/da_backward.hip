@@ -291,7 +291,7 @@ da_backward_anchor_kernel(KArgs a) {
         soff[i] = (uint32_t)(L * i * VEC * kElem);
         gi[i] = c0 / a.D;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) go[i][e] = a.grad_out[ba * a.C + c0 + e];
+        for (int e = 0; e < VEC; ++e) go[i][e] = load_elem(a.grad_out, ba * a.C + c0 + e, a.go_dtype);
     }
 
     if (x.tid == 0) desc[ns_max] = null_bwd_desc(a.feat_image_bytes, a.gfeat_image_bytes);
@@ -423,7 +423,7 @@ da_backward_sliced_kernel(KArgs a) {
         soff[i] = (uint32_t)(L * i * VEC * kElem);
         gi[i] = c0 / a.D;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) go[i][e] = a.grad_out[ba * a.C + c0 + e];
+        for (int e = 0; e < VEC; ++e) go[i][e] = load_elem(a.grad_out, ba * a.C + c0 + e, a.go_dtype);
     }
 
     if (tid == 0) desc[ns_max] = null_bwd_desc(a.feat_image_bytes, a.gfeat_image_bytes);
@@ -720,7 +720,7 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
         const uint32_t nb = gridDim.x * gridDim.y * gridDim.z;
         uint32_t mw = 0;
         if (valid) mw = abs_max_bits(a.weights + (size_t)q * a.G, a.G, 0, 1);
-        uint32_t mg = abs_max_bits(a.grad_out, (int64_t)a.n_anchors * a.C,
+        uint32_t mg = abs_max_bits(static_cast<const float*>(a.grad_out), (int64_t)a.n_anchors * a.C,
                                    (int64_t)fb * kCountThreads + threadIdx.x,
                                    (int64_t)nb * kCountThreads);
         for (int m = 1; m < kWave; m <<= 1) {
@@ -943,7 +943,7 @@ __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
 // vector per lane, measured faster despite a few spilled registers) keeps more
 // waves in flight.
 template <typename T, int VEC, int NV, bool FUSED, bool DET>
-__global__ void __launch_bounds__(256, NV == 1 ? (DET ? 4 : 5) : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
+__global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5) : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
         return;
@@ -1107,7 +1107,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET ? 4 : 5) : (NV == 2 ? 4 : 
         float cw[U];
         float go[U][NV][VEC];
         float wt[U][NV];
-        float f[U][NV][VEC];   // FUSED: the entry's feature row, where it starts a new row
+        RawVec<T, VEC> f[U][NV];   // FUSED: the entry's feature row, where it starts a new row
         bool fnew[U];          // FUSED: the entry's row differs from the previous entry's
         uint32_t dof[U];       // FUSED: float index of the entry's dot products
     };
@@ -1139,7 +1139,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET ? 4 : 5) : (NV == 2 ? 4 : 
                 if (B.fnew[u]) {
                     const uint32_t rb = (B.row[u] & ~kEntryLongRow) * (uint32_t)a.row_bytes;
 #pragma unroll
-                    for (int i = 0; i < NV; ++i) VecLoad<T, VEC>::run(r_f, lo_f[i], rb, B.f[u][i]);
+                    for (int i = 0; i < NV; ++i) B.f[u][i].load(r_f, lo_f[i], rb);
                 }
                 // (4 q + corner) * G with wo = 4 q G
                 B.dof[u] = wo + (gow & 3u) * (uint32_t)G;
@@ -1162,9 +1162,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET ? 4 : 5) : (NV == 2 ? 4 : 
         if constexpr (FUSED) {
             if (B.fnew[u]) {
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) fcur[i][k] = B.f[u][i][k];
+                for (int i = 0; i < NV; ++i) B.f[u][i].to_float(fcur[i]);
             }
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
@@ -1367,18 +1365,40 @@ hipError_t launch_fill_zero(void* p, int64_t n_words, hipStream_t stream) {
 }
 
 hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                   bool bf16, hipStream_t stream) {
+                                   int feat_dtype, hipStream_t stream) {
     KArgs k = a;
     k.anchor_blocks = (uint32_t)n_anchors_total;
     const dim3 grid((unsigned)n_anchors_total, 1);
-    return bf16 ? anchor_dispatch_scalar<uint16_t, true>(k, s, grid, stream)
-                : anchor_dispatch_scalar<float, true>(k, s, grid, stream);
+    return with_elem(feat_dtype, [&](auto t) {
+        return anchor_dispatch_scalar<decltype(t), true>(k, s, grid, stream);
+    });
+}
+
+// The gather form's first launch: zero the control words and row counts and,
+// for a 16-bit grad_out, write its binary32 copy.
+__global__ void __launch_bounds__(256) prep_kernel(uint32_t* __restrict__ zero, int64_t n_zero,
+                                                    const void* __restrict__ src, int dtype,
+                                                    float* __restrict__ dst, int64_t n_conv) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint4* z4 = reinterpret_cast<uint4*>(zero);           // 256-byte aligned
+    for (int64_t j = i0; j < n_zero / 4; j += stride) z4[j] = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t j = n_zero / 4 * 4 + i0; j < n_zero; j += stride) zero[j] = 0u;
+    for (int64_t j = i0; j < n_conv; j += stride) dst[j] = load_elem(src, j, dtype);
 }
 
 hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                  bool bf16, hipStream_t stream) {
-    // the control words and the row counts are one zeroed range
-    hipError_t e = launch_fill_zero(a.scan_done, (int64_t)(a.cnt - a.scan_done) + a.n_rows, stream);
+                                  int feat_dtype, hipStream_t stream) {
+    if (a.go_dtype != kF32) return hipErrorInvalidValue;   // the gather reads binary32 rows
+    // the control words and the row counts are one zeroed range; a 16-bit
+    // grad_out (go_src) is converted into a.grad_out in the same launch
+    const int64_t n_zero = (int64_t)(a.cnt - a.scan_done) + a.n_rows;
+    const int64_t n_conv = a.go_src ? (int64_t)a.n_anchors * a.C : 0;
+    hipLaunchKernelGGL(prep_kernel,
+                       dim3((unsigned)std::min<int64_t>(8192, blocks_for(std::max(n_zero / 4, n_conv), 256))),
+                       dim3(256), 0, stream, a.scan_done, n_zero, a.go_src, a.go_src_dtype,
+                       const_cast<float*>(static_cast<const float*>(a.grad_out)), n_conv);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
@@ -1402,8 +1422,9 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k.gather_blocks = blocks_for(waves, 256 / kWave);
         const dim3 ggrid(k.gather_blocks);
-        e = bf16 ? gather_dispatch<uint16_t, 4, true>(k, s, ggrid, stream)
-                 : gather_dispatch<float, 4, true>(k, s, ggrid, stream);
+        e = with_elem(feat_dtype, [&](auto t) {
+            return gather_dispatch<decltype(t), 4, true>(k, s, ggrid, stream);
+        });
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for((int64_t)a.n_samples, 256)), dim3(256),
                            0, stream, k);
@@ -1418,21 +1439,15 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         // does not store whole
         k.anchor_blocks = (uint32_t)(a.sliced ? n_anchors_total * kSlices : n_anchors_total);
         const dim3 grid((unsigned)(k.anchor_blocks + blocks_for(zwaves, s.waves)), 1);
-        if (a.sliced) {
-            if (bf16)
-                e = s.vec == 8 ? sliced_dispatch<uint16_t, 8>(k, s, grid, stream)
-                               : sliced_dispatch<uint16_t, 1>(k, s, grid, stream);
-            else
-                e = s.vec == 4 ? sliced_dispatch<float, 4>(k, s, grid, stream)
-                               : sliced_dispatch<float, 1>(k, s, grid, stream);
-        } else {
-            if (bf16)
-                e = s.vec == 8 ? anchor_dispatch_vec<uint16_t, 8>(k, s, grid, stream)
-                               : anchor_dispatch_scalar<uint16_t, false>(k, s, grid, stream);
-            else
-                e = s.vec == 4 ? anchor_dispatch_vec<float, 4>(k, s, grid, stream)
-                               : anchor_dispatch_scalar<float, false>(k, s, grid, stream);
-        }
+        e = with_elem(feat_dtype, [&](auto t) {
+            using T = decltype(t);
+            constexpr int V = sizeof(T) == 2 ? 8 : 4;
+            if (a.sliced)
+                return s.vec == V ? sliced_dispatch<T, V>(k, s, grid, stream)
+                                  : sliced_dispatch<T, 1>(k, s, grid, stream);
+            return s.vec == V ? anchor_dispatch_vec<T, V>(k, s, grid, stream)
+                              : anchor_dispatch_scalar<T, false>(k, s, grid, stream);
+        });
         if (e != hipSuccess) return e;
         // gather: one wave per chunk of the largest possible entry count (4 per
         // sample; waves past the real total return at once), followed in the

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "da_internal.h"
 
 namespace da {
@@ -24,8 +26,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              kRawBufferWord3);
 }
 
+// 16-bit element types: bfloat16 is held as uint16_t, IEEE binary16 as _Float16.
+// Both convert to binary32 exactly.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_bits(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits(w & 0xffffu); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits(w >> 16); }
+
+// binary32 -> bfloat16, round to nearest, ties to even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// One element of a tensor whose type is a run-time (wave-uniform) value.
+__device__ __forceinline__ void store_elem(void* base, int64_t i, float v, int dtype) {
+    if (dtype == kBF16)
+        static_cast<uint16_t*>(base)[i] = bf16_rne(v);
+    else if (dtype == kF16)
+        static_cast<_Float16*>(base)[i] = (_Float16)v;   // round to nearest even
+    else
+        static_cast<float*>(base)[i] = v;
+}
+__device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtype) {
+    if (dtype == kBF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+    if (dtype == kF16) return (float)static_cast<const _Float16*>(base)[i];
+    return static_cast<const float*>(base)[i];
+}
 
 // Load VEC consecutive channels as floats.  voff: per-lane byte offset (an
 // out-of-range value yields zeros); soff: wave-uniform byte offset.
@@ -85,6 +117,99 @@ struct VecLoad<uint16_t, 8> {
         }
     }
 };
+
+template <>
+struct VecLoad<_Float16, 1> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[1]) {
+        v[0] = f16_bits((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+    }
+};
+
+template <>
+struct VecLoad<_Float16, 4> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[4]) {
+        auto q = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        v[0] = f16_lo(q[0]);
+        v[1] = f16_hi(q[0]);
+        v[2] = f16_lo(q[1]);
+        v[3] = f16_hi(q[1]);
+    }
+};
+
+template <>
+struct VecLoad<_Float16, 8> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, float (&v)[8]) {
+        auto q = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = f16_lo(q[e]);
+            v[2 * e + 1] = f16_hi(q[e]);
+        }
+    }
+};
+
+// VEC consecutive 16-bit elements kept as the raw 32-bit words they arrive in
+// (half the registers of floats), converted when used.
+template <typename T, int VEC>
+struct RawVec {
+    static_assert(sizeof(T) == 2, "16-bit element types; binary32 is specialised below");
+    static constexpr int kWords = VEC * (int)sizeof(T) / 4;
+    static_assert(kWords >= 1, "at least one 32-bit word");
+    uint32_t w[kWords];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        if constexpr (kWords == 4) {
+            auto q = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = q[e];
+        } else if constexpr (kWords == 2) {
+            auto q = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+            w[0] = q[0];
+            w[1] = q[1];
+        } else {
+            w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        }
+    }
+    __device__ __forceinline__ void to_float(float (&v)[VEC]) const {
+#pragma unroll
+        for (int e = 0; e < kWords; ++e) {
+            if constexpr (std::is_same<T, _Float16>::value) {
+                v[2 * e] = f16_lo(w[e]);
+                v[2 * e + 1] = f16_hi(w[e]);
+            } else {
+                v[2 * e] = bf16_lo(w[e]);
+                v[2 * e + 1] = bf16_hi(w[e]);
+            }
+        }
+    }
+};
+
+// binary32 rows stay floats, loaded as before (the same registers; storing them as
+// words measured slower in the row-ordered gather)
+template <int VEC>
+struct RawVec<float, VEC> {
+    float v[VEC];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        VecLoad<float, VEC>::run(r, voff, soff, v);
+    }
+    __device__ __forceinline__ void to_float(float (&o)[VEC]) const {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = v[e];
+    }
+};
+
+// Calls f(T{}) with T the element type of dtype: float, uint16_t (bfloat16) or
+// _Float16.  Host side, to pick kernel instantiations.
+template <typename F>
+hipError_t with_elem(int dtype, F&& f) {
+    switch (dtype) {
+        case kBF16: return f(uint16_t{});
+        case kF16: return f(_Float16{});
+        default: return f(float{});
+    }
+}
 
 struct FwdDesc {
     uint32_t off[4];   // byte offsets of the four corner rows in the feature image

@@ -166,11 +166,11 @@ da_forward_kernel(KArgs a) {
     }
     __syncthreads();
     const int nwaves = nthreads / kWave;
-    float* orow = a.out + ba * a.C + (int64_t)v0 * L * VEC;
+    const int64_t o0 = ba * a.C + (int64_t)v0 * L * VEC;
     for (int c = tid; c < nch; c += nthreads) {
         float sum = 0.0f;
         for (int w = 0; w < nwaves; ++w) sum += red[w * nch + c];
-        orow[c] = sum;
+        store_elem(a.out, o0 + c, sum, a.out_dtype);
     }
 }
 
@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(256) fwd_reduce_kernel(KArgs a) {
         float s = 0.0f;
 #pragma unroll
         for (int x = 0; x < kSlices; ++x) s += a.fwd_part[x * n + i];
-        a.out[i] = s;
+        store_elem(a.out, i, s, a.out_dtype);
     }
 }
 
@@ -350,15 +350,14 @@ hipError_t fwd_dispatch_nv(const KArgs& a, const LaunchShape& s, dim3 grid, hipS
 }  // namespace
 
 hipError_t launch_forward_sliced(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                 bool bf16, hipStream_t stream) {
+                                 int feat_dtype, hipStream_t stream) {
     const dim3 grid((unsigned)(n_anchors_total * kSlices), (unsigned)s.chunks);
-    hipError_t e;
-    if (bf16)
-        e = s.vec == 8 ? fwd_sliced_dispatch<uint16_t, 8>(a, s, grid, stream)
-                       : fwd_sliced_dispatch<uint16_t, 1>(a, s, grid, stream);
-    else
-        e = s.vec == 4 ? fwd_sliced_dispatch<float, 4>(a, s, grid, stream)
-                       : fwd_sliced_dispatch<float, 1>(a, s, grid, stream);
+    const hipError_t e = with_elem(feat_dtype, [&](auto t) {
+        using T = decltype(t);
+        constexpr int V = sizeof(T) == 2 ? 8 : 4;   // 16-byte vectors
+        return s.vec == V ? fwd_sliced_dispatch<T, V>(a, s, grid, stream)
+                          : fwd_sliced_dispatch<T, 1>(a, s, grid, stream);
+    });
     if (e != hipSuccess) return e;
     int64_t blocks = ((int64_t)a.n_anchors * a.C + 255) / 256;
     if (blocks > 65536) blocks = 65536;
@@ -366,15 +365,15 @@ hipError_t launch_forward_sliced(const KArgs& a, const LaunchShape& s, int64_t n
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total, bool bf16,
-                          hipStream_t stream) {
+hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
+                          int feat_dtype, hipStream_t stream) {
     const dim3 grid((unsigned)n_anchors_total, (unsigned)s.chunks);
-    if (bf16) {
-        return s.vec == 8 ? fwd_dispatch_nv<uint16_t, 8>(a, s, grid, stream)
-                          : fwd_dispatch_nv<uint16_t, 1>(a, s, grid, stream);
-    }
-    return s.vec == 4 ? fwd_dispatch_nv<float, 4>(a, s, grid, stream)
-                      : fwd_dispatch_nv<float, 1>(a, s, grid, stream);
+    return with_elem(feat_dtype, [&](auto t) {
+        using T = decltype(t);
+        constexpr int V = sizeof(T) == 2 ? 8 : 4;
+        return s.vec == V ? fwd_dispatch_nv<T, V>(a, s, grid, stream)
+                          : fwd_dispatch_nv<T, 1>(a, s, grid, stream);
+    });
 }
 
 }  // namespace da

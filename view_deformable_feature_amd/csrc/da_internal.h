@@ -74,11 +74,11 @@ struct LevelTable {
 // one feature row: lane li covers vectors li, li + L, li + 2L, ... of VEC
 // consecutive channels each.
 struct KArgs {
-    const void* feat;          // [bs, num_feat, C] f32 or bf16
+    const void* feat;          // [bs, num_feat, C] of feat_dtype
     const float* loc;          // [bs, A, P, K, 2]
     const float* weights;      // [bs, A, P, K, S, G]
-    const float* grad_out;     // [bs, A, C]
-    float* out;                // [bs, A, C]
+    const void* grad_out;      // [bs, A, C] of go_dtype (binary32 in the gather form)
+    void* out;                 // [bs, A, C] of out_dtype
     float* grad_feat;          // [bs, num_feat, C]
     float* grad_loc;           // [bs, A, P, K, 2]
     float* grad_weights;       // [bs, A, P, K, S, G]
@@ -135,12 +135,19 @@ struct KArgs {
     int32_t seg;               // backward: group-reduction segment (lanes), see kernels
     int32_t gather_vec;        // feature-gradient gather: channels per lane vector (1 or 4)
     int32_t accumulate;        // feature-gradient gather: add to grad_feat instead of overwrite
+    int32_t out_dtype;         // kF32 / kBF16 / kF16: element type of out
+    int32_t go_dtype;          // element type of grad_out as the kernels read it
+    const void* go_src;        // gather form, 16-bit grad_out: the caller's tensor, converted
+    int32_t go_src_dtype;      // into grad_out (workspace) by the first launch
     LevelTable lv;
 };
 
+// Element types (the values of da_dtype).
+constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
+
 // Launch shapes chosen by the host.
 struct LaunchShape {
-    int vec;            // channels per lane vector (1, 4 for f32 / 8 for bf16)
+    int vec;            // channels per lane vector (1, 4 for f32 / 8 for 16-bit types)
     int nvc;            // compile-time vectors per lane (forward 1..8, backward 1..16)
     int waves;          // waves per workgroup
     int chunks;         // grid.y
@@ -153,18 +160,18 @@ constexpr int kFwdDescBytes = 32;   // 4 byte offsets + 4 corner weights
 constexpr int kBwdDescBytes = 80;   // 4 feat offsets + 4 grad offsets + 3 x 4 coefficients
 
 hipError_t launch_forward(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                          bool bf16, hipStream_t stream);
+                          int feat_dtype, hipStream_t stream);
 // Forward by level slices: per-slice partials into a.fwd_part, then their sum
 // in fixed slice order into a.out.
 hipError_t launch_forward_sliced(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                 bool bf16, hipStream_t stream);
+                                 int feat_dtype, hipStream_t stream);
 // Backward, scatter form: grad_feat must already hold zeros (or the sum to add to).
 hipError_t launch_backward_scatter(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                   bool bf16, hipStream_t stream);
+                                   int feat_dtype, hipStream_t stream);
 // Backward, gather form: count, scan, per-anchor pass (location / weight
 // gradients and entry fill), then the row-parallel feature-gradient gather.
 hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t n_anchors_total,
-                                  bool bf16, hipStream_t stream);
+                                  int feat_dtype, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, int64_t n_words, hipStream_t stream);
 
 }  // namespace da

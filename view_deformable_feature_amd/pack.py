@@ -29,7 +29,9 @@ def _dtype_code(dt: torch.dtype) -> int:
         return _lib.DA_F32
     if dt == torch.bfloat16:
         return _lib.DA_BF16
-    raise TypeError(f"packing supports float32 and bfloat16 maps, got {dt}")
+    if dt == torch.float16:
+        return _lib.DA_F16
+    raise TypeError(f"packing supports float32, bfloat16 and float16 maps, got {dt}")
 
 
 def _problem(bs, num_cams, num_scale, C, dtype) -> _lib.DAPackProblem:

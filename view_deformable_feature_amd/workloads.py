@@ -45,7 +45,7 @@ class Workload:
     groups: int
     anchors: int
     pts: int
-    feat_dtype: str = "f32"            # "f32" or "bf16"
+    feat_dtype: str = "f32"            # "f32", "bf16" or "f16"
     loc_kind: str = "uniform"          # "uniform" or "clustered"
     loc_lo: float = 0.0
     loc_hi: float = 1.0
@@ -79,7 +79,7 @@ class Workload:
 
     @property
     def feat_elem_bytes(self) -> int:
-        return 2 if self.feat_dtype == "bf16" else 4
+        return 2 if self.feat_dtype in ("bf16", "f16") else 4
 
 
 _NUSC_LEVELS = ((64, 176), (32, 88), (16, 44), (8, 22))      # 256x704 image, strides 4..32
@@ -101,6 +101,10 @@ WORKLOADS: Dict[str, Workload] = {
     "large_bf16": Workload("large_bf16", bs=4, num_cams=6, levels=_LARGE_LEVELS, C=256,
                            groups=8, anchors=1500, pts=13, feat_dtype="bf16",
                            loc_lo=0.0, loc_hi=1.0, seed=1004),
+    # the nuScenes shape with binary16 features (half precision, as DCNv4 runs)
+    "nuscenes_f16": Workload("nuscenes_f16", bs=1, num_cams=6, levels=_NUSC_LEVELS, C=256,
+                             groups=8, anchors=900, pts=13, feat_dtype="f16",
+                             loc_lo=-0.05, loc_hi=1.05, seed=1005),
 }
 
 
@@ -156,8 +160,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, with_grad_out: bool = 
                 ) -> Dict[str, np.ndarray]:
     """Draw one batch of inputs for ``wl``.
 
-    Returns a dict with ``feat`` (float32, or uint16 bf16 bit patterns when
-    ``wl.feat_dtype == "bf16"``), ``spatial_shape``, ``scale_start_index``,
+    Returns a dict with ``feat`` (float32; uint16 bf16 bit patterns when
+    ``wl.feat_dtype == "bf16"``; float16 when "f16"), ``spatial_shape``, ``scale_start_index``,
     ``loc``, ``weights`` and (optionally) ``grad_out``.
     """
     rng = np.random.default_rng(wl.seed if seed is None else seed)
@@ -167,6 +171,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, with_grad_out: bool = 
     feat = rng.standard_normal((bs, wl.num_feat, C), dtype=np.float32)
     if wl.feat_dtype == "bf16":
         feat = bf16_bits_from_f32(feat)
+    elif wl.feat_dtype == "f16":
+        feat = feat.astype(np.float16)           # round to nearest even
     elif wl.feat_dtype != "f32":
         raise ValueError(f"unknown feat dtype {wl.feat_dtype!r}")
 
