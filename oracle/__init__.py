@@ -4,9 +4,11 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
 the CPU-baseline leg of the benchmark.  The product library never imports,
 links or calls anything here, and this package imports nothing from it.
 
-The arithmetic lives in ``oracle.c``; its header states the definition it
-follows (the Sparse4D deformable_aggregation walkthrough, mhpn.cn/news/1081857,
-sections 3.1, 3.2, 4.1 and 5.1) and the readings taken where the page is
+The arithmetic lives in ``oracle.c`` (deformable aggregation) and
+``dcn_oracle.c`` (deformable convolution); their headers state the definitions
+they follow (the Sparse4D deformable_aggregation walkthrough,
+mhpn.cn/news/1081857, sections 3.1, 3.2, 4.1 and 5.1; the DCNv4 paper notes,
+docsaid.org, "Defining the problem") and the readings taken where the pages are
 silent.  This file only marshals numpy arrays.
 """
 from __future__ import annotations
@@ -19,20 +21,21 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "oracle.c")
+_SRCS = [os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "dcn_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 __all__ = ["build", "forward", "backward", "backward_anchors", "grad_feat_rows",
-           "pack_levels", "unpack_levels"]
+           "pack_levels", "unpack_levels", "dcn_out_size", "dcn_forward", "dcn_backward"]
 
 
 def build(force: bool = True) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no contraction)."""
+    """Compile the oracle sources into ``liboracle.so`` with gcc (no fast-math, no
+    contraction)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+                               "-fPIC", "-shared", *_SRCS, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -40,7 +43,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f)
+                                           for f in _SRCS):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i64, i32p, vp = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
@@ -49,8 +53,13 @@ def _load():
         lib.oracle_backward.argtypes = prob + [vp, vp, vp, vp]
         lib.oracle_backward_anchors.argtypes = prob + [vp, vp, i64, vp, vp]
         lib.oracle_grad_feat_rows.argtypes = prob + [vp, vp, i64, vp]
+        dcn = [i64] * 13
+        lib.oracle_dcn_forward.argtypes = dcn + [vp, vp, vp]
+        lib.oracle_dcn_backward.argtypes = dcn + [vp, vp, vp, vp, vp]
+        lib.oracle_dcn_out_size.argtypes = dcn + [vp, vp]
         for f in (lib.oracle_forward, lib.oracle_backward, lib.oracle_backward_anchors,
-                  lib.oracle_grad_feat_rows):
+                  lib.oracle_grad_feat_rows, lib.oracle_dcn_forward, lib.oracle_dcn_backward,
+                  lib.oracle_dcn_out_size):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -194,3 +203,77 @@ def unpack_levels(packed: np.ndarray, scale_hw: Sequence[Tuple[int, int]], num_c
             maps[s][:, k] = np.transpose(block, (0, 3, 1, 2))
             row += h * w
     return maps
+
+
+# ---------------------------------------------------------------------------------------
+# deformable convolution (dcn_oracle.c)
+# ---------------------------------------------------------------------------------------
+
+def _pair(v) -> Tuple[int, int]:
+    return (int(v), int(v)) if np.isscalar(v) else (int(v[0]), int(v[1]))
+
+
+def _dcn_input(x: np.ndarray) -> np.ndarray:
+    """float32 values of the input (binary16 converts exactly); bfloat16 comes as
+    its uint16 bit patterns."""
+    if x.dtype == np.uint16:
+        return (np.ascontiguousarray(x).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if x.dtype not in (np.float32, np.float16):
+        raise TypeError("input must be float32, float16 or uint16 bfloat16 bit patterns")
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _dcn_args(x, groups, kernel, stride, pad, dilation):
+    N, H, W, C = x.shape
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    return [N, H, W, C, int(groups), kh, kw, sh, sw, ph, pw, dh, dw]
+
+
+def dcn_out_size(H, W, kernel=3, stride=1, pad=1, dilation=1) -> Tuple[int, int]:
+    args = [1, H, W, 1, 1, *_pair(kernel), *_pair(stride), *_pair(pad), *_pair(dilation)]
+    ho, wo = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = _load().oracle_dcn_out_size(*args, ctypes.byref(ho), ctypes.byref(wo))
+    if rc:
+        raise ValueError(f"oracle_dcn_out_size rejected the problem (rc={rc})")
+    return ho.value, wo.value
+
+
+def dcn_forward(x, offset_mask, groups, kernel=3, stride=1, pad=1, dilation=1) -> np.ndarray:
+    """x [N, H, W, C], offset_mask [N, Ho, Wo, G, 3K] float32 -> out [N, Ho, Wo, C] fp64."""
+    xf = _dcn_input(x)
+    args = _dcn_args(xf, groups, kernel, stride, pad, dilation)
+    ho, wo = dcn_out_size(args[1], args[2], kernel, stride, pad, dilation)
+    K = args[5] * args[6]
+    om = np.ascontiguousarray(offset_mask, dtype=np.float32)
+    if om.shape != (args[0], ho, wo, args[4], 3 * K):
+        raise ValueError(f"offset_mask shape {om.shape}")
+    out = np.empty((args[0], ho, wo, args[3]), dtype=np.float64)
+    rc = _load().oracle_dcn_forward(*args, _ptr(xf), _ptr(om), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_dcn_forward rejected the problem (rc={rc})")
+    return out
+
+
+def dcn_backward(x, offset_mask, grad_out, groups, kernel=3, stride=1, pad=1, dilation=1):
+    """(grad_input [N, H, W, C], grad_offset_mask [N, Ho, Wo, G, 3K]), fp64."""
+    xf = _dcn_input(x)
+    args = _dcn_args(xf, groups, kernel, stride, pad, dilation)
+    ho, wo = dcn_out_size(args[1], args[2], kernel, stride, pad, dilation)
+    K = args[5] * args[6]
+    om = np.ascontiguousarray(offset_mask, dtype=np.float32)
+    if om.shape != (args[0], ho, wo, args[4], 3 * K):
+        raise ValueError(f"offset_mask shape {om.shape}")
+    if np.asarray(grad_out).dtype == np.uint16:
+        raise TypeError("pass a bfloat16 grad_out as its float32 values")
+    go = np.ascontiguousarray(grad_out, dtype=np.float32)
+    if go.shape != (args[0], ho, wo, args[3]):
+        raise ValueError(f"grad_out shape {go.shape}")
+    gi = np.empty(xf.shape, dtype=np.float64)
+    gom = np.empty(om.shape, dtype=np.float64)
+    rc = _load().oracle_dcn_backward(*args, _ptr(xf), _ptr(om), _ptr(go), _ptr(gi), _ptr(gom))
+    if rc:
+        raise ValueError(f"oracle_dcn_backward rejected the problem (rc={rc})")
+    return gi, gom

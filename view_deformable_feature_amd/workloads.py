@@ -27,7 +27,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_bits_from_f32",
-           "bf16_bits_to_f32", "level_table"]
+           "bf16_bits_to_f32", "level_table", "DcnWorkload", "DCN_WORKLOADS",
+           "make_dcn_inputs", "dcn_custom"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -201,3 +202,91 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, with_grad_out: bool = 
 def custom(name: str, **kw) -> Workload:
     """A workload with explicit fields (used by tests for ragged shapes)."""
     return Workload(name=name, **kw)
+
+
+# ---------------------------------------------------------------------------------------
+# deformable convolution (DCNv3 / DCNv4 operator) inputs
+# ---------------------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DcnWorkload:
+    """Shapes of one deformable-convolution call: input [N, H, W, C] channel-last,
+    offset_mask [N, Ho, Wo, G, 3K] ((dx, dy) per tap, then the K modulation scalars)."""
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    groups: int
+    kernel: Tuple[int, int] = (3, 3)
+    stride: Tuple[int, int] = (1, 1)
+    pad: Tuple[int, int] = (1, 1)
+    dilation: Tuple[int, int] = (1, 1)
+    dtype: str = "f32"                 # "f32", "bf16" or "f16"
+    offset_sigma: float = 1.0          # offsets N(0, sigma^2) pixels
+    seed: int = 0
+
+    @property
+    def K(self) -> int:
+        return self.kernel[0] * self.kernel[1]
+
+    @property
+    def out_hw(self) -> Tuple[int, int]:
+        ho = (self.H + 2 * self.pad[0] - self.dilation[0] * (self.kernel[0] - 1) - 1) // self.stride[0] + 1
+        wo = (self.W + 2 * self.pad[1] - self.dilation[1] * (self.kernel[1] - 1) - 1) // self.stride[1] + 1
+        return ho, wo
+
+    @property
+    def samples(self) -> int:
+        """bilinear samples per call: N * Ho * Wo * G * K"""
+        ho, wo = self.out_hw
+        return self.N * ho * wo * self.groups * self.K
+
+    @property
+    def sample_channels(self) -> int:
+        return self.samples * (self.C // self.groups)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+# The DCNv4 notes time the operator at 56x56x128 with batch 64 and 4 groups (its
+# kernel ablation table) and compare input sizes 28x28x256 and 14x14x512 (its first
+# figure; groups not stated there: 32 channels per group kept).
+DCN_WORKLOADS: Dict[str, DcnWorkload] = {
+    "dcn_tiny": DcnWorkload("dcn_tiny", N=1, H=7, W=9, C=16, groups=2, seed=2000),
+    "dcn_56": DcnWorkload("dcn_56", N=64, H=56, W=56, C=128, groups=4, seed=2001),
+    "dcn_56_f16": DcnWorkload("dcn_56_f16", N=64, H=56, W=56, C=128, groups=4, dtype="f16",
+                              seed=2002),
+    "dcn_28": DcnWorkload("dcn_28", N=64, H=28, W=28, C=256, groups=8, seed=2003),
+    "dcn_14": DcnWorkload("dcn_14", N=64, H=14, W=14, C=512, groups=16, seed=2004),
+}
+
+
+def make_dcn_inputs(wl: DcnWorkload, seed: Optional[int] = None, with_grad_out: bool = True
+                    ) -> Dict[str, np.ndarray]:
+    """Draw one call's inputs: ``input`` (float32, float16, or uint16 bfloat16 bit
+    patterns), ``offset_mask`` (offsets N(0, sigma^2) pixels, scalars U[-1, 1): DCNv4
+    leaves them unbounded) and ``grad_out`` N(0, 1)."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    ho, wo = wl.out_hw
+    x = rng.standard_normal((wl.N, wl.H, wl.W, wl.C), dtype=np.float32)
+    if wl.dtype == "bf16":
+        x = bf16_bits_from_f32(x)
+    elif wl.dtype == "f16":
+        x = x.astype(np.float16)
+    elif wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype!r}")
+    G, K = wl.groups, wl.K
+    om = np.empty((wl.N, ho, wo, G, 3 * K), dtype=np.float32)
+    om[..., :2 * K] = rng.normal(0.0, wl.offset_sigma, size=(wl.N, ho, wo, G, 2 * K))
+    om[..., 2 * K:] = rng.uniform(-1.0, 1.0, size=(wl.N, ho, wo, G, K))
+    out = dict(input=x, offset_mask=om)
+    if with_grad_out:
+        out["grad_out"] = rng.standard_normal((wl.N, ho, wo, wl.C), dtype=np.float32)
+    return out
+
+
+def dcn_custom(name: str, **kw) -> DcnWorkload:
+    return DcnWorkload(name=name, **kw)
