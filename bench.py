@@ -33,14 +33,16 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nuscenes.json")
 
 
+AGG_SOURCES = ("da_forward.hip", "da_backward.hip", "da_api.cpp", "da_internal.h", "da_device.h")
+
+
 def kernel_source_hash():
-    """Hash of the kernel and launch sources (not the public header, which only
-    declares): counter-derived traffic is reported only for the code it was
-    measured on."""
+    """Hash of the aggregation's kernel and launch sources: counter-derived traffic
+    is reported only for the code it was measured on."""
     import hashlib
-    from view_deformable_feature_amd.build import HEADERS, SOURCES
+    from view_deformable_feature_amd.build import CSRC
     h = hashlib.sha256()
-    for f in sorted(SOURCES + [x for x in HEADERS if not x.endswith("deformagg.h")]):
+    for f in sorted(os.path.join(CSRC, x) for x in AGG_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -279,3 +279,75 @@ def test_forward_workspace_checks(lib):
     assert _fwd(lib, p, ws=FAKE, ws_bytes=need - 1) == 1 and "needed" in _msg(lib)
     # a malformed problem is reported before the workspace is looked at
     assert _fwd(lib, _prob(flags=3), ws=FAKE + 16, ws_bytes=0) == 1 and "flags" in _msg(lib)
+
+
+# ---------------------------------------------------------------------------------------
+# deformable convolution (include/dcn.h): host-side checks only
+# ---------------------------------------------------------------------------------------
+
+def _dprob(**kw):
+    d = dict(batch=2, height=8, width=9, channels=16, groups=4, kernel_h=3, kernel_w=3,
+             stride_h=1, stride_w=1, pad_h=1, pad_w=1, dilation_h=1, dilation_w=1,
+             in_dtype=0, out_dtype=0, flags=0, reserved=0)
+    d.update(kw)
+    return _lib.DCNProblem(**d)
+
+
+def _dcn_fwd(lib, prob, inp=FAKE, om=FAKE, out=FAKE):
+    vp = ctypes.c_void_p
+    return lib.dcn_forward(ctypes.byref(prob), vp(inp), vp(om), vp(out), None)
+
+
+def _dcn_bwd(lib, prob, inp=FAKE, om=FAKE, go=FAKE, gi=FAKE, gom=FAKE):
+    vp = ctypes.c_void_p
+    return lib.dcn_backward(ctypes.byref(prob), vp(inp), vp(om), vp(go), vp(gi), vp(gom),
+                            None, 0, None)
+
+
+def test_dcn_out_size(lib):
+    ho, wo = ctypes.c_int64(0), ctypes.c_int64(0)
+    for kw, expect in ((dict(), (8, 9)), (dict(stride_h=2, stride_w=2), (4, 5)),
+                       (dict(kernel_h=3, kernel_w=5, pad_h=1, pad_w=2, dilation_h=2), (6, 9)),
+                       (dict(kernel_h=1, kernel_w=1, pad_h=0, pad_w=0), (8, 9))):
+        assert lib.dcn_out_size(ctypes.byref(_dprob(**kw)), ctypes.byref(ho), ctypes.byref(wo)) == 0
+        assert (ho.value, wo.value) == expect, kw
+
+
+@pytest.mark.parametrize("kw, code, needle", [
+    (dict(channels=18), 1, "multiple of groups"),
+    (dict(groups=0), 1, ">= 1"),
+    (dict(height=0), 1, ">= 1"),
+    (dict(batch=-1), 1, "batch"),
+    (dict(stride_h=0), 1, "stride"),
+    (dict(dilation_w=0), 1, "dilation"),
+    (dict(pad_h=-1), 1, "padding"),
+    (dict(kernel_h=11, pad_h=0), 1, "does not fit"),
+    (dict(in_dtype=3), 1, "da_dtype"),
+    (dict(out_dtype=-1), 1, "da_dtype"),
+    (dict(flags=1), 1, "flags"),
+    (dict(reserved=2), 1, "reserved"),
+    (dict(channels=1 << 17, groups=1), 2, "2^16"),
+    (dict(channels=2048, groups=4), 2, "channels per group"),
+    (dict(batch=64, height=1024, width=1024, channels=64, groups=4), 2, "4 GiB"),
+])
+def test_dcn_rejects_malformed_problem(lib, kw, code, needle):
+    assert _dcn_fwd(lib, _dprob(**kw)) == code
+    assert needle in _msg(lib)
+    assert _dcn_bwd(lib, _dprob(**kw)) == code
+
+
+def test_dcn_rejects_null_and_misaligned(lib):
+    p = _dprob()
+    assert _dcn_fwd(lib, p, inp=0) == 1 and "NULL" in _msg(lib)
+    assert _dcn_fwd(lib, p, om=0) == 1
+    assert _dcn_fwd(lib, p, out=0) == 1
+    assert _dcn_fwd(lib, p, out=FAKE + 2) == 1 and "aligned" in _msg(lib)
+    assert _dcn_fwd(lib, _dprob(in_dtype=2), inp=FAKE + 1) == 1
+    assert _dcn_bwd(lib, p, gi=0) == 1 and "grad_input" in _msg(lib)
+    assert _dcn_bwd(lib, p, gom=0) == 1
+    assert _dcn_bwd(lib, p, go=FAKE + 2) == 1 and "aligned" in _msg(lib)
+    assert _dcn_bwd(lib, _dprob(out_dtype=1), go=FAKE + 1) == 1
+    assert lib.dcn_forward(None, None, None, None, None) == 1 and "NULL" in _msg(lib)
+    n = ctypes.c_size_t(7)
+    assert lib.dcn_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert lib.dcn_backward_workspace_size(ctypes.byref(p), None) == 1

@@ -1,0 +1,170 @@
+"""GPU parity of the deformable convolution (include/dcn.h) against the fp64
+oracle (oracle/dcn_oracle.c): every output element on small and ragged shapes,
+the full 56x56x128 batch-64 shape of the DCNv4 notes, 16-bit inputs and outputs,
+and the edge cases of the definition (positions outside the image, NaN offsets,
+an empty batch, a 1x1 kernel).
+
+Tolerances, per element |gpu - ref| <= tol * (1 + |ref|): forward 1e-4, backward
+1e-3 (binary32 arithmetic; 16-bit inputs convert exactly, so the same bounds); an
+out stored in 16 bits adds half an ulp (2^-8 bfloat16, 2^-11 binary16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL_BWD, TOL_FWD, TOL_OUT_BF16, TOL_OUT_F16, assert_close, say
+from view_deformable_feature_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": dict(N=1, H=7, W=9, C=16, groups=2),
+    "s2": dict(N=2, H=9, W=8, C=12, groups=3, stride=(2, 2)),
+    "k35_dil": dict(N=1, H=9, W=11, C=24, groups=2, kernel=(3, 5), stride=(1, 2), pad=(1, 2),
+                    dilation=(2, 1)),
+    "k1": dict(N=2, H=6, W=5, C=8, groups=1, kernel=(1, 1), pad=(0, 0)),
+    "c6_g6": dict(N=1, H=10, W=7, C=6, groups=6),                  # one channel per group
+    "c40_g5": dict(N=2, H=8, W=8, C=40, groups=5),                 # D = 8
+    "c96_g3": dict(N=1, H=12, W=13, C=96, groups=3),               # D = 32, G * Lg = 24 lanes
+    "c256_g2": dict(N=1, H=6, W=7, C=256, groups=2),               # D = 128: 32 lanes per group
+    "c512_g16": dict(N=1, H=5, W=6, C=512, groups=16),             # two groups per lane
+    "far": dict(N=1, H=8, W=8, C=16, groups=4, offset_sigma=6.0),  # many positions outside
+    "d3_pad3": dict(N=1, H=11, W=10, C=32, groups=4, pad=(3, 3), dilation=(3, 3)),
+}
+
+
+def _wl(name, **over):
+    kw = dict(CASES[name], seed=3000 + sorted(CASES).index(name))
+    kw.update(over)
+    return W.dcn_custom(name, **kw)
+
+
+def _dev(inp):
+    x = inp["input"]
+    if x.dtype == np.uint16:
+        xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        xt = torch.from_numpy(x).cuda()
+    return xt, torch.from_numpy(inp["offset_mask"]).cuda()
+
+
+def _conf(wl):
+    return dict(groups=wl.groups, kernel=wl.kernel, stride=wl.stride, pad=wl.pad,
+                dilation=wl.dilation)
+
+
+def _check(wl, out_dtype=None, go_dtype=torch.float32):
+    import view_deformable_feature_amd as vdf
+    inp = W.make_dcn_inputs(wl)
+    x, om = _dev(inp)
+    say(f"[dcn] {wl.name} {wl.dtype} out={out_dtype} go={go_dtype}")
+    out = vdf.dcn_forward(x, om, **_conf(wl), out_dtype=out_dtype)
+    go_t = torch.from_numpy(inp["grad_out"]).cuda().to(go_dtype)
+    gi, gom = vdf.dcn_backward(x, om, go_t, **_conf(wl))
+    torch.cuda.synchronize()
+    ref = oracle.dcn_forward(inp["input"], inp["offset_mask"], **_conf(wl))
+    tol = {None: TOL_FWD, torch.float32: TOL_FWD, torch.bfloat16: TOL_OUT_BF16,
+           torch.float16: TOL_OUT_F16}[out_dtype]
+    e0 = assert_close(f"{wl.name} out", out.float().cpu().numpy(), ref, tol)
+    r_gi, r_gom = oracle.dcn_backward(inp["input"], inp["offset_mask"],
+                                      go_t.float().cpu().numpy(), **_conf(wl))
+    e1 = assert_close(f"{wl.name} grad_input", gi.cpu().numpy(), r_gi, TOL_BWD)
+    e2 = assert_close(f"{wl.name} grad_offset_mask", gom.cpu().numpy(), r_gom, TOL_BWD)
+    say(f"[dcn] {wl.name}: max err out {e0:.2e} gi {e1:.2e} gom {e2:.2e}")
+    return x, om, out, gi, gom
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_dcn_full(name):
+    _check(_wl(name))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("name", ["tiny", "c96_g3", "c512_g16", "k35_dil"])
+def test_dcn_16bit_input(name, dtype):
+    _check(_wl(name, dtype=dtype))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_dcn_16bit_out_and_grad_out(out_dtype):
+    wl = _wl("c40_g5")
+    x, om, out16, _, _ = _check(wl, out_dtype=out_dtype, go_dtype=out_dtype)
+    import view_deformable_feature_amd as vdf
+    out32 = vdf.dcn_forward(x, om, **_conf(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32.to(out_dtype)), "16-bit out is not RNE(binary32 out)"
+
+
+def test_dcn_forward_deterministic_and_offset_grads_repeatable():
+    import view_deformable_feature_amd as vdf
+    wl = _wl("c96_g3")
+    inp = W.make_dcn_inputs(wl)
+    x, om = _dev(inp)
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+    o1 = vdf.dcn_forward(x, om, **_conf(wl))
+    o2 = vdf.dcn_forward(x, om, **_conf(wl))
+    g1 = vdf.dcn_backward(x, om, go, **_conf(wl))
+    g2 = vdf.dcn_backward(x, om, go, **_conf(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(g1[1], g2[1])
+
+
+def test_dcn_nan_and_far_offsets():
+    import view_deformable_feature_amd as vdf
+    wl = _wl("tiny")
+    inp = W.make_dcn_inputs(wl)
+    om = inp["offset_mask"].copy()
+    K = wl.K
+    hits = [(0, 1, 2, 1, 0, np.nan), (0, 3, 3, 0, 1, 1e6), (0, 6, 8, 1, 8, -1e30),
+            (0, 0, 0, 0, 4, 0.999)]          # the last one stays inside
+    for n, h, w, g, t, v in hits:
+        om[n, h, w, g, 2 * t] = v
+    inp2 = dict(inp, offset_mask=om)
+    x, omt = _dev(inp2)
+    out = vdf.dcn_forward(x, omt, **_conf(wl))
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+    gi, gom = vdf.dcn_backward(x, omt, go, **_conf(wl))
+    torch.cuda.synchronize()
+    assert_close("nan out", out.cpu().numpy(), oracle.dcn_forward(inp["input"], om, **_conf(wl)),
+                 TOL_FWD)
+    r_gi, r_gom = oracle.dcn_backward(inp["input"], om, inp["grad_out"], **_conf(wl))
+    assert_close("nan grad_input", gi.cpu().numpy(), r_gi, TOL_BWD)
+    assert_close("nan grad_om", gom.cpu().numpy(), r_gom, TOL_BWD)
+    for n, h, w, g, t, v in hits[:3]:
+        assert float(gom[n, h, w, g, 2 * K + t]) == 0.0
+
+
+def test_dcn_empty_batch():
+    import view_deformable_feature_amd as vdf
+    x = torch.zeros((0, 5, 5, 8), device="cuda")
+    om = torch.zeros((0, 5, 5, 2, 27), device="cuda")
+    out = vdf.dcn_forward(x, om, 2)
+    gi, gom = vdf.dcn_backward(x, om, torch.zeros((0, 5, 5, 8), device="cuda"), 2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 5, 5, 8) and gi.shape == x.shape and gom.shape == om.shape
+
+
+def test_dcn_56_full_size():
+    """The DCNv4 notes' kernel ablation shape: 56x56x128, batch 64, 4 groups."""
+    _check(W.DCN_WORKLOADS["dcn_56"])
+
+
+def test_dcn_autograd():
+    import view_deformable_feature_amd as vdf
+    wl = _wl("c40_g5", dtype="f16")
+    inp = W.make_dcn_inputs(wl)
+    x, om = _dev(inp)
+    x = x.clone().requires_grad_(True)
+    om = om.clone().requires_grad_(True)
+    out = vdf.deformable_conv(x, om, **_conf(wl), out_dtype=torch.bfloat16)
+    g = torch.from_numpy(inp["grad_out"]).cuda()
+    (out.float() * g).sum().backward()
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16 and x.grad.dtype == torch.float16
+    gi, gom = vdf.dcn_backward(x.detach(), om.detach(), g.to(torch.bfloat16), **_conf(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(om.grad, gom)
+    assert_close("autograd grad_input", x.grad.float().cpu().numpy(),
+                 gi.to(torch.float16).float().cpu().numpy(), 1e-3)

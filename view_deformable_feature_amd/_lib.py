@@ -1,4 +1,4 @@
-"""ctypes declarations of the libdeformagg C ABI (include/deformagg.h).
+"""ctypes declarations of the libdeformagg C ABI (include/deformagg.h, include/dcn.h).
 
 Only marshalling lives here.  Loading fails loudly when the library has not
 been built: there is no CPU fallback.
@@ -13,6 +13,7 @@ from typing import List
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "deformagg.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(PKG_DIR), "include", "dcn.h")]
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
 DA_F32, DA_BF16, DA_F16 = 0, 1, 2
@@ -34,6 +35,24 @@ class DAProblem(ctypes.Structure):
         ("feat_dtype", ctypes.c_int32),
         ("flags", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class DCNProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("height", ctypes.c_int64),
+        ("width", ctypes.c_int64),
+        ("channels", ctypes.c_int64),
+        ("groups", ctypes.c_int64),
+        ("kernel_h", ctypes.c_int32), ("kernel_w", ctypes.c_int32),
+        ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+        ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
+        ("dilation_h", ctypes.c_int32), ("dilation_w", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -90,6 +109,14 @@ def load() -> ctypes.CDLL:
     lib.da_pack_levels.restype = ctypes.c_int
     lib.da_unpack_levels.argtypes = [pprob, i32p, vp, vpp, vp]
     lib.da_unpack_levels.restype = ctypes.c_int
+    dprob = ctypes.POINTER(DCNProblem)
+    i64p, szp = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
+    lib.dcn_out_size.argtypes = [dprob, i64p, i64p]
+    lib.dcn_forward.argtypes = [dprob, vp, vp, vp, vp]
+    lib.dcn_backward_workspace_size.argtypes = [dprob, szp]
+    lib.dcn_backward.argtypes = [dprob, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    for name in ("dcn_out_size", "dcn_forward", "dcn_backward_workspace_size", "dcn_backward"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.da_status_string.argtypes = [ctypes.c_int]
     lib.da_status_string.restype = ctypes.c_char_p
     lib.da_last_error.argtypes = []
@@ -107,8 +134,11 @@ def check(status: int, func: str) -> None:
 
 
 def declared_functions() -> List[str]:
-    """Names of the functions include/deformagg.h declares."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"\b(da_[a-z_]+)\s*\(", text)
+    """Names of the functions the public headers (include/*.h) declare."""
+    names = []
+    for path in HEADER_PATHS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b((?:da|dcn)_[a-z_]+)\s*\(", text)
+    return names

@@ -15,9 +15,11 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
 SOURCES = [os.path.join(CSRC, f)
-           for f in ("da_forward.hip", "da_backward.hip", "da_pack.hip", "da_api.cpp")]
-HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(CSRC, "da_internal.h"),
-           os.path.join(CSRC, "da_device.h"), os.path.join(CSRC, "da_pack.h")]
+           for f in ("da_forward.hip", "da_backward.hip", "da_pack.hip", "da_api.cpp", "dcn.hip",
+                     "dcn_api.cpp")]
+HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(INCLUDE, "dcn.h")] + [
+    os.path.join(CSRC, f) for f in ("da_internal.h", "da_device.h", "da_pack.h", "dcn_internal.h",
+                                    "host_errors.h")]
 ARCH = "gfx950"
 
 

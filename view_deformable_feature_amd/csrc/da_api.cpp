@@ -14,6 +14,7 @@
 #include "da_internal.h"
 #include "da_pack.h"
 #include "deformagg.h"
+#include "host_errors.h"
 
 namespace {
 
@@ -357,6 +358,24 @@ da_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return DA_OK;
     return fail(DA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+}  // namespace
+
+namespace da {
+
+da_status report_error(da_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+da_status report_hip(hipError_t e, const char* what) { return hip_status(e, what); }
+
+}  // namespace da
+
+namespace {
 
 // The row-ordered backward applies when 4 channels per lane fit the groups
 // (C/G a multiple of 4 with C/G/4 a power of two, at most 1024 channels), there

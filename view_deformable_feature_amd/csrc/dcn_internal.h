@@ -1,0 +1,39 @@
+// Internal launch description of the deformable-convolution kernels (dcn.hip),
+// filled by the host API (dcn_api.cpp).  Not part of the public ABI.
+//
+// Lane layout: a lane covers VEC consecutive channels (16 bytes of input: 4
+// binary32 or 8 16-bit elements, else 1).  The Dv = D / VEC vectors of a group
+// take Lg lanes (the next power of two, at most 64; lanes past Dv idle), the G
+// groups of one output pixel take Lp = min(64, G * Lg) lanes, so a wave holds
+// 64 / Lp pixels, and a lane covers NV = G * Lg / Lp groups of its pixel.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace da {
+
+struct DcnArgs {
+    const void* input;       // [N, H, W, C] of in_dtype
+    const float* om;         // [N, Ho, Wo, G, 3K]
+    void* out;               // [N, Ho, Wo, C] of out_dtype
+    const void* grad_out;    // [N, Ho, Wo, C] of out_dtype
+    float* grad_input;       // [N, H, W, C]
+    float* grad_om;          // [N, Ho, Wo, G, 3K]
+    int64_t n_pix;           // N * Ho * Wo
+    uint32_t in_bytes;       // buffer range of input; also the "outside" offset
+    uint32_t gi_bytes;       // buffer range of grad_input
+    int32_t N, H, W, C, G, D, KH, KW, SH, SW, PH, PW, DH, DW, Ho, Wo, K;
+    int32_t Dv, Lg, log2Lg, Lp, log2Lp;
+    int32_t out_dtype, go_dtype;
+    int32_t out_vec4;        // binary32 out, 16-byte aligned rows: float4 stores
+};
+
+// vec: channels per lane vector (1, 4 or 8); nv: groups per lane (1, 2, 4 or 8)
+hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, hipStream_t stream);
+// grad_input is zero-filled here, then summed into
+hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, int nv,
+                               hipStream_t stream);
+
+}  // namespace da
