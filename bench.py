@@ -179,6 +179,114 @@ def bench_pack(args):
     print(json.dumps(rec), flush=True)
 
 
+def dcn_bytes(wl, out_bytes=4):
+    """(forward, backward) algorithmic bytes of one deformable-convolution call, the
+    DCNv4 notes' worst-case accounting: every (pixel, group, tap) sample reads its
+    four corner vectors of D channels and its offsets and scalar; each output
+    element is written once.  The backward also reads grad_out and writes the
+    input gradient of every corner term and the offset / scalar gradients."""
+    D, e = wl.C // wl.groups, wl.elem_bytes
+    ho, wo = wl.out_hw
+    n_s = wl.samples
+    out_el = wl.N * ho * wo * wl.C
+    b_fwd = n_s * (4 * D * e + 12) + out_el * out_bytes
+    b_bwd = n_s * (4 * D * e + 12 + 4 * D * 4 + 12) + out_el * out_bytes
+    return b_fwd, b_bwd
+
+
+def bench_dcn(args):
+    """Deformable convolution (DCNv3 / DCNv4 operator): forward + backward on the
+    shape the DCNv4 notes time (56x56x128, batch 64, 4 groups by default)."""
+    import torch
+    import view_deformable_feature_amd as vdf
+    from view_deformable_feature_amd import workloads as W
+    wl = W.DCN_WORKLOADS[args.workload]
+    inp = W.make_dcn_inputs(wl)
+    dev = torch.device("cuda:0")
+    x = inp["input"]
+    if x.dtype == np.uint16:
+        x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(x).to(dev)
+    om = torch.from_numpy(inp["offset_mask"]).to(dev)
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.out_dtype]
+    go = torch.from_numpy(inp["grad_out"]).to(dev).to(odt)
+    conf = dict(groups=wl.groups, kernel=wl.kernel, stride=wl.stride, pad=wl.pad,
+                dilation=wl.dilation)
+    out = torch.empty(tuple(go.shape), device=dev, dtype=odt)
+    gi = torch.empty(tuple(x.shape), device=dev, dtype=torch.float32)
+    gom = torch.empty_like(om)
+    nws = vdf.dcn_workspace_size(x, **conf, grad_out_dtype=odt)
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8) if nws else None
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        vdf.dcn_forward(x, om, **conf, out=out)
+        if ev is not None:
+            ev[1].record()
+        vdf.dcn_backward(x, om, go, **conf, grad_input=gi, grad_offset_mask=gom, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    t_step = wall / args.steps
+    b_fwd, b_bwd = dcn_bytes(wl, out.element_size())
+    sc = wl.sample_channels
+
+    def roof(b, t, kernel):
+        a = b / t / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                "algorithmic_bytes": int(b), "avg_launch_us": round(t * 1e6, 2)}
+
+    ho, wo = wl.out_hw
+    rec = {"metric": "deformable convolution: bilinear sample-channels/s, forward + backward",
+           "value": sc / t_step, "unit": "sample-channels/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": ("f32" if wl.dtype == "f32" and args.out_dtype == "f32"
+                     else f"{wl.dtype}-input/{args.out_dtype}-out/f32"),
+           "data": "synthetic",
+           "config": {"workload": f"{wl.name}: N={wl.N}, {wl.H}x{wl.W}x{wl.C}, groups={wl.groups}, "
+                                  f"kernel {wl.kernel[0]}x{wl.kernel[1]}, out {ho}x{wo}",
+                      "sample_channels_per_step": sc, "out_dtype": args.out_dtype},
+           "forward": {"avg_us": t_fwd * 1e6, "value": sc / t_fwd, "unit": "sample-channels/s"},
+           "backward": {"avg_us": t_bwd * 1e6, "value": sc / t_bwd, "unit": "sample-channels/s"},
+           "roofline": roof(b_bwd, t_bwd, "dcn_backward call: fill_zero_kernel, dcn_backward_kernel"),
+           "roofline_forward": roof(b_fwd, t_fwd, "dcn_forward_kernel")}
+    if not args.no_cpu_baseline:
+        import oracle
+        sub = W.dcn_custom(wl.name + "_sample", N=1, H=wl.H, W=wl.W, C=wl.C, groups=wl.groups,
+                           kernel=wl.kernel, stride=wl.stride, pad=wl.pad, dilation=wl.dilation,
+                           dtype=wl.dtype, seed=wl.seed)
+        si = W.make_dcn_inputs(sub)
+        oracle.dcn_out_size(wl.H, wl.W, wl.kernel, wl.stride, wl.pad, wl.dilation)
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.dcn_forward(si["input"], si["offset_mask"], **conf)
+            oracle.dcn_backward(si["input"], si["offset_mask"], si["grad_out"], **conf)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds:
+                break
+        rec["cpu_baseline"] = {"value": sub.sample_channels * reps / el, "unit": "sample-channels/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"one image of {wl.name} (1 of {wl.N}), forward + backward, "
+                                         f"{reps} passes in {el:.1f} s (fp64 C loop, one thread)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,9 +302,10 @@ def main():
                     help="element type of out and grad_out (binary32 arithmetic throughout)")
     ap.add_argument("--deterministic", action="store_true",
                     help="run the backward in its deterministic (64-bit fixed-point) form")
-    ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack"),
+    ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack", "dcn"),
                     help="aggregate: forward + backward step (the headline); pack: level "
-                         "packing and unpacking of the workload's feature maps")
+                         "packing and unpacking of the workload's feature maps; dcn: the "
+                         "deformable convolution (workload dcn_56, dcn_28, dcn_14, dcn_56_f16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -211,6 +320,11 @@ def main():
         return
     if args.op == "pack":
         bench_pack(args)
+        return
+    if args.op == "dcn":
+        if args.workload == "nuscenes_bwd":
+            args.workload = "dcn_56"
+        bench_dcn(args)
         return
 
     import view_deformable_feature_amd as vdf

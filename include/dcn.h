@@ -71,7 +71,10 @@ da_status dcn_forward(const dcn_problem* problem, const void* input, const float
                       void* out, void* stream);
 
 /*
- * dcn_backward_workspace_size -- bytes of device workspace dcn_backward needs.
+ * dcn_backward_workspace_size -- bytes of device workspace dcn_backward needs:
+ * 8448 + 16 * N*Ho*Wo*G*K (0 when there is no output pixel) -- control words, a
+ * reduction buffer, and room to list every (sample, corner) whose offset carries it
+ * more than 4 pixels past its tile.
  */
 da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t* bytes);
 
@@ -86,8 +89,14 @@ da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t* bytes)
  *   workspace         device scratch of dcn_backward_workspace_size() bytes, 256-byte
  *                     aligned (may be NULL when that is 0); contents on entry do not
  *                     matter.
- * grad_offset_mask is deterministic; grad_input adds its terms in an order that may
- * vary from run to run.  Same errors as dcn_forward, plus a missing or small workspace.
+ * The input gradient is summed tile by tile in LDS by the workgroup that owns the
+ * tile, in 64-bit fixed point (each term rounded once to a multiple of 2^-E, E from
+ * max|grad_out| * max|m| so that no sum can overflow: about 2^-49 of that bound as
+ * resolution), and stored once; only corners carried more than 4 pixels past their
+ * tile are added afterwards with binary32 atomics.  grad_offset_mask is
+ * deterministic, and so is grad_input when no corner is that far.  Same errors as dcn_forward,
+ * plus DA_ERR_UNSUPPORTED for 2^30 samples (N*Ho*Wo*G*K) or more and
+ * DA_ERR_INVALID_ARG for a missing, misaligned or small workspace.
  */
 da_status dcn_backward(const dcn_problem* problem, const void* input, const float* offset_mask,
                        const void* grad_out, float* grad_input, float* grad_offset_mask,

@@ -9,13 +9,13 @@
 //
 // Design: the same gather building blocks as the aggregation (bounds-checked
 // buffer loads whose out-of-range offset reads zero, 16-byte vectors over
-// contiguous channels, DPP group sums).  A lane covers 16 bytes of one group's
-// channels of one output pixel; the group's lanes share the stencil.  The
-// backward recomputes the corner values for the offset and scalar gradients
-// and scatters the input gradient with binary32 buffer atomics.  Blocks are
-// laid out so that each XCD (workgroup i runs on XCD i mod 8) walks one
-// contiguous band of output pixels, keeping the 3 x 3 neighbourhoods it reads
-// in its own L2.
+// contiguous channels, DPP group sums).  Forward: a lane covers 16 bytes of one
+// group's channels of one output pixel; blocks are laid out so that each XCD
+// (workgroup i runs on XCD i mod 8) walks one contiguous band of output pixels,
+// keeping the neighbourhoods it reads in its own L2.  Backward: workgroups own
+// input tiles and sum their gradient in LDS (see below), so the scatter that the
+// page's design does with one global atomic per term becomes LDS additions and
+// one store per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -162,123 +162,468 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_forward_kernel(DcnArgs a) {
         if (L.valid[i]) store_out_vec<VEC>(a, L.pix * a.C + L.c0[i], acc[i]);
 }
 
-template <typename T, int VEC, int NV>
-__global__ void __launch_bounds__(kDcnThreads) dcn_backward_kernel(DcnArgs a) {
-    DcnLane<VEC, NV> L;
-    if (!dcn_lane(a, L)) return;     // whole pixels only: a group's lanes stay together
-    constexpr int kElem = (int)sizeof(T);
+// ------------------------------------------------------------------------------------
+// backward by input tiles
+// ------------------------------------------------------------------------------------
+// Workgroup (n, ty, tx, g) owns the gradient of input pixels [Iy0, Iy0 + TY) x
+// [Ix0, Ix0 + TX) (clipped to the image) in channel group g, summed in LDS and
+// stored once.  The LDS sums are 64-bit fixed point: binary32 atomic addition in
+// LDS runs several times slower than integer addition on this part, and exact
+// integer sums also make each tile's result independent of the order of its
+// terms.  A sample (output pixel, group, tap) has grid point (gy, gx) =
+// (ho*SH - PH + i*DH, wo*SW - PW + j*DW); its home is the tile holding that point
+// clamped into the image.  The home workgroup forms the sample's offset and scalar
+// gradients and adds the corners that fall in its own tile.  A corner in another
+// tile is added by that tile's workgroup when the grid point lies in the tile's
+// window -- rows [Iy0 - M - 1, Iy0 + TY - 1 + M], columns alike, which
+// holds every corner of a sample whose offsets are at most M -- through its ring
+// loop; otherwise the home appends (sample, corner) to the far list, added by
+// atomics after every tile is stored.
+
+struct DcnRec {
+    int32_t pix;        // output pixel
+    int32_t k;          // tap
+    float m;            // modulation scalar
+    float ly, lx;       // fractions over the low corner
+    int32_t y0, x0;     // low corner (meaningful when inside)
+    uint32_t flags;     // bit 0 inside; bit 1 + q: corner q in the image; bit 5 + q: in this
+                        // tile; bit 9 + q: far (no tile's ring reaches it; home samples only)
+};
+static_assert(sizeof(DcnRec) == kDcnRecBytes, "record size");
+
+// Output indices o in [0, O) whose grid coordinate o*S - P + off lies in [lo, hi].
+__device__ __forceinline__ void out_range(int lo, int hi, int S, int P, int off, int O, int& o_lo,
+                                          int& o_hi) {
+    const int a = lo + P - off, b = hi + P - off;
+    o_lo = a <= 0 ? 0 : (a + S - 1) / S;
+    o_hi = b < 0 ? -1 : min(b / S, O - 1);
+}
+
+struct TileCtx {
+    int n, g, Iy0, Ix0, Iy1, Ix1;   // owned tile [Iy0, Iy1) x [Ix0, Ix1)
+};
+
+// Phase A of one candidate sample: its stencil record (for a home sample, with
+// the corners no other tile's ring reaches flagged far).
+__device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t, int ho, int wo, int k,
+                                             bool home) {
+#pragma clang fp contract(off)
+    DcnRec r;
+    const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+    const int gy = ho * a.SH - a.PH + ki * a.DH, gx = wo * a.SW - a.PW + kj * a.DW;
+    r.pix = (t.n * a.Ho + ho) * a.Wo + wo;
+    r.k = k;
+    const float* om = a.om + ((int64_t)r.pix * a.G + t.g) * (3 * a.K);
+    const float dx = om[2 * k], dy = om[2 * k + 1];
+    r.m = om[2 * a.K + k];
+    const float y = (float)gy + dy, x = (float)gx + dx;
+    const bool inside = y > -1.0f && x > -1.0f && y < (float)a.H && x < (float)a.W;
+    const float yf = inside ? floorf(y) : 0.0f, xf = inside ? floorf(x) : 0.0f;
+    r.ly = inside ? y - yf : 0.0f;
+    r.lx = inside ? x - xf : 0.0f;
+    r.y0 = (int)yf;
+    r.x0 = (int)xf;
+    uint32_t f = inside ? 1u : 0u;
+    if (inside) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cy = r.y0 + (q >> 1), cx = r.x0 + (q & 1);
+            if (cy < 0 || cy >= a.H || cx < 0 || cx >= a.W) continue;
+            f |= 1u << (1 + q);
+            if (cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1) {
+                f |= 1u << (5 + q);
+            } else if (home) {
+                // the corner's tile reaches this sample through its ring only when
+                // the grid point lies in that tile's window
+                const int oy = cy / a.TY * a.TY, ox = cx / a.TX * a.TX;
+                const bool reach = gy >= oy - a.M - 1 && gy <= oy + a.TY - 1 + a.M &&
+                                   gx >= ox - a.M - 1 && gx <= ox + a.TX - 1 + a.M;
+                if (!reach) f |= 1u << (9 + q);
+            }
+        }
+    }
+    r.flags = f;
+    return r;
+}
+
+// grad_out[i .. i + VEC) of the run-time type go_dtype (16-byte loads for binary32
+// when the tensor allows them)
+template <int VEC>
+__device__ __forceinline__ void load_go(const DcnArgs& a, int64_t i, float (&go)[VEC]) {
+    if (VEC == 4 && a.go_dtype == kF32 && a.go_vec4) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
+        go[0] = v.x;
+        go[1] = v.y;
+        go[2] = v.z;
+        go[3] = v.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) go[e] = load_elem(a.grad_out, i + e, a.go_dtype);
+    }
+}
+
+__device__ __forceinline__ void corner_weights(const DcnRec& r, float (&cw)[4]) {
+#pragma clang fp contract(off)
+    const float hy = 1.0f - r.ly, hx = 1.0f - r.lx;
+    const bool in = r.flags & 1u;
+    cw[0] = in ? hy * hx : 0.0f;
+    cw[1] = in ? hy * r.lx : 0.0f;
+    cw[2] = in ? r.ly * hx : 0.0f;
+    cw[3] = in ? r.ly * r.lx : 0.0f;
+}
+
+// Scale of the fixed-point tile sums.  Every term is cw * m * grad_out with
+// cw <= 1, so |term| <= B = max|m| * max|grad_out|, and one tile sum takes at
+// most 2^log2_terms terms: with E = 61 - (exponent of B) - log2_terms every sum
+// stays below 2^61 and every term below 2^51 (log2_terms >= 10).  Rounding a term
+// to RNE(t 2^E): adding 1.5 * 2^52 in binary64 puts t 2^E on the integer grid of
+// the binade [2^52, 2^53), whose encoding is the integer plus a constant.
+__global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
+    __shared__ uint32_t red[2][kDcnWaves];
+    __shared__ uint32_t is_last;
+    const int64_t stride = (int64_t)gridDim.x * kDcnThreads;
+    const int64_t i0 = (int64_t)blockIdx.x * kDcnThreads + threadIdx.x;
+    uint32_t mg = 0, mm = 0;
+    const int64_t n_go = a.n_pix * a.C;
+    for (int64_t i = i0; i < n_go; i += stride)
+        mg = max(mg, __float_as_uint(fabsf(load_elem(a.grad_out, i, a.go_dtype))));
+    const int64_t n_m = a.n_pix * a.G * a.K;
+    for (int64_t i = i0; i < n_m; i += stride) {
+        const int64_t rec = i / a.K, k = i - (i / a.K) * a.K;
+        mm = max(mm, __float_as_uint(fabsf(a.om[rec * (3 * a.K) + 2 * a.K + k])));
+    }
+    for (int d = 1; d < kWave; d <<= 1) {
+        mg = max(mg, (uint32_t)__shfl_xor((int)mg, d, kWave));
+        mm = max(mm, (uint32_t)__shfl_xor((int)mm, d, kWave));
+    }
+    if (threadIdx.x % kWave == 0) {
+        red[0][threadIdx.x / kWave] = mg;
+        red[1][threadIdx.x / kWave] = mm;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kDcnWaves; ++w) {
+            mg = max(mg, red[0][w]);
+            mm = max(mm, red[1][w]);
+        }
+        a.part[2 * blockIdx.x] = mg;
+        a.part[2 * blockIdx.x + 1] = mm;
+        __threadfence();
+        is_last = atomicAdd(a.ctrl + kDcnCtrlTicket, 1u) == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    mg = 0;
+    mm = 0;
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kDcnThreads) {
+        mg = max(mg, a.part[2 * b]);
+        mm = max(mm, a.part[2 * b + 1]);
+    }
+    for (int d = 1; d < kWave; d <<= 1) {
+        mg = max(mg, (uint32_t)__shfl_xor((int)mg, d, kWave));
+        mm = max(mm, (uint32_t)__shfl_xor((int)mm, d, kWave));
+    }
+    __syncthreads();
+    if (threadIdx.x % kWave == 0) {
+        red[0][threadIdx.x / kWave] = mg;
+        red[1][threadIdx.x / kWave] = mm;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kDcnWaves; ++w) {
+            mg = max(mg, red[0][w]);
+            mm = max(mm, red[1][w]);
+        }
+        a.ctrl[kDcnCtrlMaxGo] = mg;
+        a.ctrl[kDcnCtrlMaxM] = mm;
+    }
+}
+
+__device__ __forceinline__ int dcn_fixed_exponent(const DcnArgs& a) {
+    const double b = (double)__uint_as_float(a.ctrl[kDcnCtrlMaxGo]) *
+                     (double)__uint_as_float(a.ctrl[kDcnCtrlMaxM]);
+    if (!(b > 0.0) || !(b < 1e300)) return 0;
+    int e;
+    frexp(b, &e);                       // b < 2^e
+    return 61 - e - a.log2_terms;
+}
+constexpr double kFixMagicD = 6755399441055744.0;             // 1.5 * 2^52
+__device__ __forceinline__ unsigned long long fixed_term(float t, double scale) {
+    return (unsigned long long)(__double_as_longlong(fma((double)t, scale, kFixMagicD)) -
+                                __double_as_longlong(kFixMagicD));
+}
+
+// Lanes: a group of bLg lanes takes one sample at a time; lane jj covers the NVL
+// vectors jj, jj + bLg, ... of VEC channels of the group.  Every lane of the
+// group forms the (cheap) stencil itself, so the waves never wait for one another
+// inside the loops: many samples' loads are in flight at once.
+template <typename T, int VEC, int NVL>
+__global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int TY = a.TY, TX = a.TX;
+    unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
+    const int tid = threadIdx.x;
+    const int E = dcn_fixed_exponent(a);
+    const double scale = ldexp(1.0, E);
+
+    // block -> (n, ty, tx, g), group fastest, neighbouring tiles on one XCD
+    uint32_t lb = xcd_order(blockIdx.x, gridDim.x);
+    TileCtx t;
+    t.g = (int)(lb % (uint32_t)a.G);
+    lb /= (uint32_t)a.G;
+    const int tx = (int)(lb % (uint32_t)a.tiles_x);
+    lb /= (uint32_t)a.tiles_x;
+    const int ty = (int)(lb % (uint32_t)a.tiles_y);
+    t.n = (int)(lb / (uint32_t)a.tiles_y);
+    t.Iy0 = ty * TY;
+    t.Ix0 = tx * TX;
+    t.Iy1 = min(t.Iy0 + TY, a.H);
+    t.Ix1 = min(t.Ix0 + TX, a.W);
+
+    for (int i = tid; i < TY * TX * a.Dp; i += kDcnThreads) acc[i] = 0ull;
+    __syncthreads();
+
+    const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnThreads >> a.blog2Lg;
+    int cl[NVL];             // channel offsets inside the group
+    bool vv[NVL];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+        const int vi = jj + a.bLg * u;
+        vv[u] = vi < a.Dv;
+        cl[u] = vv[u] ? vi * VEC : 0;
+    }
+    const int gD = t.g * a.D;
     const __amdgpu_buffer_rsrc_t r_in = make_rsrc(a.input, a.in_bytes);
-    const __amdgpu_buffer_rsrc_t r_gi = make_rsrc(a.grad_input, a.gi_bytes);
-    const int K3 = 3 * a.K;
-    float go[NV][VEC];
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            go[i][e] = L.valid[i] ? load_elem(a.grad_out, L.pix * a.C + L.c0[i] + e, a.go_dtype) : 0.0f;
+    constexpr int kElem = (int)sizeof(T);
+    const bool last = jj == a.bLg - 1;
+
+    // ---- home samples: offset / scalar gradients, corners in this tile ----
     for (int k = 0; k < a.K; ++k) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
-        const int gy = L.ho * a.SH - a.PH + ki * a.DH;
-        const int gx = L.wo * a.SW - a.PW + kj * a.DW;
+        int h0, h1, w0, w1;
+        out_range(t.Iy0 == 0 ? -(1 << 28) : t.Iy0, t.Iy1 == a.H ? (1 << 28) : t.Iy1 - 1, a.SH, a.PH,
+                  ki * a.DH, a.Ho, h0, h1);
+        out_range(t.Ix0 == 0 ? -(1 << 28) : t.Ix0, t.Ix1 == a.W ? (1 << 28) : t.Ix1 - 1, a.SW, a.PW,
+                  kj * a.DW, a.Wo, w0, w1);
+        const int nw = w1 - w0 + 1;
+        const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+        for (int idx = slot; idx < nh; idx += spp) {
+            const DcnRec R = dcn_record(a, t, h0 + idx / nw, w0 + idx % nw, k, true);
+            if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
+                const uint32_t sid = ((uint32_t)R.pix * (uint32_t)a.G + (uint32_t)t.g) *
+                                         (uint32_t)a.K + (uint32_t)k;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            // every lane of the group, idle ones too, takes the group's own stencil:
-            // the group's sums end in its last lane, which may hold no channels
-            const int64_t rec = (L.pix * a.G + L.gq[i]) * K3;
-            const float* om = a.om + rec;
-            const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
-            // gradient offsets: the same corners as the input, in binary32 elements
-            const DcnStencil st = dcn_stencil(a, L.n, gy, gx, dy, dx, L.c0[i], kElem);
-            float v[4][VEC];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                VecLoad<T, VEC>::run(r_in, L.valid[i] ? st.off[q] : a.in_bytes, 0u, v[q]);
-            const float hy = 1.0f - st.ly, hx = 1.0f - st.lx;
+                for (int q = 0; q < 4; ++q)
+                    if (R.flags >> (9 + q) & 1u) a.fb[atomicAdd(a.ctrl + kDcnCtrlFar, 1u)] = sid * 4u + q;
+            }
+            float cw[4];
+            corner_weights(R, cw);
+            const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
+            const int64_t gbase = (int64_t)R.pix * a.C + gD;
+            const int64_t ibase = ((int64_t)(t.n * a.H + R.y0) * a.W + R.x0) * a.C + gD;
             float pm = 0.0f, px = 0.0f, py = 0.0f;
+            float go[NVL][VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float val = st.cw[0] * v[0][e] + st.cw[1] * v[1][e] + st.cw[2] * v[2][e] +
-                                  st.cw[3] * v[3][e];
-                const float ddx = hy * (v[1][e] - v[0][e]) + st.ly * (v[3][e] - v[2][e]);
-                const float ddy = hx * (v[2][e] - v[0][e]) + st.lx * (v[3][e] - v[1][e]);
-                pm += go[i][e] * val;
-                px += go[i][e] * ddx;
-                py += go[i][e] * ddy;
-            }
-            pm = group_sum(pm, a.Lg);
-            px = group_sum(px, a.Lg);
-            py = group_sum(py, a.Lg);
-            if (L.last[i] && L.g[i] < a.G) {     // the group's sums sit in its last lane
-                const bool live = st.inside;
-                a.grad_om[rec + 2 * k] = live ? m * px : 0.0f;
-                a.grad_om[rec + 2 * k + 1] = live ? m * py : 0.0f;
-                a.grad_om[rec + 2 * a.K + k] = live ? pm : 0.0f;
-            }
-            // input gradient: corner q gets cw_q * m * grad_out (dropped outside)
-            if (L.valid[i]) {
+            for (int u = 0; u < NVL; ++u) {
+                load_go<VEC>(a, gbase + cl[u], go[u]);
+                float v[4][VEC];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t goff = st.off[q] == a.in_bytes
-                                              ? a.gi_bytes
-                                              : st.off[q] / (uint32_t)kElem * 4u;
-                    const float w = st.cw[q] * m;
+                    const uint32_t off =
+                        (R.flags >> (1 + q) & 1u) && vv[u]
+                            ? (uint32_t)(ibase + ((q >> 1) * a.W + (q & 1)) * a.C + cl[u]) *
+                                  (uint32_t)kElem
+                            : a.in_bytes;
+                    VecLoad<T, VEC>::run(r_in, off, 0u, v[q]);
+                }
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w * go[i][e], r_gi,
-                                                                        goff + 4u * e, 0, 0);
+                for (int e = 0; e < VEC; ++e) {
+                    const float gv = vv[u] ? go[u][e] : 0.0f;
+                    go[u][e] = gv;
+                    const float val = cw[0] * v[0][e] + cw[1] * v[1][e] + cw[2] * v[2][e] +
+                                      cw[3] * v[3][e];
+                    const float ddx = hy * (v[1][e] - v[0][e]) + R.ly * (v[3][e] - v[2][e]);
+                    const float ddy = hx * (v[2][e] - v[0][e]) + R.lx * (v[3][e] - v[1][e]);
+                    pm += gv * val;
+                    px += gv * ddx;
+                    py += gv * ddy;
                 }
             }
+            pm = group_sum(pm, a.bLg);
+            px = group_sum(px, a.bLg);
+            py = group_sum(py, a.bLg);
+            if (last) {
+                const bool live = R.flags & 1u;
+                float* gom = a.grad_om + ((int64_t)R.pix * a.G + t.g) * (3 * a.K);
+                gom[2 * k] = live ? R.m * px : 0.0f;
+                gom[2 * k + 1] = live ? R.m * py : 0.0f;
+                gom[2 * a.K + k] = live ? pm : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (!(R.flags >> (5 + q) & 1u)) continue;
+                const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
+                const float w = cw[q] * R.m;
+#pragma unroll
+                for (int u = 0; u < NVL; ++u) {
+                    if (!vv[u]) continue;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(w * go[u][e], scale));
+                }
+            }
+        }
+    }
+
+    // ---- ring: other tiles' samples whose grid point lies in this tile's window ----
+    for (int k = 0; k < a.K; ++k) {
+        const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+        int h0, h1, w0, w1;
+        out_range(t.Iy0 - a.M - 1, t.Iy0 + TY - 1 + a.M, a.SH, a.PH, ki * a.DH, a.Ho, h0, h1);
+        out_range(t.Ix0 - a.M - 1, t.Ix0 + TX - 1 + a.M, a.SW, a.PW, kj * a.DW, a.Wo, w0, w1);
+        const int nw = w1 - w0 + 1;
+        const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+        for (int idx = slot; idx < nh; idx += spp) {
+            const int ho = h0 + idx / nw, wo = w0 + idx % nw;
+            const int gy = ho * a.SH - a.PH + ki * a.DH, gx = wo * a.SW - a.PW + kj * a.DW;
+            const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
+            if (cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1) continue;   // home
+            const DcnRec R = dcn_record(a, t, ho, wo, k, false);
+            if (!(R.flags >> 5)) continue;
+            float cw[4];
+            corner_weights(R, cw);
+            const int64_t gbase = (int64_t)R.pix * a.C + gD;
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                if (!vv[u]) continue;
+                float go[VEC];
+                load_go<VEC>(a, gbase + cl[u], go);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (!(R.flags >> (5 + q) & 1u)) continue;
+                    const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
+                    const float w = cw[q] * R.m;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(w * go[e], scale));
+                }
+            }
+        }
+    }
+
+    // ---- store the tile ----
+    __syncthreads();
+    const double inv = ldexp(1.0, -E);
+    const int cols = t.Ix1 - t.Ix0, npx = (t.Iy1 - t.Iy0) * cols;
+    for (int i = tid; i < npx * a.D; i += kDcnThreads) {
+        const int p = i / a.D, c = i - (i / a.D) * a.D;
+        const int py = p / cols, px = p - (p / cols) * cols;
+        a.grad_input[(((int64_t)t.n * a.H + t.Iy0 + py) * a.W + t.Ix0 + px) * a.C + gD + c] =
+            (float)((double)(long long)acc[(py * TX + px) * a.Dp + c] * inv);
+    }
+}
+
+// The far list: corner q of sample s gets cw_q * m * grad_out by atomics (after every
+// tile has been stored).  Lg lanes per entry, a grid-stride loop over the entries.
+template <typename T, int VEC, int NVL>
+__global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
+#pragma clang fp contract(off)
+    const uint32_t count = a.ctrl[kDcnCtrlFar];
+    const int jj = threadIdx.x & (a.bLg - 1);
+    const __amdgpu_buffer_rsrc_t r_gi = make_rsrc(a.grad_input, a.gi_bytes);
+    const uint32_t per_block = kDcnThreads >> a.blog2Lg;
+    for (uint32_t e = blockIdx.x * per_block + (threadIdx.x >> a.blog2Lg); e < count;
+         e += gridDim.x * per_block) {
+        const uint32_t ent = a.fb[e];
+        const int q = (int)(ent & 3u);
+        uint32_t s = ent >> 2;
+        const int k = (int)(s % (uint32_t)a.K);
+        s /= (uint32_t)a.K;
+        const int g = (int)(s % (uint32_t)a.G);
+        const int pix = (int)(s / (uint32_t)a.G);
+        const int wo = pix % a.Wo, ho = (pix / a.Wo) % a.Ho, n = pix / (a.Wo * a.Ho);
+        TileCtx t{n, g, 0, 0, 0, 0};            // empty tile: no corner counts as owned
+        const DcnRec R = dcn_record(a, t, ho, wo, k, false);
+        float cw[4];
+        corner_weights(R, cw);
+        const float w = cw[q] * R.m;
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            const int vi = jj + a.bLg * u;
+            if (vi >= a.Dv) continue;
+            const int c0 = g * a.D + vi * VEC;
+            const uint32_t goff =
+                (uint32_t)(((int64_t)(n * a.H + R.y0 + (q >> 1)) * a.W + R.x0 + (q & 1)) * a.C + c0) * 4u;
+            float go[VEC];
+            load_go<VEC>(a, (int64_t)pix * a.C + c0, go);
+#pragma unroll
+            for (int e2 = 0; e2 < VEC; ++e2)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w * go[e2], r_gi, goff + 4u * e2, 0, 0);
         }
     }
 }
 
 template <typename T, int VEC, int NV>
-hipError_t dcn_launch(const DcnArgs& a, bool backward, hipStream_t st) {
+hipError_t dcn_fwd_launch(const DcnArgs& a, hipStream_t st) {
     const int64_t ppw = kWave / a.Lp;
     const int64_t blocks = (a.n_pix + ppw * kDcnWaves - 1) / (ppw * kDcnWaves);
-    if (backward)
-        hipLaunchKernelGGL((dcn_backward_kernel<T, VEC, NV>), dim3((unsigned)blocks),
-                           dim3(kDcnThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((dcn_forward_kernel<T, VEC, NV>), dim3((unsigned)blocks),
-                           dim3(kDcnThreads), 0, st, a);
+    hipLaunchKernelGGL((dcn_forward_kernel<T, VEC, NV>), dim3((unsigned)blocks), dim3(kDcnThreads),
+                       0, st, a);
     return hipGetLastError();
 }
 
 template <typename T, int VEC>
-hipError_t dcn_dispatch_nv(const DcnArgs& a, int nv, bool backward, hipStream_t st) {
+hipError_t dcn_fwd_dispatch_nv(const DcnArgs& a, int nv, hipStream_t st) {
     switch (nv) {
-        case 1: return dcn_launch<T, VEC, 1>(a, backward, st);
-        case 2: return dcn_launch<T, VEC, 2>(a, backward, st);
-        case 4: return dcn_launch<T, VEC, 4>(a, backward, st);
-        case 8: return dcn_launch<T, VEC, 8>(a, backward, st);
+        case 1: return dcn_fwd_launch<T, VEC, 1>(a, st);
+        case 2: return dcn_fwd_launch<T, VEC, 2>(a, st);
+        case 4: return dcn_fwd_launch<T, VEC, 4>(a, st);
+        case 8: return dcn_fwd_launch<T, VEC, 8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t dcn_dispatch(const DcnArgs& a, int in_dtype, int vec, int nv, bool backward,
-                        hipStream_t st) {
-    return with_elem(in_dtype, [&](auto t) {
-        using T = decltype(t);
-        constexpr int V = sizeof(T) == 2 ? 8 : 4;
-        return vec == V ? dcn_dispatch_nv<T, V>(a, nv, backward, st)
-                        : dcn_dispatch_nv<T, 1>(a, nv, backward, st);
-    });
+template <typename T, int VEC, int NVL>
+hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
+    const unsigned blocks = (unsigned)((int64_t)a.N * a.tiles_y * a.tiles_x * a.G);
+    hipLaunchKernelGGL(dcn_bound_kernel, dim3(kDcnBoundBlocks), dim3(kDcnThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL>), dim3(blocks), dim3(kDcnThreads), lds, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dcn_far_kernel<T, VEC, NVL>), dim3(1024), dim3(kDcnThreads), 0, st, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, hipStream_t stream) {
     if (a.n_pix == 0) return hipSuccess;
-    return dcn_dispatch(a, in_dtype, vec, nv, false, stream);
+    return with_elem(in_dtype, [&](auto t) {
+        using T = decltype(t);
+        constexpr int V = sizeof(T) == 2 ? 8 : 4;
+        return vec == V ? dcn_fwd_dispatch_nv<T, V>(a, nv, stream)
+                        : dcn_fwd_dispatch_nv<T, 1>(a, nv, stream);
+    });
 }
 
-hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, int nv,
+hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream) {
-    const hipError_t e =
-        launch_fill_zero(a.grad_input, (int64_t)a.N * a.H * a.W * a.C, stream);
-    if (e != hipSuccess || a.n_pix == 0) return e;
-    return dcn_dispatch(a, in_dtype, vec, nv, true, stream);
+    if (a.n_pix == 0)       // no output pixel: the input gradient is zero
+        return launch_fill_zero(a.grad_input, (int64_t)a.N * a.H * a.W * a.C, stream);
+    const hipError_t e = launch_fill_zero(a.ctrl, 4, stream);
+    if (e != hipSuccess) return e;
+    return with_elem(in_dtype, [&](auto t) {
+        using T = decltype(t);
+        constexpr int V = sizeof(T) == 2 ? 8 : 4;
+        if (vec == V)
+            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2>(a, lds_bytes, stream)
+                               : dcn_bwd_launch<T, V, 1>(a, lds_bytes, stream);
+        return a.bNVL == 2 ? dcn_bwd_launch<T, 1, 2>(a, lds_bytes, stream)
+                           : dcn_bwd_launch<T, 1, 1>(a, lds_bytes, stream);
+    });
 }
 
 }  // namespace da

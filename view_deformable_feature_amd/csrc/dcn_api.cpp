@@ -35,7 +35,19 @@ int log2i(int x) {
 struct DcnPlan {
     da::DcnArgs a;
     int vec, nv;
+    size_t lds_bytes;    // backward tile kernel
 };
+
+constexpr int kDcnMargin = 4;                 // offsets up to 4 px reach a tile through its ring
+constexpr size_t kDcnTileLds = 48 * 1024;     // LDS for one tile's gradient sums
+
+// Workspace: control words, the bound kernel's block maxima, then the far list
+// (one 32-bit entry per (sample, corner)).
+constexpr uint64_t kDcnPartOffset = 256;
+constexpr uint64_t kDcnFarOffset = kDcnPartOffset + 8 * da::kDcnBoundBlocks;
+uint64_t dcn_workspace_bytes(int64_t n_samples) {
+    return n_samples == 0 ? 0 : kDcnFarOffset + (uint64_t)n_samples * 16;
+}
 
 // Sizes, types and the output extent; fills the size fields of a.
 da_status check_problem(const dcn_problem* p, int64_t& ho, int64_t& wo) {
@@ -87,6 +99,8 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
                             (unsigned long long)in_bytes);
     const int64_t n_pix = p->batch * ho * wo;
     if (n_pix >= (int64_t(1) << 31)) return report_error(DA_ERR_UNSUPPORTED, "2^31 output pixels or more");
+    if (n_pix * p->groups * p->kernel_h * p->kernel_w >= (int64_t(1) << 30))
+        return report_error(DA_ERR_UNSUPPORTED, "2^30 samples (pixel, group, tap) or more");
     const int64_t C = p->channels, G = p->groups, D = C / G;
     // 16 bytes of channels per lane where the groups and the pointer allow it
     const int wide = 16 / elem;
@@ -131,6 +145,28 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
     a.log2Lp = log2i(lp);
     a.out_dtype = p->out_dtype;
     a.go_dtype = p->out_dtype;
+    // backward tiles: halve 32 x 32 (rows first) until the 64-bit sums fit the LDS
+    // budget; the pixel stride D + 1 words keeps neighbouring pixels' channels in
+    // different banks
+    a.Dp = (int32_t)(D + 1);
+    int ty = 32, tx = 32;
+    while ((ty > 1 || tx > 1) && (size_t)ty * tx * a.Dp * 8 > kDcnTileLds) {
+        if (ty >= tx && ty > 1) ty >>= 1;
+        else tx >>= 1;
+    }
+    a.TY = ty;
+    a.TX = tx;
+    a.M = kDcnMargin;
+    a.tiles_y = (int32_t)((p->height + ty - 1) / ty);
+    a.tiles_x = (int32_t)((p->width + tx - 1) / tx);
+    plan.lds_bytes = (size_t)ty * tx * a.Dp * 8;
+    // at most every sample of one (image, group) plane adds to one tile sum
+    a.log2_terms = std::max(10, log2i((int)std::min<int64_t>(ho * wo * a.K, 1 << 30)) + 1);
+    // backward: two vectors per lane where the group has them (fewer lanes repeat
+    // each sample's stencil)
+    a.bNVL = dv >= 2 ? 2 : 1;
+    a.bLg = next_pow2((dv + a.bNVL - 1) / a.bNVL);
+    a.blog2Lg = log2i(a.bLg);
     plan.vec = vec;
     plan.nv = nv;
     return DA_OK;
@@ -176,15 +212,13 @@ da_status dcn_backward_workspace_size(const dcn_problem* p, size_t* bytes) {
     int64_t ho = 0, wo = 0;
     const da_status st = check_problem(p, ho, wo);
     if (st != DA_OK) return st;
-    *bytes = 0;
+    *bytes = (size_t)dcn_workspace_bytes(p->batch * ho * wo * p->groups * p->kernel_h * p->kernel_w);
     return DA_OK;
 }
 
 da_status dcn_backward(const dcn_problem* p, const void* input, const float* offset_mask,
                        const void* grad_out, float* grad_input, float* grad_offset_mask,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     DcnPlan plan;
     da_status st = plan_dcn(p, input, plan);
     if (st != DA_OK) return st;
@@ -201,10 +235,24 @@ da_status dcn_backward(const dcn_problem* p, const void* input, const float* off
     a.grad_out = grad_out;
     a.grad_input = grad_input;
     a.grad_om = grad_offset_mask;
+    a.go_vec4 = p->out_dtype == DA_F32 && plan.vec == 4 && aligned(grad_out, 16);
     if (p->batch == 0) return DA_OK;
-    return da::report_hip(
-        da::launch_dcn_backward(a, p->in_dtype, plan.vec, plan.nv, static_cast<hipStream_t>(stream)),
-        "dcn backward launch");
+    const uint64_t need = dcn_workspace_bytes(a.n_pix * a.G * a.K);
+    if (need) {
+        if (!workspace) return report_error(DA_ERR_INVALID_ARG, "workspace is NULL");
+        if (!aligned(workspace, 256))
+            return report_error(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return report_error(DA_ERR_INVALID_ARG, "workspace has %zu bytes, %llu needed",
+                                workspace_bytes, (unsigned long long)need);
+        unsigned char* base = static_cast<unsigned char*>(workspace);
+        a.ctrl = reinterpret_cast<uint32_t*>(base);
+        a.part = reinterpret_cast<uint32_t*>(base + kDcnPartOffset);
+        a.fb = reinterpret_cast<uint32_t*>(base + kDcnFarOffset);
+    }
+    return da::report_hip(da::launch_dcn_backward(a, p->in_dtype, plan.vec, plan.lds_bytes,
+                                                  static_cast<hipStream_t>(stream)),
+                          "dcn backward launch");
 }
 
 }  // extern "C"

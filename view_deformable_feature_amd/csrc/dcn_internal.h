@@ -28,12 +28,34 @@ struct DcnArgs {
     int32_t Dv, Lg, log2Lg, Lp, log2Lp;
     int32_t out_dtype, go_dtype;
     int32_t out_vec4;        // binary32 out, 16-byte aligned rows: float4 stores
+    int32_t go_vec4;         // binary32 grad_out, 16-byte aligned rows: float4 loads
+    // Backward by input tiles: workgroup (n, tile, group) owns TY x TX input pixels
+    // of one group and sums their gradient in LDS as 64-bit fixed point (pixel
+    // stride Dp = D + 1 words).  Samples whose grid point lies within M + 1 pixels
+    // of a tile reach it through its ring loop; corners farther than that are
+    // listed in fb (sample * 4 + corner) and added afterwards with atomics.
+    int32_t TY, TX, M, tiles_y, tiles_x, Dp;
+    int32_t bLg, blog2Lg, bNVL;   // backward lanes: bLg lanes per sample, bNVL vectors per lane
+    uint32_t* ctrl;          // workspace control words (zeroed first): kDcnCtrl*
+    uint32_t* part;          // workspace: [kDcnBoundBlocks][2] block maxima
+    uint32_t* fb;            // workspace: [4 * N * Ho * Wo * G * K]
+    int32_t log2_terms;      // ceil(log2(most terms one tile sum can take))
 };
+
+// Workspace control words
+constexpr int kDcnCtrlFar = 0;      // entries in fb
+constexpr int kDcnCtrlMaxGo = 1;    // max |grad_out| (binary32 bits)
+constexpr int kDcnCtrlMaxM = 2;     // max |m|
+constexpr int kDcnCtrlTicket = 3;   // bound blocks done
+constexpr int kDcnBoundBlocks = 1024;
 
 // vec: channels per lane vector (1, 4 or 8); nv: groups per lane (1, 2, 4 or 8)
 hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, hipStream_t stream);
-// grad_input is zero-filled here, then summed into
-hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, int nv,
+// Backward: the bound of the fixed-point terms, the tile kernel (grad_offset_mask,
+// and grad_input stored tile by tile), then the far corners by atomics.
+// lds_bytes: the tile kernel's dynamic LDS.
+hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream);
+constexpr int kDcnRecBytes = 32;   // one sample's stencil record
 
 }  // namespace da
