@@ -285,12 +285,37 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
     const int64_t i0 = (int64_t)blockIdx.x * kDcnThreads + threadIdx.x;
     uint32_t mg = 0, mm = 0;
     const int64_t n_go = a.n_pix * a.C;
-    for (int64_t i = i0; i < n_go; i += stride)
-        mg = max(mg, __float_as_uint(fabsf(load_elem(a.grad_out, i, a.go_dtype))));
-    const int64_t n_m = a.n_pix * a.G * a.K;
-    for (int64_t i = i0; i < n_m; i += stride) {
-        const int64_t rec = i / a.K, k = i - (i / a.K) * a.K;
-        mm = max(mm, __float_as_uint(fabsf(a.om[rec * (3 * a.K) + 2 * a.K + k])));
+    if (a.go_dtype == kF32 && a.go_vec4) {        // 16-byte loads (C % 4 == 0, aligned)
+        const float4* g4 = static_cast<const float4*>(a.grad_out);
+        for (int64_t i = i0; i < n_go / 4; i += stride) {
+            const float4 v = g4[i];
+            mg = max(mg, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
+                             max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
+        }
+    } else {
+        for (int64_t i = i0; i < n_go; i += stride)
+            mg = max(mg, __float_as_uint(fabsf(load_elem(a.grad_out, i, a.go_dtype))));
+    }
+    // the scalars: the last K of every 3K-float record, read as one coalesced stream
+    const int K3 = 3 * a.K, K2 = 2 * a.K;
+    const int64_t n_om = a.n_pix * a.G * K3;
+    if ((reinterpret_cast<uintptr_t>(a.om) & 15) == 0) {
+        const float4* o4 = reinterpret_cast<const float4*>(a.om);
+        for (int64_t i = i0; i < n_om / 4; i += stride) {
+            const float4 v = o4[i];
+            const int r = (int)((i * 4) % K3);
+            const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = r + e >= K3 ? r + e - K3 : r + e;
+                if (pos >= K2) mm = max(mm, __float_as_uint(fabsf(f[e])));
+            }
+        }
+        for (int64_t i = n_om / 4 * 4 + i0; i < n_om; i += stride)
+            if ((int)(i % K3) >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[i])));
+    } else {
+        for (int64_t i = i0; i < n_om; i += stride)
+            if ((int)(i % K3) >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[i])));
     }
     for (int d = 1; d < kWave; d <<= 1) {
         mg = max(mg, (uint32_t)__shfl_xor((int)mg, d, kWave));
@@ -349,9 +374,24 @@ __device__ __forceinline__ int dcn_fixed_exponent(const DcnArgs& a) {
     return 61 - e - a.log2_terms;
 }
 constexpr double kFixMagicD = 6755399441055744.0;             // 1.5 * 2^52
-__device__ __forceinline__ unsigned long long fixed_term(float t, double scale) {
-    return (unsigned long long)(__double_as_longlong(fma((double)t, scale, kFixMagicD)) -
+// RNE(go * ws) with ws = w * 2^E already scaled: |go * ws| < 2^51 by the choice of E
+__device__ __forceinline__ unsigned long long fixed_term(double go, double ws) {
+    return (unsigned long long)(__double_as_longlong(fma(go, ws, kFixMagicD)) -
                                 __double_as_longlong(kFixMagicD));
+}
+
+// idx / n and idx % n for 0 <= idx < 2^24 and a wave-uniform n, by a float
+// reciprocal corrected by one step (integer division costs tens of instructions)
+__device__ __forceinline__ void divmod_small(int idx, int n, float inv, int& q, int& r) {
+    q = (int)((float)idx * inv);
+    r = idx - q * n;
+    if (r < 0) {
+        --q;
+        r += n;
+    } else if (r >= n) {
+        ++q;
+        r -= n;
+    }
 }
 
 // Lanes: a group of bLg lanes takes one sample at a time; lane jj covers the NVL
@@ -408,8 +448,11 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
                   kj * a.DW, a.Wo, w0, w1);
         const int nw = w1 - w0 + 1;
         const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+        const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
         for (int idx = slot; idx < nh; idx += spp) {
-            const DcnRec R = dcn_record(a, t, h0 + idx / nw, w0 + idx % nw, k, true);
+            int oh, ow;
+            divmod_small(idx, nw, inv_nw, oh, ow);
+            const DcnRec R = dcn_record(a, t, h0 + oh, w0 + ow, k, true);
             if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
                 const uint32_t sid = ((uint32_t)R.pix * (uint32_t)a.G + (uint32_t)t.g) *
                                          (uint32_t)a.K + (uint32_t)k;
@@ -424,6 +467,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
             const int64_t ibase = ((int64_t)(t.n * a.H + R.y0) * a.W + R.x0) * a.C + gD;
             float pm = 0.0f, px = 0.0f, py = 0.0f;
             float go[NVL][VEC];
+            double god[NVL][VEC];
 #pragma unroll
             for (int u = 0; u < NVL; ++u) {
                 load_go<VEC>(a, gbase + cl[u], go[u]);
@@ -440,7 +484,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const float gv = vv[u] ? go[u][e] : 0.0f;
-                    go[u][e] = gv;
+                    god[u][e] = (double)gv;
                     const float val = cw[0] * v[0][e] + cw[1] * v[1][e] + cw[2] * v[2][e] +
                                       cw[3] * v[3][e];
                     const float ddx = hy * (v[1][e] - v[0][e]) + R.ly * (v[3][e] - v[2][e]);
@@ -464,13 +508,13 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
             for (int q = 0; q < 4; ++q) {
                 if (!(R.flags >> (5 + q) & 1u)) continue;
                 const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
-                const float w = cw[q] * R.m;
+                const double ws = (double)(cw[q] * R.m) * scale;
 #pragma unroll
                 for (int u = 0; u < NVL; ++u) {
                     if (!vv[u]) continue;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(w * go[u][e], scale));
+                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(god[u][e], ws));
                 }
             }
         }
@@ -484,8 +528,11 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
         out_range(t.Ix0 - a.M - 1, t.Ix0 + TX - 1 + a.M, a.SW, a.PW, kj * a.DW, a.Wo, w0, w1);
         const int nw = w1 - w0 + 1;
         const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+        const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
         for (int idx = slot; idx < nh; idx += spp) {
-            const int ho = h0 + idx / nw, wo = w0 + idx % nw;
+            int oh, ow;
+            divmod_small(idx, nw, inv_nw, oh, ow);
+            const int ho = h0 + oh, wo = w0 + ow;
             const int gy = ho * a.SH - a.PH + ki * a.DH, gx = wo * a.SW - a.PW + kj * a.DW;
             const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
             if (cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1) continue;   // home
@@ -499,14 +546,17 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
                 if (!vv[u]) continue;
                 float go[VEC];
                 load_go<VEC>(a, gbase + cl[u], go);
+                double god[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) god[e] = (double)go[e];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (!(R.flags >> (5 + q) & 1u)) continue;
                     const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
-                    const float w = cw[q] * R.m;
+                    const double ws = (double)(cw[q] * R.m) * scale;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(w * go[e], scale));
+                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(god[e], ws));
                 }
             }
         }
