@@ -55,7 +55,7 @@ typedef struct {
 
 /* dcn_out_size -- host only: the output height and width of `problem`.  Errors:
  * DA_ERR_INVALID_ARG for NULL pointers or malformed sizes. */
-da_status dcn_out_size(const dcn_problem* problem, int64_t* out_h, int64_t* out_w);
+DA_API da_status dcn_out_size(const dcn_problem* problem, int64_t* out_h, int64_t* out_w);
 
 /*
  * dcn_forward -- out[n, ho, wo, g*D + d] = sum_k m_gk * bilinear(input[n, :, :, g*D + d],
@@ -67,7 +67,7 @@ da_status dcn_out_size(const dcn_problem* problem, int64_t* out_h, int64_t* out_
  * malformed problem), DA_ERR_UNSUPPORTED (input of 2^32 bytes or more, C > 2^16, more
  * than 2^31 output pixels), DA_ERR_HIP.
  */
-da_status dcn_forward(const dcn_problem* problem, const void* input, const float* offset_mask,
+DA_API da_status dcn_forward(const dcn_problem* problem, const void* input, const float* offset_mask,
                       void* out, void* stream);
 
 /*
@@ -76,7 +76,7 @@ da_status dcn_forward(const dcn_problem* problem, const void* input, const float
  * reduction buffer, and room to list every (sample, corner) whose offset carries it
  * more than 4 pixels past its tile.
  */
-da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t* bytes);
+DA_API da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t* bytes);
 
 /*
  * dcn_backward -- the gradients of dcn_forward's definition.
@@ -98,7 +98,7 @@ da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t* bytes)
  * plus DA_ERR_UNSUPPORTED for 2^30 samples (N*Ho*Wo*G*K) or more and
  * DA_ERR_INVALID_ARG for a missing, misaligned or small workspace.
  */
-da_status dcn_backward(const dcn_problem* problem, const void* input, const float* offset_mask,
+DA_API da_status dcn_backward(const dcn_problem* problem, const void* input, const float* offset_mask,
                        const void* grad_out, float* grad_input, float* grad_offset_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 

@@ -59,6 +59,13 @@
 extern "C" {
 #endif
 
+/* Symbols of the C ABI; the library exports nothing else. */
+#if defined(__GNUC__) || defined(__clang__)
+#define DA_API __attribute__((visibility("default")))
+#else
+#define DA_API
+#endif
+
 #define DA_VERSION 120         /* 1.2.0 */
 #define DA_MAX_LEVELS 64       /* num_cams * num_scale */
 #define DA_MAX_EXTENT 32768    /* H and W of every level */
@@ -133,7 +140,7 @@ typedef struct {
  * slices for `problem`: 8 * bs * A * C * 4 when slices are wanted, else 0.  Only the
  * sizes and flags in `problem` are read.
  */
-da_status da_forward_workspace_size(const da_problem* problem, size_t* bytes);
+DA_API da_status da_forward_workspace_size(const da_problem* problem, size_t* bytes);
 
 /*
  * da_forward -- the forward pass (sections 3.2 and 5.1).
@@ -162,7 +169,7 @@ da_status da_forward_workspace_size(const da_problem* problem, size_t* bytes);
  * stencils and weights above 48 KiB of LDS; in the backward, num_embeds more than 16
  * times the largest power of two dividing C / G, capped at 64) or DA_ERR_HIP.
  */
-da_status da_forward(const da_problem* problem,
+DA_API da_status da_forward(const da_problem* problem,
                      const void* mc_ms_feat,
                      const int32_t* spatial_shape,
                      const int32_t* scale_start_index,
@@ -184,7 +191,7 @@ da_status da_forward(const da_problem* problem,
  * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */
-da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
+DA_API da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
 
 /*
  * da_backward -- the backward pass (section 4.1).  Same inputs as da_forward, plus
@@ -209,7 +216,7 @@ da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);
  * Same errors as da_forward, plus DA_ERR_INVALID_ARG for a missing, misaligned or too
  * small workspace and the DA_ERR_UNSUPPORTED cases of da_backward_workspace_size.
  */
-da_status da_backward(const da_problem* problem,
+DA_API da_status da_backward(const da_problem* problem,
                       const void* mc_ms_feat,
                       const int32_t* spatial_shape,
                       const int32_t* scale_start_index,
@@ -229,7 +236,7 @@ da_status da_backward(const da_problem* problem,
  * aggregations that read one feature map, or a caller that keeps a running gradient).
  * grad_loc and grad_weights are still overwritten.  Same arguments and errors.
  */
-da_status da_backward_accumulate(const da_problem* problem,
+DA_API da_status da_backward_accumulate(const da_problem* problem,
                                  const void* mc_ms_feat,
                                  const int32_t* spatial_shape,
                                  const int32_t* scale_start_index,
@@ -251,7 +258,7 @@ da_status da_backward_accumulate(const da_problem* problem,
  * Arguments as da_backward without the workspace; same errors as da_forward, and
  * DA_ERR_UNSUPPORTED with DA_FLAG_DETERMINISTIC.
  */
-da_status da_backward_atomic(const da_problem* problem,
+DA_API da_status da_backward_atomic(const da_problem* problem,
                              const void* mc_ms_feat,
                              const int32_t* spatial_shape,
                              const int32_t* scale_start_index,
@@ -289,7 +296,7 @@ typedef struct {
  * NULL pointers or malformed sizes, DA_ERR_UNSUPPORTED when num_feat >= 2^31 or
  * bs * num_cams > 65535.
  */
-da_status da_pack_layout(const da_pack_problem* problem, const int32_t* scale_hw,
+DA_API da_status da_pack_layout(const da_pack_problem* problem, const int32_t* scale_hw,
                          int32_t* spatial_shape, int32_t* scale_start_index, int64_t* num_feat);
 
 /*
@@ -300,7 +307,7 @@ da_status da_pack_layout(const da_pack_problem* problem, const int32_t* scale_hw
  * Asynchronous on `stream`.  Same errors as da_pack_layout, plus DA_ERR_INVALID_ARG for
  * NULL or misaligned tensors and DA_ERR_HIP.
  */
-da_status da_pack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
+DA_API da_status da_pack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
                          const void* const* maps, void* packed, void* stream);
 
 /*
@@ -309,17 +316,17 @@ da_status da_pack_levels(const da_pack_problem* problem, const int32_t* scale_hw
  * it carries d loss / d packed back to the per-scale maps.  Arguments and errors as
  * da_pack_levels.
  */
-da_status da_unpack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
+DA_API da_status da_unpack_levels(const da_pack_problem* problem, const int32_t* scale_hw,
                            const void* packed, void* const* maps, void* stream);
 
 /* Static description of a status code. */
-const char* da_status_string(da_status status);
+DA_API const char* da_status_string(da_status status);
 
 /* Message of the last failed call on the calling thread ("" if none). */
-const char* da_last_error(void);
+DA_API const char* da_last_error(void);
 
 /* DA_VERSION of the built library. */
-int32_t da_version(void);
+DA_API int32_t da_version(void);
 
 #ifdef __cplusplus
 }

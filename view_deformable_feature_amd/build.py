@@ -31,7 +31,7 @@ def _hipcc() -> str:
 
 def compile_flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
         # no packed fp32 VALU instructions (v_pk_*_f32)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-command-line-argument",
