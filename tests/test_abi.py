@@ -351,3 +351,15 @@ def test_dcn_rejects_null_and_misaligned(lib):
     n = ctypes.c_size_t(7)
     assert lib.dcn_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert lib.dcn_backward_workspace_size(ctypes.byref(p), None) == 1
+
+
+def test_exports_only_the_declared_c_abi(lib):
+    """The library's dynamic symbol table holds the C ABI and nothing else."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(_lib.declared_functions())

@@ -168,3 +168,28 @@ def test_dcn_autograd():
     assert torch.equal(om.grad, gom)
     assert_close("autograd grad_input", x.grad.float().cpu().numpy(),
                  gi.to(torch.float16).float().cpu().numpy(), 1e-3)
+
+
+@pytest.mark.parametrize("name", ["dcn_28", "dcn_14", "dcn_56_f16"])
+def test_dcn_other_page_shapes_full_size(name):
+    """The DCNv4 notes' other input sizes (28x28x256, 14x14x512) and the 56x56x128
+    shape with binary16 input, every element against the oracle."""
+    _check(W.DCN_WORKLOADS[name])
+
+
+def test_dcn_grad_input_repeatable_without_far_corners():
+    """Tile sums are 64-bit fixed point: with every offset inside the ring margin
+    (no far corner), grad_input is the same bit for bit run after run."""
+    import view_deformable_feature_amd as vdf
+    wl = _wl("c96_g3", offset_sigma=0.5)
+    inp = W.make_dcn_inputs(wl)
+    om = inp["offset_mask"].copy()
+    K = wl.K
+    om[..., :2 * K] = np.clip(om[..., :2 * K], -3.5, 3.5)
+    x, omt = _dev(dict(inp, offset_mask=om))
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+    runs = [vdf.dcn_backward(x, omt, go, **_conf(wl))[0].cpu() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(runs[0], r) for r in runs[1:])
+    r_gi, _ = oracle.dcn_backward(inp["input"], om, inp["grad_out"], **_conf(wl))
+    assert_close("repeatable grad_input", runs[0].numpy(), r_gi, TOL_BWD)
