@@ -64,8 +64,9 @@ DA_API da_status dcn_out_size(const dcn_problem* problem, int64_t* out_h, int64_
  *   offset_mask  device float [N, Ho, Wo, G, 3K], 4-byte aligned.
  *   out          device [N, Ho, Wo, C] of out_dtype, fully overwritten, element aligned.
  * Deterministic (no atomics).  Errors: DA_ERR_INVALID_ARG (NULL or misaligned pointer,
- * malformed problem), DA_ERR_UNSUPPORTED (input of 2^32 bytes or more, C > 2^16, more
- * than 2^31 output pixels), DA_ERR_HIP.
+ * malformed problem), DA_ERR_UNSUPPORTED (input or its binary32 gradient, out as
+ * binary32, or offset_mask of 2^32 bytes or more, C > 2^16, more than 2^31 output
+ * pixels), DA_ERR_HIP.
  */
 DA_API da_status dcn_forward(const dcn_problem* problem, const void* input, const float* offset_mask,
                       void* out, void* stream);

@@ -203,20 +203,30 @@ struct TileCtx {
     int n, g, Iy0, Ix0, Iy1, Ix1;   // owned tile [Iy0, Iy1) x [Ix0, Ix1)
 };
 
-// Phase A of one candidate sample: its stencil record (for a home sample, with
-// the corners no other tile's ring reaches flagged far).
-__device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t, int ho, int wo, int k,
-                                             bool home) {
+// The offsets (dx, dy) and the scalar of sample (pixel, group g, tap k).
+struct DcnOm {
+    float dx, dy, m;
+};
+
+// (every tensor of the operator is under 4 GiB: 32-bit element indices)
+__device__ __forceinline__ DcnOm load_om(const DcnArgs& a, int pix, int g, int k) {
+    const float* om = a.om + ((uint32_t)pix * (uint32_t)a.G + (uint32_t)g) * (uint32_t)(3 * a.K);
+    return DcnOm{om[2 * k], om[2 * k + 1], om[2 * a.K + k]};
+}
+
+// Phase A of one sample with grid point (gy, gx): its stencil record.  For a home
+// sample the corners that no other tile's ring reaches are flagged far: a corner's
+// tile reaches the sample through its ring only when the grid point lies in that
+// tile's window.  Tile sides are powers of two, and the flags are formed without
+// branches, so the records of several samples are formed side by side.
+__device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t, int pix, int gy,
+                                             int gx, int k, const DcnOm& o, bool home) {
 #pragma clang fp contract(off)
     DcnRec r;
-    const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
-    const int gy = ho * a.SH - a.PH + ki * a.DH, gx = wo * a.SW - a.PW + kj * a.DW;
-    r.pix = (t.n * a.Ho + ho) * a.Wo + wo;
+    r.pix = pix;
     r.k = k;
-    const float* om = a.om + ((int64_t)r.pix * a.G + t.g) * (3 * a.K);
-    const float dx = om[2 * k], dy = om[2 * k + 1];
-    r.m = om[2 * a.K + k];
-    const float y = (float)gy + dy, x = (float)gx + dx;
+    r.m = o.m;
+    const float y = (float)gy + o.dy, x = (float)gx + o.dx;
     const bool inside = y > -1.0f && x > -1.0f && y < (float)a.H && x < (float)a.W;
     const float yf = inside ? floorf(y) : 0.0f, xf = inside ? floorf(x) : 0.0f;
     r.ly = inside ? y - yf : 0.0f;
@@ -224,38 +234,39 @@ __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t,
     r.y0 = (int)yf;
     r.x0 = (int)xf;
     uint32_t f = inside ? 1u : 0u;
-    if (inside) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int cy = r.y0 + (q >> 1), cx = r.x0 + (q & 1);
-            if (cy < 0 || cy >= a.H || cx < 0 || cx >= a.W) continue;
-            f |= 1u << (1 + q);
-            if (cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1) {
-                f |= 1u << (5 + q);
-            } else if (home) {
-                // the corner's tile reaches this sample through its ring only when
-                // the grid point lies in that tile's window
-                const int oy = cy / a.TY * a.TY, ox = cx / a.TX * a.TX;
-                const bool reach = gy >= oy - a.M - 1 && gy <= oy + a.TY - 1 + a.M &&
-                                   gx >= ox - a.M - 1 && gx <= ox + a.TX - 1 + a.M;
-                if (!reach) f |= 1u << (9 + q);
-            }
+    for (int q = 0; q < 4; ++q) {
+        const int cy = r.y0 + (q >> 1), cx = r.x0 + (q & 1);
+        const bool img = inside && cy >= 0 && cy < a.H && cx >= 0 && cx < a.W;
+        const bool own = img && cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1;
+        f |= (img ? 1u : 0u) << (1 + q);
+        f |= (own ? 1u : 0u) << (5 + q);
+        if (home) {
+            const int oy = cy & -a.TY, ox = cx & -a.TX;     // origin of the corner's tile
+            const bool reach = gy >= oy - a.M - 1 && gy <= oy + a.TY - 1 + a.M &&
+                               gx >= ox - a.M - 1 && gx <= ox + a.TX - 1 + a.M;
+            f |= (img && !own && !reach ? 1u : 0u) << (9 + q);
         }
     }
     r.flags = f;
     return r;
 }
 
-// grad_out[i .. i + VEC) of the run-time type go_dtype (16-byte loads for binary32
-// when the tensor allows them)
-template <int VEC>
-__device__ __forceinline__ void load_go(const DcnArgs& a, int64_t i, float (&go)[VEC]) {
-    if (VEC == 4 && a.go_dtype == kF32 && a.go_vec4) {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
-        go[0] = v.x;
-        go[1] = v.y;
-        go[2] = v.z;
-        go[3] = v.w;
+// grad_out[i .. i + VEC): GOV -- binary32 with 16-byte aligned vectors (VEC a multiple
+// of 4) -- takes 16-byte loads; otherwise element loads of the run-time type go_dtype.
+template <int VEC, bool GOV>
+__device__ __forceinline__ void load_go(const DcnArgs& a, uint32_t i, float (&go)[VEC]) {
+    if constexpr (GOV) {
+        static_assert(VEC % 4 == 0, "16-byte grad_out loads cover 4 channels");
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) {
+            const float4 v = p[h];
+            go[4 * h] = v.x;
+            go[4 * h + 1] = v.y;
+            go[4 * h + 2] = v.z;
+            go[4 * h + 3] = v.w;
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) go[e] = load_elem(a.grad_out, i + e, a.go_dtype);
@@ -374,11 +385,6 @@ __device__ __forceinline__ int dcn_fixed_exponent(const DcnArgs& a) {
     return 61 - e - a.log2_terms;
 }
 constexpr double kFixMagicD = 6755399441055744.0;             // 1.5 * 2^52
-// RNE(go * ws) with ws = w * 2^E already scaled: |go * ws| < 2^51 by the choice of E
-__device__ __forceinline__ unsigned long long fixed_term(double go, double ws) {
-    return (unsigned long long)(__double_as_longlong(fma(go, ws, kFixMagicD)) -
-                                __double_as_longlong(kFixMagicD));
-}
 
 // idx / n and idx % n for 0 <= idx < 2^24 and a wave-uniform n, by a float
 // reciprocal corrected by one step (integer division costs tens of instructions)
@@ -394,16 +400,51 @@ __device__ __forceinline__ void divmod_small(int idx, int n, float inv, int& q, 
     }
 }
 
-// Lanes: a group of bLg lanes takes one sample at a time; lane jj covers the NVL
-// vectors jj, jj + bLg, ... of VEC channels of the group.  Every lane of the
-// group forms the (cheap) stencil itself, so the waves never wait for one another
-// inside the loops: many samples' loads are in flight at once.
-template <typename T, int VEC, int NVL>
+// group_sum of four values at once (one test of the group width per step)
+__device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        if (n <= (1 << step)) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            switch (step) {
+                case 0: v[q] += dpp<0xB1, 0xF>(v[q]); break;     // quad_perm [1,0,3,2]
+                case 1: v[q] += dpp<0x4E, 0xF>(v[q]); break;     // quad_perm [2,3,0,1]
+                case 2: v[q] += dpp<0x141, 0xF>(v[q]); break;    // row_half_mirror
+                case 3: v[q] += dpp<0x140, 0xF>(v[q]); break;    // row_mirror
+                case 4: v[q] += dpp<0x142, 0xA>(v[q]); break;    // row_bcast:15
+                default: v[q] += dpp<0x143, 0xC>(v[q]); break;   // row_bcast:31
+            }
+        }
+    }
+}
+
+// Lanes: in the home loop a group of bLg lanes takes one sample at a time; lane jj
+// covers the NVL vectors jj, jj + bLg, ... of VEC channels of the group, and every
+// lane of the group forms the (cheap) stencil itself, so the waves never wait for
+// one another.  The ring loop tests one candidate per lane, lists the accepted ones
+// (a corner in this tile: about one candidate in eight for offsets of a pixel or
+// so) in the wave's LDS list at their rank among the wave's accepted lanes, and
+// then each lane group takes listed samples one at a time, so that their loads and
+// additions run on full waves.
+//
+// Tile sums: a term t is added as the binary64 encoding of RNE(t 2^E) + 1.5 * 2^52,
+// an integer in [2^52, 2^53) whose encoding is kFixMagicBits + RNE(t 2^E), and each
+// tile pixel counts the terms it takes (the same count for every channel of the
+// group; every lane of the group adds it, so the LDS count is bLg times that).  The
+// store subtracts count * kFixMagicBits modulo 2^64, which leaves the exact sum of
+// the rounded terms.
+constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;   // encoding of 1.5 * 2^52
+static_assert(kDcnWaves == kDcnBwdWaves, "ring lists: one per wave");
+
+template <typename T, int VEC, int NVL, bool GOV>
 __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int TY = a.TY, TX = a.TX;
     unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
-    const int tid = threadIdx.x;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * a.Dp);        // [TY*TX]
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    uint32_t* wl = cnt + (TY * TX + 3) / 4 * 4 + wave * (kDcnListWords * kWave);
     const int E = dcn_fixed_exponent(a);
     const double scale = ldexp(1.0, E);
 
@@ -422,6 +463,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
     for (int i = tid; i < TY * TX * a.Dp; i += kDcnThreads) acc[i] = 0ull;
+    for (int i = tid; i < TY * TX; i += kDcnThreads) cnt[i] = 0u;
     __syncthreads();
 
     const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnThreads >> a.blog2Lg;
@@ -433,14 +475,45 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
         vv[u] = vi < a.Dv;
         cl[u] = vv[u] ? vi * VEC : 0;
     }
-    const int gD = t.g * a.D;
+    const uint32_t gD = (uint32_t)(t.g * a.D);
     const __amdgpu_buffer_rsrc_t r_in = make_rsrc(a.input, a.in_bytes);
     constexpr int kElem = (int)sizeof(T);
     const bool last = jj == a.bLg - 1;
+    // byte steps from corner 0 to corner q, and of the lane's vectors
+    const uint32_t cq[4] = {0u, (uint32_t)(a.C * kElem), (uint32_t)(a.W * a.C * kElem),
+                            (uint32_t)((a.W + 1) * a.C * kElem)};
+    uint32_t clb[NVL], vvb[NVL];
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+        clb[u] = (uint32_t)(cl[u] * kElem);
+        vvb[u] = vv[u] ? 1u : 0u;
+    }
+
+    // the terms of R's corners that lie in this tile; gd: the lane's grad_out values
+    // in binary64 (idle vectors add nothing)
+    auto add_tile = [&](const DcnRec& R, const float (&cw)[4], const double (&gd)[NVL][VEC]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (!(R.flags >> (5 + q) & 1u)) continue;
+            const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
+            atomicAdd(&cnt[p], 1u);        // once per lane of the group: bLg per term
+            const double ws = (double)(cw[q] * R.m) * scale;
+            unsigned long long* row = acc + p * a.Dp;
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                if (!vv[u]) continue;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    atomicAdd(&row[cl[u] + e], (unsigned long long)__double_as_longlong(
+                                                   fma(gd[u][e], ws, kFixMagicD)));
+            }
+        }
+    };
 
     // ---- home samples: offset / scalar gradients, corners in this tile ----
     for (int k = 0; k < a.K; ++k) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+        const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
         int h0, h1, w0, w1;
         out_range(t.Iy0 == 0 ? -(1 << 28) : t.Iy0, t.Iy1 == a.H ? (1 << 28) : t.Iy1 - 1, a.SH, a.PH,
                   ki * a.DH, a.Ho, h0, h1);
@@ -452,113 +525,134 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
         for (int idx = slot; idx < nh; idx += spp) {
             int oh, ow;
             divmod_small(idx, nw, inv_nw, oh, ow);
-            const DcnRec R = dcn_record(a, t, h0 + oh, w0 + ow, k, true);
+            const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
+            const DcnRec R = dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox, k,
+                                        load_om(a, pix, t.g, k), true);
             if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
-                const uint32_t sid = ((uint32_t)R.pix * (uint32_t)a.G + (uint32_t)t.g) *
+                const uint32_t sid = ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
                                          (uint32_t)a.K + (uint32_t)k;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     if (R.flags >> (9 + q) & 1u) a.fb[atomicAdd(a.ctrl + kDcnCtrlFar, 1u)] = sid * 4u + q;
             }
-            float cw[4];
-            corner_weights(R, cw);
-            const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
-            const int64_t gbase = (int64_t)R.pix * a.C + gD;
-            const int64_t ibase = ((int64_t)(t.n * a.H + R.y0) * a.W + R.x0) * a.C + gD;
-            float pm = 0.0f, px = 0.0f, py = 0.0f;
+            // byte offset of corner 0's group channels (modulo 2^32: a corner outside
+            // the image is never addressed, and the others come out in range)
+            const uint32_t ib0 =
+                (((uint32_t)(t.n * a.H + R.y0) * (uint32_t)a.W + (uint32_t)R.x0) * (uint32_t)a.C + gD) *
+                (uint32_t)kElem;
             float go[NVL][VEC];
-            double god[NVL][VEC];
+            float v[NVL][4][VEC];
 #pragma unroll
             for (int u = 0; u < NVL; ++u) {
-                load_go<VEC>(a, gbase + cl[u], go[u]);
-                float v[4][VEC];
+                load_go<VEC, GOV>(a, (uint32_t)pix * (uint32_t)a.C + gD + cl[u], go[u]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t off =
-                        (R.flags >> (1 + q) & 1u) && vv[u]
-                            ? (uint32_t)(ibase + ((q >> 1) * a.W + (q & 1)) * a.C + cl[u]) *
-                                  (uint32_t)kElem
-                            : a.in_bytes;
-                    VecLoad<T, VEC>::run(r_in, off, 0u, v[q]);
-                }
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float gv = vv[u] ? go[u][e] : 0.0f;
-                    god[u][e] = (double)gv;
-                    const float val = cw[0] * v[0][e] + cw[1] * v[1][e] + cw[2] * v[2][e] +
-                                      cw[3] * v[3][e];
-                    const float ddx = hy * (v[1][e] - v[0][e]) + R.ly * (v[3][e] - v[2][e]);
-                    const float ddy = hx * (v[2][e] - v[0][e]) + R.lx * (v[3][e] - v[1][e]);
-                    pm += gv * val;
-                    px += gv * ddx;
-                    py += gv * ddy;
+                    const uint32_t at = ib0 + cq[q] + clb[u];
+                    const uint32_t off = (R.flags >> (1 + q) & vvb[u]) ? at : a.in_bytes;
+                    VecLoad<T, VEC>::run(r_in, off, 0u, v[u][q]);
                 }
             }
-            pm = group_sum(pm, a.bLg);
-            px = group_sum(px, a.bLg);
-            py = group_sum(py, a.bLg);
+            // S_q = sum over the group's channels of grad_out * corner q: the value,
+            // x- and y-derivative sums are fixed combinations of the four
+            float cw[4];
+            corner_weights(R, cw);
+            float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            double gd[NVL][VEC];
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float g = vv[u] ? go[u][e] : 0.0f;
+                    gd[u][e] = (double)g;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) S[q] += g * v[u][q][e];
+                }
+            }
+            group_sum4(S, a.bLg);
             if (last) {
                 const bool live = R.flags & 1u;
-                float* gom = a.grad_om + ((int64_t)R.pix * a.G + t.g) * (3 * a.K);
+                const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
+                const float px = hy * (S[1] - S[0]) + R.ly * (S[3] - S[2]);
+                const float py = hx * (S[2] - S[0]) + R.lx * (S[3] - S[1]);
+                const float pm = cw[0] * S[0] + cw[1] * S[1] + cw[2] * S[2] + cw[3] * S[3];
+                float* gom = a.grad_om + ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
+                                             (uint32_t)(3 * a.K);
                 gom[2 * k] = live ? R.m * px : 0.0f;
                 gom[2 * k + 1] = live ? R.m * py : 0.0f;
                 gom[2 * a.K + k] = live ? pm : 0.0f;
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (!(R.flags >> (5 + q) & 1u)) continue;
-                const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
-                const double ws = (double)(cw[q] * R.m) * scale;
-#pragma unroll
-                for (int u = 0; u < NVL; ++u) {
-                    if (!vv[u]) continue;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(god[u][e], ws));
-                }
-            }
+            add_tile(R, cw, gd);
         }
     }
 
     // ---- ring: other tiles' samples whose grid point lies in this tile's window ----
+    const int gpw = kWave >> a.blog2Lg;              // lane groups per wave
+    const int grp = lane >> a.blog2Lg;
     for (int k = 0; k < a.K; ++k) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+        const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
         int h0, h1, w0, w1;
         out_range(t.Iy0 - a.M - 1, t.Iy0 + TY - 1 + a.M, a.SH, a.PH, ki * a.DH, a.Ho, h0, h1);
         out_range(t.Ix0 - a.M - 1, t.Ix0 + TX - 1 + a.M, a.SW, a.PW, kj * a.DW, a.Wo, w0, w1);
         const int nw = w1 - w0 + 1;
         const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
         const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
-        for (int idx = slot; idx < nh; idx += spp) {
+        for (int base = wave * kWave; base < nh; base += kDcnThreads) {    // wave-uniform
+            const int idx = base + lane;
             int oh, ow;
-            divmod_small(idx, nw, inv_nw, oh, ow);
-            const int ho = h0 + oh, wo = w0 + ow;
-            const int gy = ho * a.SH - a.PH + ki * a.DH, gx = wo * a.SW - a.PW + kj * a.DW;
+            divmod_small(idx < nh ? idx : base, nw, inv_nw, oh, ow);
+            const int gy = (h0 + oh) * a.SH + oy, gx = (w0 + ow) * a.SW + ox;
+            const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
             const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
-            if (cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1) continue;   // home
-            const DcnRec R = dcn_record(a, t, ho, wo, k, false);
-            if (!(R.flags >> 5)) continue;
-            float cw[4];
-            corner_weights(R, cw);
-            const int64_t gbase = (int64_t)R.pix * a.C + gD;
-#pragma unroll
-            for (int u = 0; u < NVL; ++u) {
-                if (!vv[u]) continue;
-                float go[VEC];
-                load_go<VEC>(a, gbase + cl[u], go);
-                double god[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) god[e] = (double)go[e];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (!(R.flags >> (5 + q) & 1u)) continue;
-                    const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
-                    const double ws = (double)(cw[q] * R.m) * scale;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        atomicAdd(&acc[p * a.Dp + cl[u] + e], fixed_term(god[e], ws));
-                }
+            const bool cand = idx < nh && !(cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1);
+            const DcnOm o = cand ? load_om(a, pix, t.g, k) : DcnOm{0.0f, 0.0f, 0.0f};
+            const DcnRec R = dcn_record(a, t, pix, gy, gx, k, o, false);
+            const bool take = cand && (R.flags >> 5) != 0u;
+            const unsigned long long mask = __ballot(take);
+            if (take) {
+                const int r = (int)__builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                wl[r] = (uint32_t)pix;
+                wl[kWave + r] = __float_as_uint(R.m);
+                wl[2 * kWave + r] = __float_as_uint(R.ly);
+                wl[3 * kWave + r] = __float_as_uint(R.lx);
+                // low corner relative to the tile (in [-1, TY] x [-1, TX] for an
+                // accepted sample), the inside bit and the in-tile corner bits
+                wl[4 * kWave + r] = (uint32_t)(R.y0 - t.Iy0 + 1) | (uint32_t)(R.x0 - t.Ix0 + 1) << 8 |
+                                    (R.flags & 0x1e1u) << 16;
             }
+            // the list is written and read by this wave only, and LDS executes one
+            // wave's instructions in order: no barrier, only no reordering
+            __builtin_amdgcn_wave_barrier();
+            const int n_take = __popcll(mask);
+            for (int r = grp; r < n_take; r += gpw) {
+                DcnRec L;
+                L.pix = (int)wl[r];
+                L.m = __uint_as_float(wl[kWave + r]);
+                L.ly = __uint_as_float(wl[2 * kWave + r]);
+                L.lx = __uint_as_float(wl[3 * kWave + r]);
+                const uint32_t pk = wl[4 * kWave + r];
+                L.y0 = (int)(pk & 0xffu) - 1 + t.Iy0;
+                L.x0 = (int)(pk >> 8 & 0xffu) - 1 + t.Ix0;
+                L.flags = pk >> 16;
+                float cw[4];
+                corner_weights(L, cw);
+                double gd[NVL][VEC];
+#pragma unroll
+                for (int u = 0; u < NVL; ++u) {
+                    float go[VEC];
+                    if (vv[u]) {
+                        load_go<VEC, GOV>(a, (uint32_t)L.pix * (uint32_t)a.C + gD + cl[u], go);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) go[e] = 0.0f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) gd[u][e] = (double)go[e];
+                }
+                add_tile(L, cw, gd);
+            }
+            __builtin_amdgcn_wave_barrier();      // the next pass rewrites the list
         }
     }
 
@@ -569,14 +663,17 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     for (int i = tid; i < npx * a.D; i += kDcnThreads) {
         const int p = i / a.D, c = i - (i / a.D) * a.D;
         const int py = p / cols, px = p - (p / cols) * cols;
+        const int tp = py * TX + px;
+        const long long code =
+            (long long)(acc[tp * a.Dp + c] - (unsigned long long)(cnt[tp] >> a.blog2Lg) * kFixMagicBits);
         a.grad_input[(((int64_t)t.n * a.H + t.Iy0 + py) * a.W + t.Ix0 + px) * a.C + gD + c] =
-            (float)((double)(long long)acc[(py * TX + px) * a.Dp + c] * inv);
+            (float)((double)code * inv);
     }
 }
 
 // The far list: corner q of sample s gets cw_q * m * grad_out by atomics (after every
 // tile has been stored).  Lg lanes per entry, a grid-stride loop over the entries.
-template <typename T, int VEC, int NVL>
+template <typename T, int VEC, int NVL, bool GOV>
 __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
 #pragma clang fp contract(off)
     const uint32_t count = a.ctrl[kDcnCtrlFar];
@@ -593,8 +690,10 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
         const int g = (int)(s % (uint32_t)a.G);
         const int pix = (int)(s / (uint32_t)a.G);
         const int wo = pix % a.Wo, ho = (pix / a.Wo) % a.Ho, n = pix / (a.Wo * a.Ho);
+        const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         TileCtx t{n, g, 0, 0, 0, 0};            // empty tile: no corner counts as owned
-        const DcnRec R = dcn_record(a, t, ho, wo, k, false);
+        const DcnRec R = dcn_record(a, t, pix, ho * a.SH - a.PH + ki * a.DH,
+                                    wo * a.SW - a.PW + kj * a.DW, k, load_om(a, pix, g, k), false);
         float cw[4];
         corner_weights(R, cw);
         const float w = cw[q] * R.m;
@@ -606,7 +705,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
             const uint32_t goff =
                 (uint32_t)(((int64_t)(n * a.H + R.y0 + (q >> 1)) * a.W + R.x0 + (q & 1)) * a.C + c0) * 4u;
             float go[VEC];
-            load_go<VEC>(a, (int64_t)pix * a.C + c0, go);
+            load_go<VEC, GOV>(a, (uint32_t)pix * (uint32_t)a.C + (uint32_t)c0, go);
 #pragma unroll
             for (int e2 = 0; e2 < VEC; ++e2)
                 __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w * go[e2], r_gi, goff + 4u * e2, 0, 0);
@@ -634,16 +733,16 @@ hipError_t dcn_fwd_dispatch_nv(const DcnArgs& a, int nv, hipStream_t st) {
     }
 }
 
-template <typename T, int VEC, int NVL>
+template <typename T, int VEC, int NVL, bool GOV>
 hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
     const unsigned blocks = (unsigned)((int64_t)a.N * a.tiles_y * a.tiles_x * a.G);
     hipLaunchKernelGGL(dcn_bound_kernel, dim3(kDcnBoundBlocks), dim3(kDcnThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL>), dim3(blocks), dim3(kDcnThreads), lds, st, a);
+    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV>), dim3(blocks), dim3(kDcnThreads), lds, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dcn_far_kernel<T, VEC, NVL>), dim3(1024), dim3(kDcnThreads), 0, st, a);
+    hipLaunchKernelGGL((dcn_far_kernel<T, VEC, NVL, GOV>), dim3(1024), dim3(kDcnThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -668,11 +767,14 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
     return with_elem(in_dtype, [&](auto t) {
         using T = decltype(t);
         constexpr int V = sizeof(T) == 2 ? 8 : 4;
+        if (vec == V && a.go_vec4)
+            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2, true>(a, lds_bytes, stream)
+                               : dcn_bwd_launch<T, V, 1, true>(a, lds_bytes, stream);
         if (vec == V)
-            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2>(a, lds_bytes, stream)
-                               : dcn_bwd_launch<T, V, 1>(a, lds_bytes, stream);
-        return a.bNVL == 2 ? dcn_bwd_launch<T, 1, 2>(a, lds_bytes, stream)
-                           : dcn_bwd_launch<T, 1, 1>(a, lds_bytes, stream);
+            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2, false>(a, lds_bytes, stream)
+                               : dcn_bwd_launch<T, V, 1, false>(a, lds_bytes, stream);
+        return a.bNVL == 2 ? dcn_bwd_launch<T, 1, 2, false>(a, lds_bytes, stream)
+                           : dcn_bwd_launch<T, 1, 1, false>(a, lds_bytes, stream);
     });
 }
 

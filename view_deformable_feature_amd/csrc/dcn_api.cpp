@@ -99,6 +99,13 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
                             (unsigned long long)in_bytes);
     const int64_t n_pix = p->batch * ho * wo;
     if (n_pix >= (int64_t(1) << 31)) return report_error(DA_ERR_UNSUPPORTED, "2^31 output pixels or more");
+    // the kernels index out / grad_out (as binary32) and offset_mask with 32-bit offsets
+    const uint64_t out_bytes = (uint64_t)n_pix * p->channels * 4;
+    const uint64_t om_bytes = (uint64_t)n_pix * p->groups * 3 * p->kernel_h * p->kernel_w * 4;
+    if (out_bytes + 64 > kU32Max || om_bytes + 64 > kU32Max)
+        return report_error(DA_ERR_UNSUPPORTED,
+                            "output (%llu bytes as binary32) or offset_mask (%llu bytes) reaches 4 GiB",
+                            (unsigned long long)out_bytes, (unsigned long long)om_bytes);
     if (n_pix * p->groups * p->kernel_h * p->kernel_w >= (int64_t(1) << 30))
         return report_error(DA_ERR_UNSUPPORTED, "2^30 samples (pixel, group, tap) or more");
     const int64_t C = p->channels, G = p->groups, D = C / G;
@@ -150,7 +157,7 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
     // different banks
     a.Dp = (int32_t)(D + 1);
     int ty = 32, tx = 32;
-    while ((ty > 1 || tx > 1) && (size_t)ty * tx * a.Dp * 8 > kDcnTileLds) {
+    while ((ty > 1 || tx > 1) && da::dcn_tile_lds_bytes(ty, tx, a.Dp) > kDcnTileLds) {
         if (ty >= tx && ty > 1) ty >>= 1;
         else tx >>= 1;
     }
@@ -159,7 +166,7 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
     a.M = kDcnMargin;
     a.tiles_y = (int32_t)((p->height + ty - 1) / ty);
     a.tiles_x = (int32_t)((p->width + tx - 1) / tx);
-    plan.lds_bytes = (size_t)ty * tx * a.Dp * 8;
+    plan.lds_bytes = da::dcn_tile_lds_bytes(ty, tx, a.Dp);
     // at most every sample of one (image, group) plane adds to one tile sum
     a.log2_terms = std::max(10, log2i((int)std::min<int64_t>(ho * wo * a.K, 1 << 30)) + 1);
     // backward: two vectors per lane where the group has them (fewer lanes repeat
@@ -235,7 +242,7 @@ da_status dcn_backward(const dcn_problem* p, const void* input, const float* off
     a.grad_out = grad_out;
     a.grad_input = grad_input;
     a.grad_om = grad_offset_mask;
-    a.go_vec4 = p->out_dtype == DA_F32 && plan.vec == 4 && aligned(grad_out, 16);
+    a.go_vec4 = p->out_dtype == DA_F32 && plan.vec % 4 == 0 && aligned(grad_out, 16);
     if (p->batch == 0) return DA_OK;
     const uint64_t need = dcn_workspace_bytes(a.n_pix * a.G * a.K);
     if (need) {

@@ -8,6 +8,7 @@
 // 64 / Lp pixels, and a lane covers NV = G * Lg / Lp groups of its pixel.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -57,5 +58,14 @@ hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, h
 hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream);
 constexpr int kDcnRecBytes = 32;   // one sample's stencil record
+// Dynamic LDS of the backward tile kernel: the [TY*TX][Dp] 64-bit sums, the number of
+// terms each tile pixel took (32-bit, padded to 16 bytes), and per wave a list of up to
+// 64 accepted ring candidates (kDcnListWords words each).
+constexpr int kDcnBwdWaves = 4;
+constexpr int kDcnListWords = 5;
+inline size_t dcn_tile_lds_bytes(int ty, int tx, int dp) {
+    return (size_t)ty * tx * dp * 8 + ((size_t)ty * tx + 3) / 4 * 16 +
+           (size_t)kDcnBwdWaves * 64 * kDcnListWords * 4;
+}
 
 }  // namespace da
