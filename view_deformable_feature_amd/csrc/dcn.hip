@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "da_device.h"
 #include "dcn_internal.h"
 
@@ -289,44 +291,87 @@ __device__ __forceinline__ void corner_weights(const DcnRec& r, float (&cw)[4]) 
 // stays below 2^61 and every term below 2^51 (log2_terms >= 10).  Rounding a term
 // to RNE(t 2^E): adding 1.5 * 2^52 in binary64 puts t 2^E on the integer grid of
 // the binade [2^52, 2^53), whose encoding is the integer plus a constant.
-__global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
-    __shared__ uint32_t red[2][kDcnWaves];
+// One wave of 1024-thread blocks (one per CU): the blocks finish together, and each
+// takes one ticket from a single counter, so fewer blocks shorten that tail.
+constexpr int kBoundThreads = 1024;
+constexpr int kBoundWaves = kBoundThreads / kWave;
+constexpr int kBoundGrid = 256;
+static_assert(kBoundGrid <= kDcnBoundBlocks, "partials fit the workspace");
+
+__global__ void __launch_bounds__(kBoundThreads) dcn_bound_kernel(DcnArgs a) {
+    __shared__ uint32_t red[2][kBoundWaves];
     __shared__ uint32_t is_last;
-    const int64_t stride = (int64_t)gridDim.x * kDcnThreads;
-    const int64_t i0 = (int64_t)blockIdx.x * kDcnThreads + threadIdx.x;
+    constexpr int U = 4;                    // loads in flight per thread
+    // element counts are below 2^30 (every tensor is under 4 GiB)
+    const uint32_t stride = gridDim.x * kBoundThreads;
+    const uint32_t i0 = blockIdx.x * kBoundThreads + threadIdx.x;
     uint32_t mg = 0, mm = 0;
-    const int64_t n_go = a.n_pix * a.C;
+    const uint32_t n_go = (uint32_t)(a.n_pix * a.C);
     if (a.go_dtype == kF32 && a.go_vec4) {        // 16-byte loads (C % 4 == 0, aligned)
         const float4* g4 = static_cast<const float4*>(a.grad_out);
-        for (int64_t i = i0; i < n_go / 4; i += stride) {
+        const uint32_t n4 = n_go / 4;
+        uint32_t i = i0;
+        for (; i + (U - 1) * stride < n4; i += U * stride) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = g4[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                mg = max(mg, max(max(__float_as_uint(fabsf(v[u].x)), __float_as_uint(fabsf(v[u].y))),
+                                 max(__float_as_uint(fabsf(v[u].z)), __float_as_uint(fabsf(v[u].w)))));
+        }
+        for (; i < n4; i += stride) {
             const float4 v = g4[i];
             mg = max(mg, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
                              max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
         }
     } else {
-        for (int64_t i = i0; i < n_go; i += stride)
+        for (uint32_t i = i0; i < n_go; i += stride)
             mg = max(mg, __float_as_uint(fabsf(load_elem(a.grad_out, i, a.go_dtype))));
     }
     // the scalars: the last K of every 3K-float record, read as one coalesced stream
-    const int K3 = 3 * a.K, K2 = 2 * a.K;
-    const int64_t n_om = a.n_pix * a.G * K3;
+    // of 16-byte vectors; r tracks the record position of a vector's first float
+    const uint32_t K3 = (uint32_t)(3 * a.K), K2 = (uint32_t)(2 * a.K);
+    const uint32_t n_om = (uint32_t)(a.n_pix * a.G) * K3;
     if ((reinterpret_cast<uintptr_t>(a.om) & 15) == 0) {
         const float4* o4 = reinterpret_cast<const float4*>(a.om);
-        for (int64_t i = i0; i < n_om / 4; i += stride) {
-            const float4 v = o4[i];
-            const int r = (int)((i * 4) % K3);
+        const uint32_t n4 = n_om / 4;
+        const uint32_t step = (stride * 4u) % K3;
+        uint32_t r = (i0 * 4u) % K3;
+        auto take = [&](const float4& v, uint32_t r0) {
             const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int pos = r + e >= K3 ? r + e - K3 : r + e;
-                if (pos >= K2) mm = max(mm, __float_as_uint(fabsf(f[e])));
+                uint32_t pos = r0 + (uint32_t)e;
+                pos = pos >= K3 ? pos - K3 : pos;
+                // a select, not a branch, so that the loads stay unconditional
+                mm = max(mm, pos >= K2 ? __float_as_uint(fabsf(f[e])) : 0u);
+            }
+        };
+        auto advance = [&](uint32_t x) {
+            x += step;
+            return x >= K3 ? x - K3 : x;
+        };
+        uint32_t i = i0;
+        for (; i + (U - 1) * stride < n4; i += U * stride) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = o4[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                take(v[u], r);
+                r = advance(r);
             }
         }
-        for (int64_t i = n_om / 4 * 4 + i0; i < n_om; i += stride)
-            if ((int)(i % K3) >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[i])));
+        for (; i < n4; i += stride) {
+            take(o4[i], r);
+            r = advance(r);
+        }
+        for (uint32_t j = n4 * 4 + i0; j < n_om; j += stride)
+            if (j % K3 >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[j])));
     } else {
-        for (int64_t i = i0; i < n_om; i += stride)
-            if ((int)(i % K3) >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[i])));
+        for (uint32_t j = i0; j < n_om; j += stride)
+            if (j % K3 >= K2) mm = max(mm, __float_as_uint(fabsf(a.om[j])));
     }
     for (int d = 1; d < kWave; d <<= 1) {
         mg = max(mg, (uint32_t)__shfl_xor((int)mg, d, kWave));
@@ -338,7 +383,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kDcnWaves; ++w) {
+        for (int w = 1; w < kBoundWaves; ++w) {
             mg = max(mg, red[0][w]);
             mm = max(mm, red[1][w]);
         }
@@ -352,7 +397,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
     __threadfence();
     mg = 0;
     mm = 0;
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kDcnThreads) {
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBoundThreads) {
         mg = max(mg, a.part[2 * b]);
         mm = max(mm, a.part[2 * b + 1]);
     }
@@ -367,7 +412,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bound_kernel(DcnArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kDcnWaves; ++w) {
+        for (int w = 1; w < kBoundWaves; ++w) {
             mg = max(mg, red[0][w]);
             mm = max(mm, red[1][w]);
         }
@@ -435,10 +480,9 @@ __device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
 // store subtracts count * kFixMagicBits modulo 2^64, which leaves the exact sum of
 // the rounded terms.
 constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;   // encoding of 1.5 * 2^52
-static_assert(kDcnWaves == kDcnBwdWaves, "ring lists: one per wave");
 
 template <typename T, int VEC, int NVL, bool GOV>
-__global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
+__global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int TY = a.TY, TX = a.TX;
     unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
@@ -462,11 +506,11 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     t.Iy1 = min(t.Iy0 + TY, a.H);
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
-    for (int i = tid; i < TY * TX * a.Dp; i += kDcnThreads) acc[i] = 0ull;
-    for (int i = tid; i < TY * TX; i += kDcnThreads) cnt[i] = 0u;
+    for (int i = tid; i < TY * TX * a.Dp; i += kDcnTileThreads) acc[i] = 0ull;
+    for (int i = tid; i < TY * TX; i += kDcnTileThreads) cnt[i] = 0u;
     __syncthreads();
 
-    const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnThreads >> a.blog2Lg;
+    const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnTileThreads >> a.blog2Lg;
     int cl[NVL];             // channel offsets inside the group
     bool vv[NVL];
 #pragma unroll
@@ -491,14 +535,18 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
 
     // the terms of R's corners that lie in this tile; gd: the lane's grad_out values
     // in binary64 (idle vectors add nothing)
+    // tile-pixel and sum-row steps from corner 0 to corner q
+    const int dpq[4] = {0, 1, TX, TX + 1};
+    const int dpr[4] = {0, a.Dp, TX * a.Dp, (TX + 1) * a.Dp};
     auto add_tile = [&](const DcnRec& R, const float (&cw)[4], const double (&gd)[NVL][VEC]) {
+        const int pb = (R.y0 - t.Iy0) * TX + (R.x0 - t.Ix0);   // corner 0 (may lie outside)
+        const int rb = pb * a.Dp;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (!(R.flags >> (5 + q) & 1u)) continue;
-            const int p = (R.y0 + (q >> 1) - t.Iy0) * TX + (R.x0 + (q & 1) - t.Ix0);
-            atomicAdd(&cnt[p], 1u);        // once per lane of the group: bLg per term
+            atomicAdd(&cnt[pb + dpq[q]], 1u);     // once per lane of the group: bLg per term
             const double ws = (double)(cw[q] * R.m) * scale;
-            unsigned long long* row = acc + p * a.Dp;
+            unsigned long long* row = acc + (rb + dpr[q]);
 #pragma unroll
             for (int u = 0; u < NVL; ++u) {
                 if (!vv[u]) continue;
@@ -597,7 +645,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
         const int nw = w1 - w0 + 1;
         const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
         const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
-        for (int base = wave * kWave; base < nh; base += kDcnThreads) {    // wave-uniform
+        for (int base = wave * kWave; base < nh; base += kDcnTileThreads) {    // wave-uniform
             const int idx = base + lane;
             int oh, ow;
             divmod_small(idx < nh ? idx : base, nw, inv_nw, oh, ow);
@@ -660,7 +708,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     __syncthreads();
     const double inv = ldexp(1.0, -E);
     const int cols = t.Ix1 - t.Ix0, npx = (t.Iy1 - t.Iy0) * cols;
-    for (int i = tid; i < npx * a.D; i += kDcnThreads) {
+    for (int i = tid; i < npx * a.D; i += kDcnTileThreads) {
         const int p = i / a.D, c = i - (i / a.D) * a.D;
         const int py = p / cols, px = p - (p / cols) * cols;
         const int tp = py * TX + px;
@@ -736,10 +784,10 @@ hipError_t dcn_fwd_dispatch_nv(const DcnArgs& a, int nv, hipStream_t st) {
 template <typename T, int VEC, int NVL, bool GOV>
 hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
     const unsigned blocks = (unsigned)((int64_t)a.N * a.tiles_y * a.tiles_x * a.G);
-    hipLaunchKernelGGL(dcn_bound_kernel, dim3(kDcnBoundBlocks), dim3(kDcnThreads), 0, st, a);
+    hipLaunchKernelGGL(dcn_bound_kernel, dim3(kBoundGrid), dim3(kBoundThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV>), dim3(blocks), dim3(kDcnThreads), lds, st, a);
+    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV>), dim3(blocks), dim3(kDcnTileThreads), lds, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dcn_far_kernel<T, VEC, NVL, GOV>), dim3(1024), dim3(kDcnThreads), 0, st, a);
@@ -764,17 +812,24 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
         return launch_fill_zero(a.grad_input, (int64_t)a.N * a.H * a.W * a.C, stream);
     const hipError_t e = launch_fill_zero(a.ctrl, 4, stream);
     if (e != hipSuccess) return e;
+    // vectors per lane (the host's choice)
+    auto by_nvl = [&](auto tv, auto vv, auto gv) -> hipError_t {
+        using T = decltype(tv);
+        constexpr int V = decltype(vv)::value;
+        constexpr bool G = decltype(gv)::value;
+        switch (a.bNVL) {
+            case 1: return dcn_bwd_launch<T, V, 1, G>(a, lds_bytes, stream);
+            case 2: return dcn_bwd_launch<T, V, 2, G>(a, lds_bytes, stream);
+            default: return hipErrorInvalidValue;
+        }
+    };
+    using I1 = std::integral_constant<int, 1>;
     return with_elem(in_dtype, [&](auto t) {
         using T = decltype(t);
-        constexpr int V = sizeof(T) == 2 ? 8 : 4;
-        if (vec == V && a.go_vec4)
-            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2, true>(a, lds_bytes, stream)
-                               : dcn_bwd_launch<T, V, 1, true>(a, lds_bytes, stream);
-        if (vec == V)
-            return a.bNVL == 2 ? dcn_bwd_launch<T, V, 2, false>(a, lds_bytes, stream)
-                               : dcn_bwd_launch<T, V, 1, false>(a, lds_bytes, stream);
-        return a.bNVL == 2 ? dcn_bwd_launch<T, 1, 2, false>(a, lds_bytes, stream)
-                           : dcn_bwd_launch<T, 1, 1, false>(a, lds_bytes, stream);
+        using V = std::integral_constant<int, sizeof(T) == 2 ? 8 : 4>;
+        if (vec == V::value && a.go_vec4) return by_nvl(t, V{}, std::true_type{});
+        if (vec == V::value) return by_nvl(t, V{}, std::false_type{});
+        return by_nvl(t, I1{}, std::false_type{});
     });
 }
 

@@ -169,9 +169,10 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
     plan.lds_bytes = da::dcn_tile_lds_bytes(ty, tx, a.Dp);
     // at most every sample of one (image, group) plane adds to one tile sum
     a.log2_terms = std::max(10, log2i((int)std::min<int64_t>(ho * wo * a.K, 1 << 30)) + 1);
-    // backward: two vectors per lane where the group has them (fewer lanes repeat
-    // each sample's stencil)
-    a.bNVL = dv >= 2 ? 2 : 1;
+    // backward: up to 8 channels per lane, two vectors where the group has them
+    // (fewer lanes repeat each sample's stencil; more channels per lane cost the
+    // registers that keep six waves per SIMD)
+    a.bNVL = (dv >= 2 && vec <= 4) ? 2 : 1;
     a.bLg = next_pow2((dv + a.bNVL - 1) / a.bNVL);
     a.blog2Lg = log2i(a.bLg);
     plan.vec = vec;

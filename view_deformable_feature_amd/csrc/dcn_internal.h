@@ -61,7 +61,8 @@ constexpr int kDcnRecBytes = 32;   // one sample's stencil record
 // Dynamic LDS of the backward tile kernel: the [TY*TX][Dp] 64-bit sums, the number of
 // terms each tile pixel took (32-bit, padded to 16 bytes), and per wave a list of up to
 // 64 accepted ring candidates (kDcnListWords words each).
-constexpr int kDcnBwdWaves = 4;
+constexpr int kDcnTileThreads = 512;   // backward tile kernel workgroup
+constexpr int kDcnBwdWaves = kDcnTileThreads / 64;
 constexpr int kDcnListWords = 5;
 inline size_t dcn_tile_lds_bytes(int ty, int tx, int dp) {
     return (size_t)ty * tx * dp * 8 + ((size_t)ty * tx + 3) / 4 * 16 +
