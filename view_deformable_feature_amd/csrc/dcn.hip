@@ -243,10 +243,20 @@ __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t,
         const bool own = img && cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1;
         f |= (img ? 1u : 0u) << (1 + q);
         f |= (own ? 1u : 0u) << (5 + q);
-        if (home) {
+    }
+    // With -M <= dy <= M every corner row cy satisfies gy - M <= cy <= gy + M + 1
+    // (binary32 rounding of gy + dy is monotonic and gy +- M is exact), so gy lies
+    // in the row window of the corner's tile; the same for x.  Only a sample with a
+    // larger offset (or none at all) can have a far corner.
+    const float fm = (float)a.M;
+    if (home && !(o.dy >= -fm && o.dy <= fm && o.dx >= -fm && o.dx <= fm)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cy = r.y0 + (q >> 1), cx = r.x0 + (q & 1);
             const int oy = cy & -a.TY, ox = cx & -a.TX;     // origin of the corner's tile
             const bool reach = gy >= oy - a.M - 1 && gy <= oy + a.TY - 1 + a.M &&
                                gx >= ox - a.M - 1 && gx <= ox + a.TX - 1 + a.M;
+            const bool img = f >> (1 + q) & 1u, own = f >> (5 + q) & 1u;
             f |= (img && !own && !reach ? 1u : 0u) << (9 + q);
         }
     }
@@ -526,11 +536,11 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     // byte steps from corner 0 to corner q, and of the lane's vectors
     const uint32_t cq[4] = {0u, (uint32_t)(a.C * kElem), (uint32_t)(a.W * a.C * kElem),
                             (uint32_t)((a.W + 1) * a.C * kElem)};
-    uint32_t clb[NVL], vvb[NVL];
+    uint32_t clb[NVL], vvm[NVL];
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
         clb[u] = (uint32_t)(cl[u] * kElem);
-        vvb[u] = vv[u] ? 1u : 0u;
+        vvm[u] = vv[u] ? ~0u : 0u;
     }
 
     // the terms of R's corners that lie in this tile; gd: the lane's grad_out values
@@ -595,8 +605,9 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
                 load_go<VEC, GOV>(a, (uint32_t)pix * (uint32_t)a.C + gD + cl[u], go[u]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t at = ib0 + cq[q] + clb[u];
-                    const uint32_t off = (R.flags >> (1 + q) & vvb[u]) ? at : a.in_bytes;
+                    // all ones when the corner is in the image and the vector exists
+                    const uint32_t m = (0u - (R.flags >> (1 + q) & 1u)) & vvm[u];
+                    const uint32_t off = ((ib0 + cq[q] + clb[u]) & m) | (a.in_bytes & ~m);
                     VecLoad<T, VEC>::run(r_in, off, 0u, v[u][q]);
                 }
             }
