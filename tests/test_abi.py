@@ -329,6 +329,9 @@ def test_dcn_out_size(lib):
     (dict(channels=1 << 17, groups=1), 2, "2^16"),
     (dict(channels=2048, groups=4), 2, "channels per group"),
     (dict(batch=64, height=1024, width=1024, channels=64, groups=4), 2, "4 GiB"),
+    # a 1x1 input padded to a 39999x39999 output: out and offset_mask reach 4 GiB
+    (dict(batch=1, height=1, width=1, channels=1, groups=1, pad_h=20000, pad_w=20000), 2,
+     "offset_mask"),
 ])
 def test_dcn_rejects_malformed_problem(lib, kw, code, needle):
     assert _dcn_fwd(lib, _dprob(**kw)) == code

@@ -193,3 +193,33 @@ def test_dcn_grad_input_repeatable_without_far_corners():
     assert all(torch.equal(runs[0], r) for r in runs[1:])
     r_gi, _ = oracle.dcn_backward(inp["input"], om, inp["grad_out"], **_conf(wl))
     assert_close("repeatable grad_input", runs[0].numpy(), r_gi, TOL_BWD)
+
+
+def test_dcn_unaligned_views():
+    """input, offset_mask and grad_out as views one element into larger buffers: one
+    channel per lane vector, the bound kernel's element-wise scans and element-wise
+    grad_out loads, each against the oracle."""
+    import view_deformable_feature_amd as vdf
+    wl = _wl("c40_g5")
+    inp = W.make_dcn_inputs(wl)
+    x, om = _dev(inp)
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+
+    def shifted(t):
+        buf = torch.zeros(t.numel() + 1, device="cuda", dtype=t.dtype)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    xv, omv, gov = shifted(x), shifted(om), shifted(go)
+    assert xv.data_ptr() % 16 and omv.data_ptr() % 16 and gov.data_ptr() % 16
+    say("[dcn] unaligned views c40_g5")
+    out = vdf.dcn_forward(xv, omv, **_conf(wl))
+    gi, gom = vdf.dcn_backward(xv, omv, gov, **_conf(wl))
+    torch.cuda.synchronize()
+    assert_close("unaligned out", out.cpu().numpy(),
+                 oracle.dcn_forward(inp["input"], inp["offset_mask"], **_conf(wl)), TOL_FWD)
+    r_gi, r_gom = oracle.dcn_backward(inp["input"], inp["offset_mask"], inp["grad_out"],
+                                      **_conf(wl))
+    assert_close("unaligned grad_input", gi.cpu().numpy(), r_gi, TOL_BWD)
+    assert_close("unaligned grad_om", gom.cpu().numpy(), r_gom, TOL_BWD)
