@@ -13,7 +13,12 @@ four corners, locations, weights, outputs; backward also the feature-gradient
 payload of every (sample, corner, channel) term) over the HIP-event time of
 that call; traffic is the counter-measured HBM bytes of the same call from
 profiles/traffic_nuscenes.json while the kernel sources are unchanged.  cpu_baseline is the
-plain fp64 C oracle, single-threaded, on the same workload.
+plain fp64 C oracle, single-threaded, on the same workload (with the host's CPU
+model and core counts); cpu_baseline_forward_parallel times the oracle's forward
+spread over all usable host cores.  copy_reference is a plain device copy's rate,
+and each roofline entry also gives its fraction of that (frac_of_copy).  --cold
+adds per-call times after a 512 MiB write that evicts the inputs from L2 and the
+MALL.
 """
 from __future__ import annotations
 
@@ -91,6 +96,66 @@ def algorithmic_bytes(wl, out_bytes=4):
     return b_fwd, b_bwd
 
 
+def host_info():
+    """CPU model and core counts of the host that runs the oracle baselines."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu": model, "nproc": os.cpu_count(), "usable_cores": usable}
+
+
+def cpu_forward_parallel(wl, inp, min_seconds=3.0):
+    """The oracle's forward spread over the host's usable cores by anchor (OpenMP,
+    race-free: every anchor writes its own row); a second CPU reference beside the
+    one-thread loop, forward only."""
+    import oracle
+    args = [inp[k] for k in ("feat", "spatial_shape", "scale_start_index", "loc", "weights")]
+    threads = host_info()["usable_cores"] or 1
+    oracle.forward_parallel(*args, threads=threads)          # warm up, spawn the threads
+    reps, t0, used = 0, time.perf_counter(), 0
+    while True:
+        _, used = oracle.forward_parallel(*args, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return dict(value=wl.sample_channels * reps / el, unit="sample-channels/s", cores=used,
+                kind="oracle, forward only, OpenMP over anchors",
+                sample=f"full {wl.name} workload, forward, {reps} passes in {el:.1f} s")
+
+
+def copy_reference(nbytes=1 << 30, reps=10):
+    """GB/s (bytes read + written) of a plain device-to-device copy of nbytes: what a
+    pure streaming kernel reaches on this GPU, printed beside the vendor peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return {"achieved": round(2 * nbytes / float(np.median(ts)) / 1e9, 1), "unit": "GB/s",
+            "bytes_per_copy": nbytes, "kind": "device-to-device copy, read + write, median of "
+                                              f"{reps}"}
+
+
 def cpu_baseline(wl, inp, min_seconds=10.0):
     """Time the fp64 oracle (forward + backward) on the host; single-threaded C."""
     import oracle
@@ -107,7 +172,7 @@ def cpu_baseline(wl, inp, min_seconds=10.0):
     return dict(value=wl.sample_channels * reps / el, unit="sample-channels/s", cores=1,
                 kind="oracle",
                 sample=f"full {wl.name} workload, forward + backward, {reps} passes in {el:.1f} s "
-                       f"(fp64 C loop, one thread)")
+                       f"(fp64 C loop, one thread)", host=host_info())
 
 
 def bench_pack(args):
@@ -302,6 +367,9 @@ def main():
                     help="element type of out and grad_out (binary32 arithmetic throughout)")
     ap.add_argument("--deterministic", action="store_true",
                     help="run the backward in its deterministic (64-bit fixed-point) form")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each call after writing a 512 MiB buffer (L2 and MALL "
+                         "hold none of the inputs)")
     ap.add_argument("--op", default="aggregate", choices=("aggregate", "pack", "dcn"),
                     help="aggregate: forward + backward step (the headline); pack: level "
                          "packing and unpacking of the workload's feature maps; dcn: the "
@@ -431,8 +499,37 @@ def main():
         if dominant == "backward" else roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
         "roofline_forward": roof(b_fwd, fwd_s, FWD_KERNELS, "forward"),
     }
+    rec["forward"]["median_us"] = float(np.median(t_fwd)) * 1e6
+    rec["backward"]["median_us"] = float(np.median(t_bwd)) * 1e6
+    if args.cold:
+        # a 512 MiB write between calls evicts the inputs from L2 and the MALL
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        cf, cb = [], []
+        for _ in range(max(5, args.steps // 5)):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush.fill_(0.0)
+            e[0].record()
+            vdf.da_forward(feat, shape, start, loc, w, out=out, workspace=fws)
+            e[1].record()
+            flush.fill_(1.0)
+            e[2].record()
+            vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                            grad_weights=gw, workspace=bws, deterministic=det)
+            e[3].record()
+            torch.cuda.synchronize()
+            cf.append(e[0].elapsed_time(e[1]) * 1e-3)
+            cb.append(e[2].elapsed_time(e[3]) * 1e-3)
+        del flush
+        rec["cold"] = {"forward_median_us": float(np.median(cf)) * 1e6,
+                       "backward_median_us": float(np.median(cb)) * 1e6,
+                       "calls": len(cf), "flush_bytes": 512 << 20}
+    cref = copy_reference()
+    rec["copy_reference"] = cref
+    for key in ("roofline", "roofline_forward"):
+        rec[key]["frac_of_copy"] = round(rec[key]["achieved"] / cref["achieved"], 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        rec["cpu_baseline_forward_parallel"] = cpu_forward_parallel(wl, inp)
     print(json.dumps(rec), flush=True)
 
 

@@ -39,6 +39,7 @@
  * (no fast-math: the binary32 pixel coordinate must be rounded twice).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -242,6 +243,26 @@ int oracle_forward(ORACLE_PROBLEM_ARGS, const int64_t* anchor_ids, int64_t n_ids
         if (id < 0 || id >= bs * A) return 1;
         forward_anchor(&pb, id / A, id % A, out + i * C);
     }
+    return 0;
+}
+
+/* Forward of every anchor, spread over `threads` OpenMP threads by (b, a): each
+ * anchor writes only its own out row, so the result equals oracle_forward's bit
+ * for bit.  *threads_used receives the thread count of the parallel region.
+ * Used only to time the definition on all host cores beside the one-thread loop. */
+int oracle_forward_parallel(ORACLE_PROBLEM_ARGS, int threads, double* out, int* threads_used) {
+    ORACLE_FILL_PROBLEM(pb);
+    if (check_problem(&pb) || threads < 1) return 1;
+    const int64_t n = bs * A;
+    int used = 1;
+#pragma omp parallel num_threads(threads)
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < n; ++i) forward_anchor(&pb, i / A, i % A, out + i * C);
+    }
+    if (threads_used) *threads_used = used;
     return 0;
 }
 

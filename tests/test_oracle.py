@@ -414,3 +414,16 @@ def test_rejects_malformed_problem():
     bad["scale_start_index"] = np.array([[1]], np.int32)      # 1 + 256 > num_feat
     with pytest.raises(ValueError):
         oracle.forward(*_args(bad))
+
+
+@pytest.mark.parametrize("threads", [1, 3])
+def test_forward_parallel_equals_forward(threads):
+    """The OpenMP forward (a timing reference only) gives the one-thread loop's
+    result bit for bit: each anchor's row is formed by the same code, in the same
+    order, by one thread."""
+    inp = W.make_inputs(W.WORKLOADS["nuscenes_fwd"])
+    args = [inp[k] for k in ("feat", "spatial_shape", "scale_start_index", "loc", "weights")]
+    seq = oracle.forward(*args)
+    par, used = oracle.forward_parallel(*args, threads=threads)
+    assert used == threads
+    assert np.array_equal(seq, par)
