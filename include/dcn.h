@@ -92,10 +92,12 @@ DA_API da_status dcn_backward_workspace_size(const dcn_problem* problem, size_t*
  *                     matter.
  * The input gradient is summed tile by tile in LDS by the workgroup that owns the
  * tile, in 64-bit fixed point (each term rounded once to a multiple of 2^-E, E from
- * max|grad_out| * max|m| so that no sum can overflow: about 2^-49 of that bound as
- * resolution), and stored once; only corners carried more than 4 pixels past their
- * tile are added afterwards with binary32 atomics.  grad_offset_mask is
- * deterministic, and so is grad_input when no corner is that far.  Same errors as dcn_forward,
+ * max|grad_out| * max|m| and from the most terms one sum can take, so that no sum can
+ * overflow: a resolution of 2^-46 to 2^-45 of that bound for a 56x56 output and a 3x3
+ * kernel, finer for fewer output pixels), and stored once; only corners carried more
+ * than 4 pixels past their tile are added afterwards with binary32 atomics.
+ * grad_offset_mask is deterministic, and so is grad_input when no corner is that far.
+ * Same errors as dcn_forward,
  * plus DA_ERR_UNSUPPORTED for 2^30 samples (N*Ho*Wo*G*K) or more and
  * DA_ERR_INVALID_ARG for a missing, misaligned or small workspace.
  */

@@ -184,14 +184,12 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_forward_kernel(DcnArgs a) {
 
 struct DcnRec {
     int32_t pix;        // output pixel
-    int32_t k;          // tap
     float m;            // modulation scalar
     float ly, lx;       // fractions over the low corner
     int32_t y0, x0;     // low corner (meaningful when inside)
     uint32_t flags;     // bit 0 inside; bit 1 + q: corner q in the image; bit 5 + q: in this
                         // tile; bit 9 + q: far (no tile's ring reaches it; home samples only)
 };
-static_assert(sizeof(DcnRec) == kDcnRecBytes, "record size");
 
 // Output indices o in [0, O) whose grid coordinate o*S - P + off lies in [lo, hi].
 __device__ __forceinline__ void out_range(int lo, int hi, int S, int P, int off, int O, int& o_lo,
@@ -222,11 +220,10 @@ __device__ __forceinline__ DcnOm load_om(const DcnArgs& a, int pix, int g, int k
 // tile's window.  Tile sides are powers of two, and the flags are formed without
 // branches, so the records of several samples are formed side by side.
 __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t, int pix, int gy,
-                                             int gx, int k, const DcnOm& o, bool home) {
+                                             int gx, const DcnOm& o, bool home) {
 #pragma clang fp contract(off)
     DcnRec r;
     r.pix = pix;
-    r.k = k;
     r.m = o.m;
     const float y = (float)gy + o.dy, x = (float)gx + o.dx;
     const bool inside = y > -1.0f && x > -1.0f && y < (float)a.H && x < (float)a.W;
@@ -455,23 +452,28 @@ __device__ __forceinline__ void divmod_small(int idx, int n, float inv, int& q, 
     }
 }
 
-// group_sum of four values at once (one test of the group width per step)
+// group_sum of four values at once over groups of n lanes (a power of two): the
+// set bits of n - 1 are the steps to take, tested on one scalar per step
 __device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
+    const uint32_t steps = (uint32_t)n - 1u;
+    if (steps & 1u)
 #pragma unroll
-    for (int step = 0; step < 6; ++step) {
-        if (n <= (1 << step)) break;
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0xB1, 0xF>(v[q]);     // quad_perm [1,0,3,2]
+    if (steps & 2u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            switch (step) {
-                case 0: v[q] += dpp<0xB1, 0xF>(v[q]); break;     // quad_perm [1,0,3,2]
-                case 1: v[q] += dpp<0x4E, 0xF>(v[q]); break;     // quad_perm [2,3,0,1]
-                case 2: v[q] += dpp<0x141, 0xF>(v[q]); break;    // row_half_mirror
-                case 3: v[q] += dpp<0x140, 0xF>(v[q]); break;    // row_mirror
-                case 4: v[q] += dpp<0x142, 0xA>(v[q]); break;    // row_bcast:15
-                default: v[q] += dpp<0x143, 0xC>(v[q]); break;   // row_bcast:31
-            }
-        }
-    }
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0x4E, 0xF>(v[q]);     // quad_perm [2,3,0,1]
+    if (steps & 4u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0x141, 0xF>(v[q]);    // row_half_mirror
+    if (steps & 8u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0x140, 0xF>(v[q]);    // row_mirror
+    if (steps & 16u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0x142, 0xA>(v[q]);    // row_bcast:15
+    if (steps & 32u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += dpp<0x143, 0xC>(v[q]);    // row_bcast:31
 }
 
 // Lanes: in the home loop a group of bLg lanes takes one sample at a time; lane jj
@@ -584,7 +586,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
             int oh, ow;
             divmod_small(idx, nw, inv_nw, oh, ow);
             const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
-            const DcnRec R = dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox, k,
+            const DcnRec R = dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox,
                                         load_om(a, pix, t.g, k), true);
             if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
                 const uint32_t sid = ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
@@ -665,7 +667,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
             const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
             const bool cand = idx < nh && !(cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1);
             const DcnOm o = cand ? load_om(a, pix, t.g, k) : DcnOm{0.0f, 0.0f, 0.0f};
-            const DcnRec R = dcn_record(a, t, pix, gy, gx, k, o, false);
+            const DcnRec R = dcn_record(a, t, pix, gy, gx, o, false);
             const bool take = cand && (R.flags >> 5) != 0u;
             const unsigned long long mask = __ballot(take);
             if (take) {
@@ -752,7 +754,7 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         TileCtx t{n, g, 0, 0, 0, 0};            // empty tile: no corner counts as owned
         const DcnRec R = dcn_record(a, t, pix, ho * a.SH - a.PH + ki * a.DH,
-                                    wo * a.SW - a.PW + kj * a.DW, k, load_om(a, pix, g, k), false);
+                                    wo * a.SW - a.PW + kj * a.DW, load_om(a, pix, g, k), false);
         float cw[4];
         corner_weights(R, cw);
         const float w = cw[q] * R.m;

@@ -57,7 +57,6 @@ hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, h
 // lds_bytes: the tile kernel's dynamic LDS.
 hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream);
-constexpr int kDcnRecBytes = 32;   // one sample's stencil record
 // Dynamic LDS of the backward tile kernel: the [TY*TX][Dp] 64-bit sums, the number of
 // terms each tile pixel took (32-bit, padded to 16 bytes), and per wave a list of up to
 // 64 accepted ring candidates (kDcnListWords words each).
