@@ -223,3 +223,27 @@ def test_dcn_unaligned_views():
                                       **_conf(wl))
     assert_close("unaligned grad_input", gi.cpu().numpy(), r_gi, TOL_BWD)
     assert_close("unaligned grad_om", gom.cpu().numpy(), r_gom, TOL_BWD)
+
+
+def test_dcn_hand_worked_golden():
+    """The hand-worked problem of tests/golden/hand_dcn_1x2_taps_two_groups.json
+    through the HIP path, against its printed values."""
+    import json
+    import os
+    import view_deformable_feature_amd as vdf
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_dcn_1x2_taps_two_groups.json")
+    with open(path) as f:
+        g = json.load(f)
+    conf = dict(groups=g["groups"], kernel=tuple(g["kernel"]), stride=tuple(g["stride"]),
+                pad=tuple(g["pad"]), dilation=tuple(g["dilation"]))
+    x = torch.tensor(g["input"], dtype=torch.float32, device="cuda")
+    om = torch.tensor(g["offset_mask"], dtype=torch.float32, device="cuda")
+    go = torch.tensor(g["grad_out"], dtype=torch.float32, device="cuda")
+    say("[dcn] hand-worked golden")
+    out = vdf.dcn_forward(x, om, **conf)
+    gi, gom = vdf.dcn_backward(x, om, go, **conf)
+    torch.cuda.synchronize()
+    assert_close("golden out", out.cpu().numpy(), np.array(g["expect_out"]), TOL_FWD)
+    assert_close("golden grad_input", gi.cpu().numpy(), np.array(g["expect_grad_input"]), TOL_BWD)
+    assert_close("golden grad_om", gom.cpu().numpy(), np.array(g["expect_grad_offset_mask"]),
+                 TOL_BWD)

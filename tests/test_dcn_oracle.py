@@ -189,3 +189,28 @@ def test_rejects_malformed():
         oracle.dcn_forward(x, np.zeros((1, 4, 4, 2, 26), np.float32), 2)   # bad last dim
     with pytest.raises(ValueError):
         oracle.dcn_out_size(2, 2, kernel=5, pad=0)
+
+
+def _golden_dcn():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_dcn_1x2_taps_two_groups.json")
+    with open(path) as f:
+        g = json.load(f)
+    conf = dict(groups=g["groups"], kernel=tuple(g["kernel"]), stride=tuple(g["stride"]),
+                pad=tuple(g["pad"]), dilation=tuple(g["dilation"]))
+    arr = {k: np.array(g[k], dtype=np.float32) for k in ("input", "offset_mask", "grad_out")}
+    return g, conf, arr
+
+
+def test_hand_worked_golden():
+    """tests/golden/hand_dcn_1x2_taps_two_groups.json: a 1x2-tap, stride-2, two-group
+    problem worked by hand (affine and bilinear channels, a position in (-1, 0) with
+    one corner in the image, a position past the right border); every value is exact
+    in binary64."""
+    g, conf, a = _golden_dcn()
+    out = oracle.dcn_forward(a["input"], a["offset_mask"], **conf)
+    gi, gom = oracle.dcn_backward(a["input"], a["offset_mask"], a["grad_out"], **conf)
+    assert np.array_equal(out, np.array(g["expect_out"]))
+    assert np.array_equal(gi, np.array(g["expect_grad_input"]))
+    assert np.array_equal(gom, np.array(g["expect_grad_offset_mask"]))
