@@ -649,6 +649,45 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     // ---- ring: other tiles' samples whose grid point lies in this tile's window ----
     const int gpw = kWave >> a.blog2Lg;              // lane groups per wave
     const int grp = lane >> a.blog2Lg;
+    // The wave's list collects the accepted candidates of every tap and is drained
+    // (each lane group taking listed samples one at a time) only when the next batch
+    // would not fit, and once at the end: one tap accepts only a few candidates per
+    // wave, and draining after each would leave most lane groups idle.  The list is
+    // written and read by this wave only, and LDS executes one wave's instructions
+    // in order: no barrier, only no reordering across the writes and reads.
+    int n_list = 0;                                  // wave-uniform
+    auto drain = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        for (int r = grp; r < n_list; r += gpw) {
+            DcnRec L;
+            L.pix = (int)wl[r];
+            L.m = __uint_as_float(wl[kWave + r]);
+            L.ly = __uint_as_float(wl[2 * kWave + r]);
+            L.lx = __uint_as_float(wl[3 * kWave + r]);
+            const uint32_t pk = wl[4 * kWave + r];
+            L.y0 = (int)(pk & 0xffu) - 1 + t.Iy0;
+            L.x0 = (int)(pk >> 8 & 0xffu) - 1 + t.Ix0;
+            L.flags = pk >> 16;
+            float cw[4];
+            corner_weights(L, cw);
+            double gd[NVL][VEC];
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                float go[VEC];
+                if (vv[u]) {
+                    load_go<VEC, GOV>(a, (uint32_t)L.pix * (uint32_t)a.C + gD + cl[u], go);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) go[e] = 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gd[u][e] = (double)go[e];
+            }
+            add_tile(L, cw, gd);
+        }
+        __builtin_amdgcn_wave_barrier();            // the list is rewritten next
+        n_list = 0;
+    };
     for (int k = 0; k < a.K; ++k) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
@@ -670,8 +709,10 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
             const DcnRec R = dcn_record(a, t, pix, gy, gx, o, false);
             const bool take = cand && (R.flags >> 5) != 0u;
             const unsigned long long mask = __ballot(take);
+            const int n_take = __popcll(mask);
+            if (n_list + n_take > kWave) drain();
             if (take) {
-                const int r = (int)__builtin_amdgcn_mbcnt_hi(
+                const int r = n_list + (int)__builtin_amdgcn_mbcnt_hi(
                     (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
                 wl[r] = (uint32_t)pix;
                 wl[kWave + r] = __float_as_uint(R.m);
@@ -682,40 +723,10 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
                 wl[4 * kWave + r] = (uint32_t)(R.y0 - t.Iy0 + 1) | (uint32_t)(R.x0 - t.Ix0 + 1) << 8 |
                                     (R.flags & 0x1e1u) << 16;
             }
-            // the list is written and read by this wave only, and LDS executes one
-            // wave's instructions in order: no barrier, only no reordering
-            __builtin_amdgcn_wave_barrier();
-            const int n_take = __popcll(mask);
-            for (int r = grp; r < n_take; r += gpw) {
-                DcnRec L;
-                L.pix = (int)wl[r];
-                L.m = __uint_as_float(wl[kWave + r]);
-                L.ly = __uint_as_float(wl[2 * kWave + r]);
-                L.lx = __uint_as_float(wl[3 * kWave + r]);
-                const uint32_t pk = wl[4 * kWave + r];
-                L.y0 = (int)(pk & 0xffu) - 1 + t.Iy0;
-                L.x0 = (int)(pk >> 8 & 0xffu) - 1 + t.Ix0;
-                L.flags = pk >> 16;
-                float cw[4];
-                corner_weights(L, cw);
-                double gd[NVL][VEC];
-#pragma unroll
-                for (int u = 0; u < NVL; ++u) {
-                    float go[VEC];
-                    if (vv[u]) {
-                        load_go<VEC, GOV>(a, (uint32_t)L.pix * (uint32_t)a.C + gD + cl[u], go);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) go[e] = 0.0f;
-                    }
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) gd[u][e] = (double)go[e];
-                }
-                add_tile(L, cw, gd);
-            }
-            __builtin_amdgcn_wave_barrier();      // the next pass rewrites the list
+            n_list += n_take;
         }
     }
+    drain();
 
     // ---- store the tile ----
     __syncthreads();
@@ -832,7 +843,9 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
         constexpr bool G = decltype(gv)::value;
         switch (a.bNVL) {
             case 1: return dcn_bwd_launch<T, V, 1, G>(a, lds_bytes, stream);
-            case 2: return dcn_bwd_launch<T, V, 2, G>(a, lds_bytes, stream);
+            case 2:       // two vectors per lane only where a vector holds 4 channels or fewer
+                if constexpr (V <= 4) return dcn_bwd_launch<T, V, 2, G>(a, lds_bytes, stream);
+                return hipErrorInvalidValue;
             default: return hipErrorInvalidValue;
         }
     };
