@@ -13,8 +13,24 @@ import numpy as np
 GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
+def _with_keys(*keys):
+    out = []
+    for p in sorted(glob.glob(os.path.join(GOLDEN_DIR, "*.json"))):
+        with open(p) as f:
+            d = json.load(f)
+        if all(k in d for k in keys):
+            out.append(p)
+    return out
+
+
 def fixture_paths():
-    return sorted(glob.glob(os.path.join(GOLDEN_DIR, "*.json")))
+    """The deformable-aggregation fixtures (features, locations, weights)."""
+    return _with_keys("feat", "loc", "weights")
+
+
+def dcn_fixture_paths():
+    """The deformable-convolution fixtures (input, offset_mask)."""
+    return _with_keys("input", "offset_mask")
 
 
 def load(path):
