@@ -328,7 +328,8 @@ def bench_dcn(args):
                       "sample_channels_per_step": sc, "out_dtype": args.out_dtype},
            "forward": {"avg_us": t_fwd * 1e6, "value": sc / t_fwd, "unit": "sample-channels/s"},
            "backward": {"avg_us": t_bwd * 1e6, "value": sc / t_bwd, "unit": "sample-channels/s"},
-           "roofline": roof(b_bwd, t_bwd, "dcn_backward call: fill_zero_kernel, dcn_backward_kernel"),
+           "roofline": roof(b_bwd, t_bwd, "dcn_backward call: fill_zero_kernel, dcn_bound_kernel, "
+                                          "dcn_bwd_tile_kernel, dcn_far_kernel"),
            "roofline_forward": roof(b_fwd, t_fwd, "dcn_forward_kernel")}
     if not args.no_cpu_baseline:
         import oracle
