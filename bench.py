@@ -303,8 +303,9 @@ def bench_dcn(args):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    f_all = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    b_all = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_fwd, t_bwd = float(f_all.mean()), float(b_all.mean())
     t_step = wall / args.steps
     b_fwd, b_bwd = dcn_bytes(wl, out.element_size())
     sc = wl.sample_channels
@@ -326,11 +327,17 @@ def bench_dcn(args):
            "config": {"workload": f"{wl.name}: N={wl.N}, {wl.H}x{wl.W}x{wl.C}, groups={wl.groups}, "
                                   f"kernel {wl.kernel[0]}x{wl.kernel[1]}, out {ho}x{wo}",
                       "sample_channels_per_step": sc, "out_dtype": args.out_dtype},
-           "forward": {"avg_us": t_fwd * 1e6, "value": sc / t_fwd, "unit": "sample-channels/s"},
-           "backward": {"avg_us": t_bwd * 1e6, "value": sc / t_bwd, "unit": "sample-channels/s"},
+           "forward": {"avg_us": t_fwd * 1e6, "median_us": float(np.median(f_all)) * 1e6,
+                       "value": sc / t_fwd, "unit": "sample-channels/s"},
+           "backward": {"avg_us": t_bwd * 1e6, "median_us": float(np.median(b_all)) * 1e6,
+                        "value": sc / t_bwd, "unit": "sample-channels/s"},
            "roofline": roof(b_bwd, t_bwd, "dcn_backward call: fill_zero_kernel, dcn_bound_kernel, "
                                           "dcn_bwd_tile_kernel, dcn_far_kernel"),
            "roofline_forward": roof(b_fwd, t_fwd, "dcn_forward_kernel")}
+    cref = copy_reference()
+    rec["copy_reference"] = cref
+    for key in ("roofline", "roofline_forward"):
+        rec[key]["frac_of_copy"] = round(rec[key]["achieved"] / cref["achieved"], 4)
     if not args.no_cpu_baseline:
         import oracle
         sub = W.dcn_custom(wl.name + "_sample", N=1, H=wl.H, W=wl.W, C=wl.C, groups=wl.groups,
@@ -349,7 +356,8 @@ def bench_dcn(args):
         rec["cpu_baseline"] = {"value": sub.sample_channels * reps / el, "unit": "sample-channels/s",
                                "cores": 1, "kind": "oracle",
                                "sample": f"one image of {wl.name} (1 of {wl.N}), forward + backward, "
-                                         f"{reps} passes in {el:.1f} s (fp64 C loop, one thread)"}
+                                         f"{reps} passes in {el:.1f} s (fp64 C loop, one thread)",
+                               "host": host_info()}
     print(json.dumps(rec), flush=True)
 
 
