@@ -120,12 +120,39 @@ template <int VEC>
 __device__ __forceinline__ void store_out_vec(const DcnArgs& a, int64_t i, const float (&v)[VEC]) {
     void* out = a.out;
     const int dtype = a.out_dtype;
-    if (dtype == kF32 && VEC == 4 && a.out_vec4) {
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
+    if constexpr (VEC % 4 == 0) {
+        if (a.out_vec4 && dtype == kF32) {                  // 16-byte stores
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) store_elem(out, i + e, v[e], dtype);
+            for (int h = 0; h < VEC / 4; ++h)
+                reinterpret_cast<float4*>(static_cast<float*>(out) + i)[h] =
+                    make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+            return;
+        }
+        if (a.out_vec4) {                                   // 16-bit: 8- or 16-byte stores
+            uint32_t w[VEC / 2];
+#pragma unroll
+            for (int h = 0; h < VEC / 2; ++h) {
+                const float x0 = v[2 * h], x1 = v[2 * h + 1];
+                const uint32_t lo = dtype == kBF16 ? (uint32_t)bf16_rne(x0)
+                                                   : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0);
+                const uint32_t hi = dtype == kBF16 ? (uint32_t)bf16_rne(x1)
+                                                   : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1);
+                w[h] = lo | hi << 16;
+            }
+            uint16_t* o16 = static_cast<uint16_t*>(out) + i;
+            if constexpr (VEC == 4) {
+                *reinterpret_cast<uint2*>(o16) = make_uint2(w[0], w[1]);
+            } else {
+#pragma unroll
+                for (int h = 0; h < VEC / 8; ++h)
+                    reinterpret_cast<uint4*>(o16)[h] =
+                        make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+            }
+            return;
+        }
     }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) store_elem(out, i + e, v[e], dtype);
 }
 
 template <typename T, int VEC, int NV>
@@ -261,20 +288,46 @@ __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t,
     return r;
 }
 
-// grad_out[i .. i + VEC): GOV -- binary32 with 16-byte aligned vectors (VEC a multiple
-// of 4) -- takes 16-byte loads; otherwise element loads of the run-time type go_dtype.
+// grad_out[i .. i + VEC): GOV -- 16-byte aligned rows and VEC a multiple of 4 --
+// takes 8- or 16-byte vector loads of any grad_out type (the type test is
+// wave-uniform); otherwise element loads of the run-time type go_dtype.
 template <int VEC, bool GOV>
 __device__ __forceinline__ void load_go(const DcnArgs& a, uint32_t i, float (&go)[VEC]) {
     if constexpr (GOV) {
-        static_assert(VEC % 4 == 0, "16-byte grad_out loads cover 4 channels");
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
+        static_assert(VEC % 4 == 0, "vector grad_out loads cover 4 channels or more");
+        if (a.go_dtype == kF32) {
+            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
 #pragma unroll
-        for (int h = 0; h < VEC / 4; ++h) {
-            const float4 v = p[h];
-            go[4 * h] = v.x;
-            go[4 * h + 1] = v.y;
-            go[4 * h + 2] = v.z;
-            go[4 * h + 3] = v.w;
+            for (int h = 0; h < VEC / 4; ++h) {
+                const float4 v = p[h];
+                go[4 * h] = v.x;
+                go[4 * h + 1] = v.y;
+                go[4 * h + 2] = v.z;
+                go[4 * h + 3] = v.w;
+            }
+        } else {
+            const uint16_t* p16 = static_cast<const uint16_t*>(a.grad_out) + i;
+            uint32_t w[VEC / 2];
+            if constexpr (VEC == 4) {
+                const uint2 q = *reinterpret_cast<const uint2*>(p16);
+                w[0] = q.x;
+                w[1] = q.y;
+            } else {
+#pragma unroll
+                for (int h = 0; h < VEC / 8; ++h) {
+                    const uint4 q = reinterpret_cast<const uint4*>(p16)[h];
+                    w[4 * h] = q.x;
+                    w[4 * h + 1] = q.y;
+                    w[4 * h + 2] = q.z;
+                    w[4 * h + 3] = q.w;
+                }
+            }
+            const bool bf = a.go_dtype == kBF16;
+#pragma unroll
+            for (int h = 0; h < VEC / 2; ++h) {
+                go[2 * h] = bf ? bf16_lo(w[h]) : f16_lo(w[h]);
+                go[2 * h + 1] = bf ? bf16_hi(w[h]) : f16_hi(w[h]);
+            }
         }
     } else {
 #pragma unroll

@@ -209,7 +209,7 @@ da_status dcn_forward(const dcn_problem* p, const void* input, const float* offs
     a.input = input;
     a.om = offset_mask;
     a.out = out;
-    a.out_vec4 = p->out_dtype == DA_F32 && plan.vec == 4 && aligned(out, 16);
+    a.out_vec4 = plan.vec % 4 == 0 && aligned(out, 16);
     return da::report_hip(
         da::launch_dcn_forward(a, p->in_dtype, plan.vec, plan.nv, static_cast<hipStream_t>(stream)),
         "dcn forward launch");
@@ -243,7 +243,7 @@ da_status dcn_backward(const dcn_problem* p, const void* input, const float* off
     a.grad_out = grad_out;
     a.grad_input = grad_input;
     a.grad_om = grad_offset_mask;
-    a.go_vec4 = p->out_dtype == DA_F32 && plan.vec % 4 == 0 && aligned(grad_out, 16);
+    a.go_vec4 = plan.vec % 4 == 0 && aligned(grad_out, 16);
     if (p->batch == 0) return DA_OK;
     const uint64_t need = dcn_workspace_bytes(a.n_pix * a.G * a.K);
     if (need) {

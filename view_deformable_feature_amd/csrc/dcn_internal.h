@@ -28,8 +28,8 @@ struct DcnArgs {
     int32_t N, H, W, C, G, D, KH, KW, SH, SW, PH, PW, DH, DW, Ho, Wo, K;
     int32_t Dv, Lg, log2Lg, Lp, log2Lp;
     int32_t out_dtype, go_dtype;
-    int32_t out_vec4;        // binary32 out, 16-byte aligned rows: float4 stores
-    int32_t go_vec4;         // binary32 grad_out, 16-byte aligned rows: float4 loads
+    int32_t out_vec4;        // out 16-byte aligned, VEC % 4 == 0: 8- or 16-byte vector stores
+    int32_t go_vec4;         // grad_out 16-byte aligned, VEC % 4 == 0: vector loads (any type)
     // Backward by input tiles: workgroup (n, tile, group) owns TY x TX input pixels
     // of one group and sums their gradient in LDS as 64-bit fixed point (pixel
     // stride Dp = D + 1 words).  Samples whose grid point lies within M + 1 pixels
