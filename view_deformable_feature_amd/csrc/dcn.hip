@@ -167,6 +167,41 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_forward_kernel(DcnArgs a) {
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[i][e] = 0.0f;
+    if (a.K == 9) {
+        // 3x3 kernel: a group's 27 offsets and scalars in seven 16-byte loads (the
+        // 28th float is the next record's, or outside the buffer: zero), one group
+        // at a time; each group's sum still runs over the taps in order
+        const __amdgpu_buffer_rsrc_t r_om = make_rsrc(a.om, a.om_bytes);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float rec[28];
+            const uint32_t ro = ((uint32_t)L.pix * (uint32_t)a.G + (uint32_t)L.gq[i]) * 108u;
+#pragma unroll
+            for (int j = 0; j < 7; ++j) {
+                const auto q = __builtin_amdgcn_raw_buffer_load_b128(r_om, ro + 16u * j, 0u, 0);
+                rec[4 * j] = __uint_as_float(q[0]);
+                rec[4 * j + 1] = __uint_as_float(q[1]);
+                rec[4 * j + 2] = __uint_as_float(q[2]);
+                rec[4 * j + 3] = __uint_as_float(q[3]);
+            }
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const int ki = k / 3, kj = k % 3;
+                const int gy = L.ho * a.SH - a.PH + ki * a.DH;
+                const int gx = L.wo * a.SW - a.PW + kj * a.DW;
+                const DcnStencil st = dcn_stencil(a, L.n, gy, gx, rec[2 * k + 1], rec[2 * k], L.c0[i], kElem);
+                float v[4][VEC];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    VecLoad<T, VEC>::run(r_in, L.valid[i] ? st.off[q] : a.in_bytes, 0u, v[q]);
+                const float m = rec[18 + k];
+                const float w0 = m * st.cw[0], w1 = m * st.cw[1], w2 = m * st.cw[2], w3 = m * st.cw[3];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    acc[i][e] += w0 * v[0][e] + w1 * v[1][e] + w2 * v[2][e] + w3 * v[3][e];
+            }
+        }
+    } else
     for (int k = 0; k < a.K; ++k) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         const int gy = L.ho * a.SH - a.PH + ki * a.DH;

@@ -128,6 +128,7 @@ da_status plan_dcn(const dcn_problem* p, const void* input, DcnPlan& plan) {
     a.n_pix = n_pix;
     a.in_bytes = (uint32_t)in_bytes;
     a.gi_bytes = (uint32_t)gi_bytes;
+    a.om_bytes = (uint32_t)om_bytes;
     a.N = (int32_t)p->batch;
     a.H = (int32_t)p->height;
     a.W = (int32_t)p->width;

@@ -25,6 +25,7 @@ struct DcnArgs {
     int64_t n_pix;           // N * Ho * Wo
     uint32_t in_bytes;       // buffer range of input; also the "outside" offset
     uint32_t gi_bytes;       // buffer range of grad_input
+    uint32_t om_bytes;       // buffer range of offset_mask
     int32_t N, H, W, C, G, D, KH, KW, SH, SW, PH, PW, DH, DW, Ho, Wo, K;
     int32_t Dv, Lg, log2Lg, Lp, log2Lp;
     int32_t out_dtype, go_dtype;
