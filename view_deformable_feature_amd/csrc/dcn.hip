@@ -420,6 +420,28 @@ __global__ void __launch_bounds__(kBoundThreads) dcn_bound_kernel(DcnArgs a) {
             mg = max(mg, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
                              max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
         }
+    } else if (a.go_vec4 && (n_go & 7u) == 0) {      // 16-bit: 16-byte loads of 8 values
+        const uint4* g8 = static_cast<const uint4*>(a.grad_out);
+        const uint32_t n8 = n_go / 8;
+        const bool bf = a.go_dtype == kBF16;
+        auto take8 = [&](const uint4& q) {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float x0 = bf ? bf16_lo(w[h]) : f16_lo(w[h]);
+                const float x1 = bf ? bf16_hi(w[h]) : f16_hi(w[h]);
+                mg = max(mg, max(__float_as_uint(fabsf(x0)), __float_as_uint(fabsf(x1))));
+            }
+        };
+        uint32_t i = i0;
+        for (; i + (U - 1) * stride < n8; i += U * stride) {
+            uint4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = g8[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u) take8(v[u]);
+        }
+        for (; i < n8; i += stride) take8(g8[i]);
     } else {
         for (uint32_t i = i0; i < n_go; i += stride)
             mg = max(mg, __float_as_uint(fabsf(load_elem(a.grad_out, i, a.go_dtype))));
