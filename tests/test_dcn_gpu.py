@@ -31,6 +31,12 @@ CASES = {
     "c512_g16": dict(N=1, H=5, W=6, C=512, groups=16),             # two groups per lane
     "far": dict(N=1, H=8, W=8, C=16, groups=4, offset_sigma=6.0),  # many positions outside
     "d3_pad3": dict(N=1, H=11, W=10, C=32, groups=4, pad=(3, 3), dilation=(3, 3)),
+    # several tiles with ragged right and bottom edges, at stride 2
+    "tiles_s2": dict(N=2, H=37, W=45, C=64, groups=4, stride=(2, 2)),
+    # a 5x5 kernel with dilation 2 (the generic tap loop) across several tiles
+    "k5_d2": dict(N=1, H=29, W=35, C=32, groups=2, kernel=(5, 5), pad=(4, 4), dilation=(2, 2)),
+    # offsets of sigma 15 px: most corners leave the image or go to the far list
+    "far_all": dict(N=1, H=40, W=40, C=16, groups=2, offset_sigma=15.0),
 }
 
 
