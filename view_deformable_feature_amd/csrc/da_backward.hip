@@ -506,6 +506,8 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
     bucket_sample(a, st, (int64_t)b, (int64_t)ba, q);
 }
 
+constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot products for G <= 8
+
 // One thread per sample q: from the per-corner group dot products
 // d[c][g] = sum over the channels of group g of grad_out * corner value c (formed
 // by the gather), section 4.1's gradients --
@@ -519,7 +521,28 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
 // otherwise each sample's term goes to loc_part and loc_reduce_kernel adds them.
 __global__ void __launch_bounds__(256) finalize_kernel(KArgs a) {
     __shared__ int32_t lvl_lds[3 * kMaxLevels];
-    const LevelsLds lv = stage_levels(a, lvl_lds);
+    // the block's dot products (256 samples x 4 corners x G <= 8 floats, one
+    // contiguous range), copied with coalesced 16-byte loads; an odd row stride
+    // keeps each thread's reads of its own row free of bank conflicts
+    constexpr int kDotRow = 4 * kFinalizeLdsGroups + 1;
+    __shared__ float sdots[256 * kDotRow];
+    const bool staged = a.w_vec4 && a.G <= kFinalizeLdsGroups;
+    if (staged) {
+        const uint32_t q0 = blockIdx.x * blockDim.x;
+        const uint32_t nq = min((uint32_t)blockDim.x, a.n_samples - q0);
+        const int row = 4 * a.G;                           // floats per sample, a multiple of 16
+        const float4* src = reinterpret_cast<const float4*>(a.dots + (size_t)q0 * row);
+        for (uint32_t i = threadIdx.x; i < nq * (uint32_t)row / 4; i += blockDim.x) {
+            const float4 v = src[i];
+            const uint32_t e = 4 * i, sq = e / (uint32_t)row, j = e - sq * (uint32_t)row;
+            float* d = sdots + sq * kDotRow + j;
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+        }
+    }
+    const LevelsLds lv = stage_levels(a, lvl_lds);      // (its barrier also covers sdots)
     const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
     const bool valid = q < a.n_samples;
     const uint32_t qq = valid ? q : 0u;
@@ -536,12 +559,15 @@ __global__ void __launch_bounds__(256) finalize_kernel(KArgs a) {
     for (int c = 0; c < 4; ++c) in[c] = st.row[c] >= 0;
     float tc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (a.w_vec4) {
+        const float* srow = sdots + threadIdx.x * kDotRow;
         for (int g = 0; g < G; g += 4) {
             const float4 w = *reinterpret_cast<const float4*>(wrow + g);
             float4 d[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float4 v = *reinterpret_cast<const float4*>(drow + c * G + g);
+                const float* sp = srow + c * G + g;
+                const float4 v = staged ? make_float4(sp[0], sp[1], sp[2], sp[3])
+                                        : *reinterpret_cast<const float4*>(drow + c * G + g);
                 d[c] = in[c] ? v : make_float4(0.f, 0.f, 0.f, 0.f);
                 tc[c] += w.x * d[c].x + w.y * d[c].y + w.z * d[c].z + w.w * d[c].w;
             }
