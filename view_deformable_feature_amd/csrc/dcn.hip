@@ -608,9 +608,9 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     extern __shared__ __align__(16) unsigned char smem[];
     const int TY = a.TY, TX = a.TX;
     unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * a.Dp);        // [TY*TX]
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * a.Dp);        // [TY*TX][4]
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    uint32_t* wl = cnt + (TY * TX + 3) / 4 * 4 + wave * (kDcnListWords * kWave);
+    uint32_t* wl = cnt + TY * TX * 4 + wave * (kDcnListWords * kWave);
     const int E = dcn_fixed_exponent(a);
     const double scale = ldexp(1.0, E);
 
@@ -629,7 +629,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
     for (int i = tid; i < TY * TX * a.Dp; i += kDcnTileThreads) acc[i] = 0ull;
-    for (int i = tid; i < TY * TX; i += kDcnTileThreads) cnt[i] = 0u;
+    for (int i = tid; i < TY * TX * 4; i += kDcnTileThreads) cnt[i] = 0u;
     __syncthreads();
 
     const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnTileThreads >> a.blog2Lg;
@@ -666,7 +666,9 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (!(R.flags >> (5 + q) & 1u)) continue;
-            atomicAdd(&cnt[pb + dpq[q]], 1u);     // once per lane of the group: bLg per term
+            // once per lane of the group (bLg per term), each lane on its own of the
+            // pixel's 4 counters so that no two lanes of a group add to one address
+            atomicAdd(&cnt[(pb + dpq[q]) * 4 + (jj & 3)], 1u);
             const double ws = (double)(cw[q] * R.m) * scale;
             unsigned long long* row = acc + (rb + dpr[q]);
 #pragma unroll
@@ -847,7 +849,9 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
         const int py = p / cols, px = p - (p / cols) * cols;
         const int tp = py * TX + px;
         const long long code =
-            (long long)(acc[tp * a.Dp + c] - (unsigned long long)(cnt[tp] >> a.blog2Lg) * kFixMagicBits);
+            (long long)(acc[tp * a.Dp + c] -
+                        (unsigned long long)((cnt[4 * tp] + cnt[4 * tp + 1] + cnt[4 * tp + 2] +
+                                              cnt[4 * tp + 3]) >> a.blog2Lg) * kFixMagicBits);
         a.grad_input[(((int64_t)t.n * a.H + t.Iy0 + py) * a.W + t.Ix0 + px) * a.C + gD + c] =
             (float)((double)code * inv);
     }

@@ -59,13 +59,13 @@ hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, h
 hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream);
 // Dynamic LDS of the backward tile kernel: the [TY*TX][Dp] 64-bit sums, the number of
-// terms each tile pixel took (32-bit, padded to 16 bytes), and per wave a list of up to
-// 64 accepted ring candidates (kDcnListWords words each).
+// terms each tile pixel took (four 32-bit counters per pixel), and per wave a list of
+// up to 64 accepted ring candidates (kDcnListWords words each).
 constexpr int kDcnTileThreads = 512;   // backward tile kernel workgroup
 constexpr int kDcnBwdWaves = kDcnTileThreads / 64;
 constexpr int kDcnListWords = 5;
 inline size_t dcn_tile_lds_bytes(int ty, int tx, int dp) {
-    return (size_t)ty * tx * dp * 8 + ((size_t)ty * tx + 3) / 4 * 16 +
+    return (size_t)ty * tx * dp * 8 + (size_t)ty * tx * 16 +
            (size_t)kDcnBwdWaves * 64 * kDcnListWords * 4;
 }
 
