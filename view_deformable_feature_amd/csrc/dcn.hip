@@ -589,18 +589,18 @@ __device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
 // Lanes: in the home loop a group of bLg lanes takes one sample at a time; lane jj
 // covers the NVL vectors jj, jj + bLg, ... of VEC channels of the group, and every
 // lane of the group forms the (cheap) stencil itself, so the waves never wait for
-// one another.  The ring loop tests one candidate per lane, lists the accepted ones
-// (a corner in this tile: about one candidate in eight for offsets of a pixel or
-// so) in the wave's LDS list at their rank among the wave's accepted lanes, and
-// then each lane group takes listed samples one at a time, so that their loads and
-// additions run on full waves.
+// one another.  The ring loop tests one candidate per lane and appends the accepted
+// ones (a corner in this tile: about one candidate in eight for offsets of a pixel
+// or so) to the wave's LDS list at their rank among the wave's accepted lanes; the
+// list collects several taps' candidates before the lane groups take listed samples
+// one at a time, so that their loads and additions run on full waves.
 //
 // Tile sums: a term t is added as the binary64 encoding of RNE(t 2^E) + 1.5 * 2^52,
 // an integer in [2^52, 2^53) whose encoding is kFixMagicBits + RNE(t 2^E), and each
 // tile pixel counts the terms it takes (the same count for every channel of the
-// group; every lane of the group adds it, so the LDS count is bLg times that).  The
-// store subtracts count * kFixMagicBits modulo 2^64, which leaves the exact sum of
-// the rounded terms.
+// group; each lane of the group adds 1 to its own of the pixel's four counters, so
+// their sum is bLg times that).  The store subtracts count * kFixMagicBits modulo
+// 2^64, which leaves the exact sum of the rounded terms.
 constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;   // encoding of 1.5 * 2^52
 
 template <typename T, int VEC, int NVL, bool GOV>
