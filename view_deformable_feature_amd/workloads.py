@@ -22,7 +22,7 @@ locations, weights, grad_out, all from ``numpy.random.default_rng(seed)``.
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
