@@ -396,15 +396,19 @@ bool fused_capable(const da_problem* p) {
 
 // The row-ordered form loads a feature row once per run of entries on that row;
 // it pays when rows are shared.  Expected corners per row on the largest level
-// for spread-out sampling: 4 A P / (H W); below 2 the per-anchor form is faster
-// (measured: 4.2 on the nuScenes-shaped workload, 1.2 on 4 x 160x400 levels).
+// for spread-out sampling: 4 A P / (H W).  Measured: at 4.2 (nuScenes-shaped)
+// row-ordered 154-162 us against per-anchor 189 us; at 1.2 (4 images of
+// 160x400 levels, 1500 anchors) the two forms tie within 1.5 % for uniform
+// locations (2.00 against 1.98 ms) and row-ordered wins by 12 % for clustered
+// ones (1.80 against 2.04 ms), which share rows more than the estimate says.
+// Below one corner per row each entry loads a row of its own.
 bool rows_reused(const da_problem* p, const da::KArgs& ka) {
     if (p->flags & DA_FLAG_BWD_ROW_ORDER) return true;
     double worst = 1e30;
     for (int l = 0; l < ka.K * ka.S; ++l)
         worst = std::min(worst, 4.0 * (double)p->num_anchors * (double)p->num_pts /
                                     ((double)ka.lv.H[l] * (double)ka.lv.W[l]));
-    return worst >= 2.0;
+    return worst >= 1.0;
 }
 
 // Workspace of the gather form of the backward, each part 256-byte aligned.
