@@ -968,7 +968,9 @@ __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
 // The walk is latency-bound: small batches that leave room for many waves per
 // SIMD beat deep batches (row-ordered, nuScenes-shaped: 2 entries per batch at 7
 // waves per SIMD 154 us per backward call, 4 entries at 5 waves 179 us).
-template <typename T, int VEC, int NV, bool FUSED, bool DET>
+// SEG: lanes per weight group in the row-ordered form when fixed at compile time
+// (0: read from D), so that the group sums unroll to their DPP steps alone.
+template <typename T, int VEC, int NV, bool FUSED, bool DET, int SEG = 0>
 __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5) : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
@@ -1049,7 +1051,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
     // FUSED: feature rows of every batch image, by flat row
     const __amdgpu_buffer_rsrc_t r_f = make_rsrc(a.feat, FUSED ? a.feat_all_bytes : 0u);
     const int G = a.G;
-    const int seg = FUSED ? a.D / VEC : 1;    // lanes per weight group (a power of two)
+    const int seg = SEG ? SEG : (FUSED ? a.D / VEC : 1);   // lanes per weight group (a power of two)
     uint32_t lo_f[NV];
     bool dvalid[NV];
 #pragma unroll
@@ -1351,7 +1353,17 @@ template <typename T, int VEC, bool FUSED, bool DET>
 hipError_t gather_dispatch_det(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
     // C <= 1024 in the backward: 16-byte vectors need at most 4 per lane
     switch (s.gather_nv) {
-        case 1: hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET>), grid, dim3(256), 0, st, a); break;
+        case 1:
+            if constexpr (FUSED) {
+                // 32 channels per weight group (C = 256 with G = 8, and the like)
+                if (a.D == 8 * VEC) {
+                    hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8>), grid, dim3(256), 0,
+                                       st, a);
+                    break;
+                }
+            }
+            hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET>), grid, dim3(256), 0, st, a);
+            break;
         case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED, DET>), grid, dim3(256), 0, st, a); break;
         case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED, DET>), grid, dim3(256), 0, st, a); break;
         case 8:
