@@ -507,6 +507,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
 }
 
 constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot products for G <= 8
+constexpr int kFinalizeThreads = 256;
 
 // One thread per sample q: from the per-corner group dot products
 // d[c][g] = sum over the channels of group g of grad_out * corner value c (formed
@@ -519,27 +520,38 @@ constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot produc
 // 0.  The S samples of a (point, camera) are consecutive threads: with S a power
 // of two their location terms are summed across lanes (total in the last lane),
 // otherwise each sample's term goes to loc_part and loc_reduce_kernel adds them.
-__global__ void __launch_bounds__(256) finalize_kernel(KArgs a) {
+__global__ void __launch_bounds__(kFinalizeThreads) finalize_kernel(KArgs a) {
     __shared__ int32_t lvl_lds[3 * kMaxLevels];
-    // the block's dot products (256 samples x 4 corners x G <= 8 floats, one
+    // the block's dot products (kFinalizeThreads samples x 4 corners x G <= 8 floats, one
     // contiguous range), copied with coalesced 16-byte loads; an odd row stride
     // keeps each thread's reads of its own row free of bank conflicts
     constexpr int kDotRow = 4 * kFinalizeLdsGroups + 1;
-    __shared__ float sdots[256 * kDotRow];
+    __shared__ float sdots[kFinalizeThreads * kDotRow];
     const bool staged = a.w_vec4 && a.G <= kFinalizeLdsGroups;
     if (staged) {
         const uint32_t q0 = blockIdx.x * blockDim.x;
         const uint32_t nq = min((uint32_t)blockDim.x, a.n_samples - q0);
         const int row = 4 * a.G;                           // floats per sample, a multiple of 16
         const float4* src = reinterpret_cast<const float4*>(a.dots + (size_t)q0 * row);
-        for (uint32_t i = threadIdx.x; i < nq * (uint32_t)row / 4; i += blockDim.x) {
-            const float4 v = src[i];
-            const uint32_t e = 4 * i, sq = e / (uint32_t)row, j = e - sq * (uint32_t)row;
-            float* d = sdots + sq * kDotRow + j;
-            d[0] = v.x;
-            d[1] = v.y;
-            d[2] = v.z;
-            d[3] = v.w;
+        // at most G <= 8 vectors per thread: all loads issued before the first store
+        const uint32_t n4 = nq * (uint32_t)row / 4;
+        float4 v[kFinalizeLdsGroups];
+#pragma unroll
+        for (int k = 0; k < kFinalizeLdsGroups; ++k) {
+            const uint32_t i = threadIdx.x + (uint32_t)(k * kFinalizeThreads);
+            if (i < n4) v[k] = src[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kFinalizeLdsGroups; ++k) {
+            const uint32_t i = threadIdx.x + (uint32_t)(k * kFinalizeThreads);
+            if (i < n4) {
+                const uint32_t e = 4 * i, sq = e / (uint32_t)row, j = e - sq * (uint32_t)row;
+                float* d = sdots + sq * kDotRow + j;
+                d[0] = v[k].x;
+                d[1] = v[k].y;
+                d[2] = v[k].z;
+                d[3] = v[k].w;
+            }
         }
     }
     const LevelsLds lv = stage_levels(a, lvl_lds);      // (its barrier also covers sdots)
@@ -1468,7 +1480,8 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
             return gather_dispatch<decltype(t), 4, true>(k, s, ggrid, stream);
         });
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for((int64_t)a.n_samples, 256)), dim3(256),
+        hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for((int64_t)a.n_samples, kFinalizeThreads)),
+                           dim3(kFinalizeThreads),
                            0, stream, k);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((a.S & (a.S - 1)) != 0 || a.S > kWave) {
