@@ -7,7 +7,11 @@ feature row through a caller-side workspace) on the nuScenes-shaped workload (bs
 8x22, C=256, G=8, 900 anchors, 13 keypoints), inputs resident in HBM.
 
 Prints ONE JSON line.  value = bilinear sample-channels per second over
-forward + backward (bs*A*P*K*S*C per step / step time).  The roofline
+forward + backward (bs*A*P*K*S*C per step / step time); the step time is the
+wall time of K replays of one HIP graph holding a captured step (the library
+launches kernels only, so the graph replays exactly the calls' kernels), between
+device synchronisations; --launch eager times K eager steps instead, and
+eager_ms_per_step always reports that figure.  The roofline
 entries use the algorithmic bytes of each direction (feature rows of the
 four corners, locations, weights, outputs; backward also the feature-gradient
 payload of every (sample, corner, channel) term) over the HIP-event time of
@@ -376,6 +380,9 @@ def main():
                     help="element type of out and grad_out (binary32 arithmetic throughout)")
     ap.add_argument("--deterministic", action="store_true",
                     help="run the backward in its deterministic (64-bit fixed-point) form")
+    ap.add_argument("--launch", default="graph", choices=("graph", "eager"),
+                    help="time the step as replays of one captured HIP graph (default) or as "
+                         "eager calls; the per-call forward / backward times are eager either way")
     ap.add_argument("--cold", action="store_true",
                     help="also time each call after writing a 512 MiB buffer (L2 and MALL "
                          "hold none of the inputs)")
@@ -457,6 +464,30 @@ def main():
     t_fwd = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_bwd = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     t_step = wall / args.steps
+    t_eager = t_step
+    launch = "eager calls"
+    if args.launch == "graph":
+        # one step captured in a HIP graph (the library only launches kernels), warmed
+        # up and then replayed: the same kernels without the host's per-call work
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_step = (time.perf_counter() - t0) / args.steps
+        launch = "hip graph: one captured step (forward + backward), replayed"
+        del graph
     b_fwd, b_bwd = algorithmic_bytes(wl, out.element_size())
     sc = wl.sample_channels
     fwd_s, bwd_s = float(t_fwd.mean()), float(t_bwd.mean())
@@ -499,7 +530,9 @@ def main():
                                + f", C={wl.C}, groups={wl.groups}, anchors={wl.anchors}, "
                                  f"points={wl.pts}",
                    "sample_channels_per_step": sc, "out_dtype": args.out_dtype,
-                   "backward_form": "deterministic" if det else "default"},
+                   "backward_form": "deterministic" if det else "default",
+                   "launch": launch},
+        "eager_ms_per_step": t_eager * 1e3,
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
         "roofline": roof(b_bwd, bwd_s, BWD_KERNELS + (" (prep_kernel also converts grad_out)"

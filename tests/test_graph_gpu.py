@@ -1,0 +1,89 @@
+"""A whole step (da_forward then da_backward) captured in a HIP graph and
+replayed: every replay must reproduce the eager call.
+
+The library launches kernels only (no allocation, memset or synchronisation),
+so one captured step can be replayed; each replay here follows eager work on
+the same buffers (they are overwritten with NaN first) and a synchronisation.
+Outputs whose arithmetic order is fixed (out, grad_loc, grad_weights, and
+grad_feat of the deterministic form) must match the eager call bit for bit;
+grad_feat of the default form sums long rows with atomics, so it is compared
+within the backward tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import view_deformable_feature_amd as vdf
+from view_deformable_feature_amd import workloads as W
+from gpu_helpers import TOL_BWD, assert_close, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = dict(bs=2, num_cams=3, levels=((13, 29), (7, 15), (3, 8)), C=96, groups=3, anchors=37,
+              pts=5, loc_lo=-0.1, loc_hi=1.1, seed=91)
+
+# (name, custom shape or None, deterministic, backward form: None = library's choice,
+#  True = per-anchor)
+CASES = [
+    ("nuscenes_bwd", None, False, None),
+    ("nuscenes_bwd", None, True, None),
+    ("ragged_c96_g3", RAGGED, False, None),
+    ("ragged_c96_g3_per_anchor", RAGGED, False, True),
+]
+
+
+@pytest.mark.parametrize("name, kw, det, regather", CASES,
+                         ids=[f"{c[0]}{'_det' if c[2] else ''}" for c in CASES])
+def test_graph_replays_match_eager(name, kw, det, regather):
+    wl = W.WORKLOADS[name] if kw is None else W.custom(name, **kw)
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    feat, loc, w, go = dev["feat"], dev["loc"], dev["weights"], dev["grad_out"]
+    shape, start = dev["spatial_shape"], dev["scale_start_index"]
+    out = torch.empty((wl.bs, wl.anchors, wl.C), device="cuda", dtype=torch.float32)
+    gf = torch.empty(tuple(feat.shape), device="cuda", dtype=torch.float32)
+    gl = torch.empty(tuple(loc.shape), device="cuda", dtype=torch.float32)
+    gw = torch.empty(tuple(w.shape), device="cuda", dtype=torch.float32)
+    fws_n = vdf.forward_workspace_size(feat, shape, loc, w)
+    fws = torch.empty(fws_n, device="cuda", dtype=torch.uint8) if fws_n else None
+    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w, regather=regather,
+                                         deterministic=det), device="cuda", dtype=torch.uint8)
+
+    def step():
+        vdf.da_forward(feat, shape, start, loc, w, out=out, workspace=fws)
+        vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                        grad_weights=gw, workspace=bws, regather=regather, deterministic=det)
+
+    say(f"[graph] {name} det={det} regather={regather}: eager")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, gf, gl, gw)]
+
+    # warm up on a side stream, then capture one step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for r in range(4):
+        for t in (out, gf, gl, gw):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"[graph] {name}: replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]), f"replay {r}: out differs from the eager call"
+        assert torch.equal(gl, ref[2]), f"replay {r}: grad_loc differs from the eager call"
+        assert torch.equal(gw, ref[3]), f"replay {r}: grad_weights differs from the eager call"
+        if det:
+            assert torch.equal(gf, ref[1]), f"replay {r}: grad_feat differs from the eager call"
+        else:
+            assert_close(f"graph replay {r} grad_feat", gf.cpu().numpy(),
+                         ref[1].cpu().numpy().astype(np.float64), TOL_BWD)
+    del graph
