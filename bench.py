@@ -263,6 +263,36 @@ def dcn_bytes(wl, out_bytes=4):
     return b_fwd, b_bwd
 
 
+GRAPH_LAUNCH = "hip graph: one captured step (forward + backward), replayed"
+
+
+def graph_step_seconds(step, warmup, steps):
+    """Wall time per step of `steps` replays of one HIP graph holding a captured
+    step (after a warm-up call on a side stream and `warmup` replays), between
+    device synchronisations.  The library's calls only launch kernels, so the
+    graph replays exactly their kernels."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    del graph
+    return t
+
+
 def bench_dcn(args):
     """Deformable convolution (DCNv3 / DCNv4 operator): forward + backward on the
     shape the DCNv4 notes time (56x56x128, batch 64, 4 groups by default)."""
@@ -310,7 +340,11 @@ def bench_dcn(args):
     f_all = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     b_all = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     t_fwd, t_bwd = float(f_all.mean()), float(b_all.mean())
-    t_step = wall / args.steps
+    t_step = t_eager = wall / args.steps
+    launch = "eager calls"
+    if args.launch == "graph":
+        t_step = graph_step_seconds(step, args.warmup, args.steps)
+        launch = GRAPH_LAUNCH
     b_fwd, b_bwd = dcn_bytes(wl, out.element_size())
     sc = wl.sample_channels
 
@@ -330,7 +364,9 @@ def bench_dcn(args):
            "data": "synthetic",
            "config": {"workload": f"{wl.name}: N={wl.N}, {wl.H}x{wl.W}x{wl.C}, groups={wl.groups}, "
                                   f"kernel {wl.kernel[0]}x{wl.kernel[1]}, out {ho}x{wo}",
-                      "sample_channels_per_step": sc, "out_dtype": args.out_dtype},
+                      "sample_channels_per_step": sc, "out_dtype": args.out_dtype,
+                      "launch": launch},
+           "eager_ms_per_step": t_eager * 1e3,
            "forward": {"avg_us": t_fwd * 1e6, "median_us": float(np.median(f_all)) * 1e6,
                        "value": sc / t_fwd, "unit": "sample-channels/s"},
            "backward": {"avg_us": t_bwd * 1e6, "median_us": float(np.median(b_all)) * 1e6,
@@ -467,27 +503,8 @@ def main():
     t_eager = t_step
     launch = "eager calls"
     if args.launch == "graph":
-        # one step captured in a HIP graph (the library only launches kernels), warmed
-        # up and then replayed: the same kernels without the host's per-call work
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        t_step = (time.perf_counter() - t0) / args.steps
-        launch = "hip graph: one captured step (forward + backward), replayed"
-        del graph
+        t_step = graph_step_seconds(step, args.warmup, args.steps)
+        launch = GRAPH_LAUNCH
     b_fwd, b_bwd = algorithmic_bytes(wl, out.element_size())
     sc = wl.sample_channels
     fwd_s, bwd_s = float(t_fwd.mean()), float(t_bwd.mean())

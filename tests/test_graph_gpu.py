@@ -1,5 +1,6 @@
-"""A whole step (da_forward then da_backward) captured in a HIP graph and
-replayed: every replay must reproduce the eager call.
+"""A whole step (da_forward then da_backward; dcn_forward then dcn_backward)
+captured in a HIP graph and replayed: every replay must reproduce the eager
+call.
 
 The library launches kernels only (no allocation, memset or synchronisation),
 so one captured step can be replayed; each replay here follows eager work on
@@ -86,4 +87,60 @@ def test_graph_replays_match_eager(name, kw, det, regather):
         else:
             assert_close(f"graph replay {r} grad_feat", gf.cpu().numpy(),
                          ref[1].cpu().numpy().astype(np.float64), TOL_BWD)
+    del graph
+
+
+# deformable convolution: forward then backward, captured and replayed the same way;
+# out and grad_offset_mask have a fixed arithmetic order, grad_input adds its far
+# corners with atomics and is compared within the backward tolerance
+DCN_CASES = [
+    ("dcn_56", None),
+    ("tiles_s2", dict(N=2, H=37, W=45, C=64, groups=4, stride=(2, 2), seed=3101)),
+]
+
+
+@pytest.mark.parametrize("name, kw", DCN_CASES, ids=[c[0] for c in DCN_CASES])
+def test_dcn_graph_replays_match_eager(name, kw):
+    wl = W.DCN_WORKLOADS[name] if kw is None else W.dcn_custom(name, **kw)
+    inp = W.make_dcn_inputs(wl)
+    x = torch.from_numpy(inp["input"]).cuda()
+    om = torch.from_numpy(inp["offset_mask"]).cuda()
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+    conf = dict(groups=wl.groups, kernel=wl.kernel, stride=wl.stride, pad=wl.pad,
+                dilation=wl.dilation)
+    out = torch.empty(tuple(go.shape), device="cuda", dtype=torch.float32)
+    gi = torch.empty(tuple(x.shape), device="cuda", dtype=torch.float32)
+    gom = torch.empty_like(om)
+    nws = vdf.dcn_workspace_size(x, **conf)
+    ws = torch.empty(nws, device="cuda", dtype=torch.uint8) if nws else None
+
+    def step():
+        vdf.dcn_forward(x, om, **conf, out=out)
+        vdf.dcn_backward(x, om, go, **conf, grad_input=gi, grad_offset_mask=gom, workspace=ws)
+
+    say(f"[graph] {name}: eager")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, gi, gom)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in (out, gi, gom):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"[graph] {name}: replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]), f"replay {r}: out differs from the eager call"
+        assert torch.equal(gom, ref[2]), f"replay {r}: grad_offset_mask differs from the eager call"
+        assert_close(f"graph replay {r} grad_input", gi.cpu().numpy(),
+                     ref[1].cpu().numpy().astype(np.float64), TOL_BWD)
     del graph
