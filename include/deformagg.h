@@ -166,8 +166,9 @@ DA_API da_status da_forward_workspace_size(const da_problem* problem, size_t* by
  * workspace), DA_ERR_UNSUPPORTED (one batch image of the
  * features -- or, in the backward, of the feature gradient -- plus two rows above
  * 2^32 - 1 bytes; num_embeds > 2^20; bs * A * 512 >= 2^32; one (point, camera) pair's
- * stencils and weights above 48 KiB of LDS; in the backward, num_embeds more than 16
- * times the largest power of two dividing C / G, capped at 64) or DA_ERR_HIP.
+ * stencils and weights above 48 KiB of LDS; in the backward, num_embeds above 1024 or
+ * more than 16 times the largest power of two dividing C / G, capped at 64) or
+ * DA_ERR_HIP.
  */
 DA_API da_status da_forward(const da_problem* problem,
                      const void* mc_ms_feat,

@@ -3,8 +3,8 @@ binary16, and a 16-bit grad_out in every backward form.
 
 Binary16 features convert to binary32 exactly, so the oracle takes the same
 values and the binary32 tolerances hold.  A 16-bit out is the binary32 out
-rounded once to nearest even: checked bit for bit against numpy's rounding of
-the binary32 out of the same launch configuration, and against the oracle within
+rounded once to nearest even: checked bit for bit against torch's CPU conversion
+of the binary32 out of the same launch configuration, and against the oracle within
 the forward bound plus that rounding.  A 16-bit grad_out converts exactly, so
 the backward must equal the one given those values in binary32.
 """
@@ -43,10 +43,9 @@ def _wl(name):
 
 
 def _round_out(out_f32: np.ndarray, dtype: torch.dtype) -> np.ndarray:
-    """numpy's round-to-nearest-even of binary32 values, as float64."""
-    if dtype == torch.bfloat16:
-        return W.bf16_bits_to_f32(W.bf16_bits_from_f32(out_f32)).astype(np.float64)
-    return out_f32.astype(np.float16).astype(np.float64)
+    """torch's CPU conversion of binary32 values to dtype (round to nearest, ties to
+    even), as float64 -- a rounding implemented independently of this repository."""
+    return torch.from_numpy(out_f32).to(dtype).to(torch.float64).numpy()
 
 
 def _half(x: np.ndarray, dtype: torch.dtype):

@@ -377,13 +377,46 @@ def test_sampled_entry_points_match_dense():
     assert np.array_equal(gf2, gf.reshape(-1, wl.C)[rows])
 
 
+def _torch_bf16_values(bits: np.ndarray) -> np.ndarray:
+    """float32 values of bfloat16 bit patterns, widened by torch (not by this repository)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).float().numpy()
+
+
 def test_bf16_features_read_exactly():
+    # bfloat16 patterns and their values (sign, 8-bit exponent biased by 127, 7-bit
+    # fraction; subnormals below 2^-126)
+    golden = {0x3F80: 1.0, 0xC000: -2.0, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+              0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x3EAB: 0.333984375, 0x8000: -0.0}
+    bits = np.array(list(golden), np.uint16)
+    assert np.array_equal(_torch_bf16_values(bits).astype(np.float64), list(golden.values()))
     wl = W.custom("tb", bs=1, num_cams=1, levels=((16, 16),), C=32, groups=4, anchors=8,
                   pts=4, feat_dtype="bf16", loc_lo=-0.1, loc_hi=1.1, seed=31)
     inp = W.make_inputs(wl)
     as_f32 = dict(inp)
-    as_f32["feat"] = W.bf16_bits_to_f32(inp["feat"])
+    as_f32["feat"] = _torch_bf16_values(inp["feat"])
     assert np.array_equal(oracle.forward(*_args(inp)), oracle.forward(*_args(as_f32)))
+    gi = oracle.backward(*_args(inp), inp["grad_out"])
+    gf = oracle.backward(*_args(as_f32), inp["grad_out"])
+    for a, b in zip(gi, gf):
+        assert np.array_equal(a, b)
+
+
+def test_generator_bf16_rounding_matches_torch():
+    """The input generator's bfloat16 rounding (used for the bf16 features) is torch's
+    round-to-nearest-even, ties included: values whose low 16 bits are exactly 0x8000
+    round to the even neighbour, 0x7FFF down and 0x8001 up."""
+    import torch
+    rng = np.random.default_rng(5)
+    hi = rng.integers(0, 0x7F7F, size=4096, dtype=np.uint32)     # finite, below the top binade
+    sign = rng.integers(0, 2, size=hi.size, dtype=np.uint32) << np.uint32(31)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    u = (sign[:, None] | (hi[:, None] << np.uint32(16)) | lows[None, :]).reshape(-1)
+    x = np.concatenate([u.view(np.float32),
+                        rng.standard_normal(100000).astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.bf16_bits_from_f32(x), ref)
 
 
 def test_f16_features_read_exactly():

@@ -14,12 +14,16 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdeformagg.so")
+# read-bandwidth reference kernel for the benchmark (not part of the C ABI)
+PROBE_PATH = os.path.join(PKG_DIR, "libbwprobe.so")
+PROBE_SOURCE = os.path.join(PKG_DIR, "csrc", "bw_probe.hip")
 SOURCES = [os.path.join(CSRC, f)
            for f in ("da_forward.hip", "da_backward.hip", "da_pack.hip", "da_api.cpp", "dcn.hip",
                      "dcn_api.cpp")]
 HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(INCLUDE, "dcn.h")] + [
     os.path.join(CSRC, f) for f in ("da_internal.h", "da_device.h", "da_pack.h", "dcn_internal.h",
                                     "host_errors.h")]
+EXPORTS = os.path.join(CSRC, "exports.map")   # the C ABI is the only export
 ARCH = "gfx950"
 
 
@@ -64,16 +68,23 @@ def build(verbose: bool = False) -> str:
                     zip(SOURCES, objs)))
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp,
-          f"-Wl,-rpath,{rocm_lib}", "-Wl,--no-undefined"], verbose)
+          f"-Wl,-rpath,{rocm_lib}", "-Wl,--no-undefined", f"-Wl,--version-script={EXPORTS}"],
+         verbose)
     os.replace(tmp, LIB_PATH)
+    tmp = PROBE_PATH + ".tmp"
+    _run([hipcc, *compile_flags(), "-shared", PROBE_SOURCE, "-o", tmp, f"-Wl,-rpath,{rocm_lib}"],
+         verbose)
+    os.replace(tmp, PROBE_PATH)
     return LIB_PATH
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_PATH):
+        return True
+    if os.path.getmtime(PROBE_SOURCE) > os.path.getmtime(PROBE_PATH):
         return True
     t = os.path.getmtime(LIB_PATH)
-    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS + [EXPORTS])
 
 
 if __name__ == "__main__":

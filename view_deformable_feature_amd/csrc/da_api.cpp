@@ -174,7 +174,7 @@ bool want_slices(const da_problem* p) {
     if (nlev < da::kSlices) return false;
     const int64_t m = (nlev + da::kSlices - 1) / da::kSlices;
     if (4 * m * da::kSlices > 5 * nlev) return false;   // more than 1/4 of the slots idle
-    const uint64_t elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    const uint64_t elem = (uint64_t)elem_bytes(p->feat_dtype);
     return (uint64_t)p->num_feat * (uint64_t)p->num_embeds * elem >= kSliceMinImageBytes;
 }
 
@@ -309,10 +309,18 @@ bool bwd_layout(int64_t C, int64_t D, int64_t vec, int64_t max_nv, int64_t& L, i
     return nv <= max_nv;
 }
 
-da_status plan_backward(const da_problem* p, Plan& plan, bool gather) {
+// Largest num_embeds the feature-gradient gather handles: 64 lanes of at most 16
+// channels (gather_kernel's vectors per lane: 1..4 of 4 channels, 1..16 single
+// channels).
+constexpr int64_t kGatherMaxC = 1024;
+
+da_status plan_backward(const da_problem* p, Plan& plan, bool gather, const float* grad_feat) {
     da::KArgs& ka = plan.ka;
-    int s_gather_nv_out = 1;
     const int64_t C = ka.C, D = ka.D;
+    if (gather && C > kGatherMaxC)
+        return fail(DA_ERR_UNSUPPORTED,
+                    "backward: num_embeds = %lld exceeds the feature-gradient gather's %lld",
+                    (long long)C, (long long)kGatherMaxC);
     // the gather form only reads features: 16-byte vectors per lane when the
     // rows and groups allow; the scatter form keeps one channel per lane so that
     // each atomic instruction covers consecutive floats
@@ -331,12 +339,12 @@ da_status plan_backward(const da_problem* p, Plan& plan, bool gather) {
     ka.nv = (int32_t)nv;
     ka.nv_chunk = (int32_t)nv;
     ka.seg = (int32_t)seg;
-    // feature-gradient gather: 16-byte vectors when rows and groups allow
-    ka.gather_vec = (C % 4 == 0 && D % 4 == 0) ? 4 : 1;
+    // feature-gradient gather: 16-byte vectors when rows, groups and the
+    // grad_feat pointer allow; then the vectors each lane covers (a power of two)
+    ka.gather_vec = (C % 4 == 0 && D % 4 == 0 && aligned(grad_feat, 16)) ? 4 : 1;
     const int64_t gvec = (C / ka.gather_vec + da::kWave - 1) / da::kWave;
     int gnv = 1;
     while (gnv < gvec) gnv <<= 1;
-    s_gather_nv_out = gnv;
     const uint64_t gimg = (uint64_t)p->num_feat * (uint64_t)C * 4u;
     if (gimg + 8 * (uint64_t)C > kU32Max)
         return fail(DA_ERR_UNSUPPORTED, "one batch image of grad_feat (%llu bytes) exceeds 4 GiB",
@@ -346,7 +354,7 @@ da_status plan_backward(const da_problem* p, Plan& plan, bool gather) {
     da::LaunchShape& s = plan.shape;
     s.vec = (int)vec;
     s.nvc = (int)nv;
-    s.gather_nv = s_gather_nv_out;
+    s.gather_nv = gnv;
     s.chunks = 1;
     const int64_t spw = da::kWave / L;
     s.waves = (int)std::max<int64_t>(
@@ -389,7 +397,7 @@ bool fused_capable(const da_problem* p) {
     if (C % 4 != 0 || D % 4 != 0 || C > 1024 || G > 16) return false;
     const int64_t seg = D / 4;
     if (seg > 64 || (seg & (seg - 1)) != 0) return false;
-    const uint64_t elem = p->feat_dtype == DA_BF16 ? 2 : 4;
+    const uint64_t elem = (uint64_t)elem_bytes(p->feat_dtype);
     const uint64_t all = (uint64_t)p->bs * (uint64_t)p->num_feat * (uint64_t)C * elem;
     return all + 2 * (uint64_t)C * elem <= kU32Max;
 }
@@ -507,7 +515,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
     if (mode == BwdMode::kScatter && (p->flags & DA_FLAG_DETERMINISTIC))
         return fail(DA_ERR_UNSUPPORTED,
                     "da_backward_atomic has no deterministic form (use da_backward)");
-    st = plan_backward(p, plan, mode != BwdMode::kScatter);
+    st = plan_backward(p, plan, mode != BwdMode::kScatter, grad_feat);
     if (st != DA_OK) return st;
     da::KArgs& ka = plan.ka;
     ka.grad_out = grad_out;
@@ -557,7 +565,6 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.n_tiles = (uint32_t)((n_rows + da::kScanTile - 1) / da::kScanTile);
             ka.num_feat = (int32_t)p->num_feat;
             ka.accumulate = mode == BwdMode::kGatherAccumulate ? 1 : 0;
-            if (ka.gather_vec == 4 && !aligned(grad_feat, 16)) ka.gather_vec = 1;
             if (fusable && ka.gather_vec == 4 && aligned(feat, 16) && rows_reused(p, ka)) {
                 ka.fused = 1;
                 ka.dots = reinterpret_cast<float*>(base + w.dots);
