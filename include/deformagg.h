@@ -272,6 +272,40 @@ DA_API da_status da_backward_atomic(const da_problem* problem,
                              void* stream);
 
 /*
+ * da_backward_noalloc -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): da_backward
+ * with its workspace taken from a fixed array of DA_NOALLOC_SCRATCH_BYTES inside the
+ * library's code object instead of from the caller.  The call allocates and frees
+ * nothing.  Every GPU the library runs on holds its own copy of the array until the
+ * process ends; its device address is looked up on the first call on each device.
+ *
+ * Arguments as da_backward without workspace / workspace_bytes; grad_feat, grad_loc and
+ * grad_weights are fully overwritten.  Every call on one GPU shares that GPU's array,
+ * whose contents a call leaves behind (nothing in it needs to start at zero): calls
+ * that overlap in time on one GPU -- on different streams or threads -- race, and the
+ * caller must serialise them.  Returns da_backward's errors, plus DA_ERR_UNSUPPORTED
+ * (checked after the arguments, before anything is enqueued) when
+ * da_backward_workspace_size reports more than DA_NOALLOC_SCRATCH_BYTES for the problem
+ * -- enough for the nuScenes-shaped
+ * problem (6 cameras, 4 scales from 64x176, C = 256, 900 anchors, 13 points) in every
+ * backward form, deterministic included -- and DA_ERR_HIP if the array's device
+ * address cannot be found.
+ */
+#define DA_NOALLOC_SCRATCH_BYTES (96ull << 20)   /* 96 MiB per device */
+
+DA_API da_status da_backward_noalloc(const da_problem* problem,
+                              const void* mc_ms_feat,
+                              const int32_t* spatial_shape,
+                              const int32_t* scale_start_index,
+                              const float* sampling_location,
+                              const float* weights,
+                              const void* grad_out,
+                              float* grad_feat,
+                              float* grad_loc,
+                              float* grad_weights,
+                              void* stream);
+
+/*
  * Level packing -- section 6 of the walkthrough: feature_maps_format turns the list of
  * per-scale camera feature maps into the flattened tensor the aggregation reads (plus
  * its level table), and back.  The page prints this step only in garbled form; the

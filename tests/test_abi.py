@@ -67,8 +67,8 @@ def _bwd(lib, prob, name="da_backward", feat=FAKE, loc=FAKE, w=FAKE, go=FAKE, gf
     vp = ctypes.c_void_p
     args = [ctypes.byref(prob), vp(feat), _i32p(shape), _i32p(start), vp(loc), vp(w), vp(go),
             vp(gf), vp(gl), vp(gw)]
-    if name == "da_backward_atomic":
-        return lib.da_backward_atomic(*args, None)
+    if name in ("da_backward_atomic", "da_backward_noalloc"):
+        return getattr(lib, name)(*args, None)
     return getattr(lib, name)(*args, vp(ws), ws_bytes, None)
 
 
@@ -405,3 +405,21 @@ def test_backward_rejects_more_than_1024_channels(lib, C, G, dtype, name):
     assert _bwd(lib, prob, name=name) == 2
     assert "1024" in _msg(lib) or "exceeds 16" in _msg(lib)
 
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """da_backward_noalloc refuses, on the host and before any HIP call, a problem whose
+    workspace exceeds the static scratch array (4 images of 160x400 levels here)."""
+    from view_deformable_feature_amd import workloads as W
+    wl = W.WORKLOADS["large"]
+    prob = _prob(bs=wl.bs, num_feat=wl.num_feat, num_embeds=wl.C, num_anchors=wl.anchors,
+                 num_pts=wl.pts, num_cams=wl.num_cams, num_scale=len(wl.levels),
+                 num_groups=wl.groups)
+    need = ctypes.c_size_t(0)
+    assert lib.da_backward_workspace_size(ctypes.byref(prob), ctypes.byref(need)) == 0
+    assert need.value > _lib.DA_NOALLOC_SCRATCH_BYTES
+    shape = np.tile(np.array([[[1, 1]]], np.int32), (wl.num_cams, len(wl.levels), 1))
+    start = np.zeros((wl.num_cams, len(wl.levels)), np.int32)
+    assert _bwd(lib, prob, name="da_backward_noalloc", shape=shape, start=start) == 2
+    assert "da_backward_noalloc" in _msg(lib) and str(need.value) in _msg(lib)
+    # malformed problems are reported as by da_backward
+    assert _bwd(lib, _prob(num_groups=0), name="da_backward_noalloc") == 1

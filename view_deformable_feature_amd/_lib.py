@@ -20,6 +20,7 @@ DA_F32, DA_BF16, DA_F16 = 0, 1, 2
 DA_FLAG_SLICES_ALWAYS, DA_FLAG_SLICES_NEVER, DA_FLAG_BWD_REGATHER, DA_FLAG_BWD_ROW_ORDER = \
     1, 2, 4, 8
 DA_FLAG_DETERMINISTIC = 16
+DA_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 class DAProblem(ctypes.Structure):
@@ -97,8 +98,10 @@ def load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         f.restype = ctypes.c_int
-    lib.da_backward_atomic.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp]
-    lib.da_backward_atomic.restype = ctypes.c_int
+    for name in ("da_backward_atomic", "da_backward_noalloc"):
+        f = getattr(lib, name)
+        f.argtypes = [prob, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp]
+        f.restype = ctypes.c_int
     lib.da_backward_workspace_size.argtypes = [prob, ctypes.POINTER(ctypes.c_size_t)]
     lib.da_backward_workspace_size.restype = ctypes.c_int
     pprob = ctypes.POINTER(DAPackProblem)

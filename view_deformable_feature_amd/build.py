@@ -19,7 +19,7 @@ PROBE_PATH = os.path.join(PKG_DIR, "libbwprobe.so")
 PROBE_SOURCE = os.path.join(PKG_DIR, "csrc", "bw_probe.hip")
 SOURCES = [os.path.join(CSRC, f)
            for f in ("da_forward.hip", "da_backward.hip", "da_pack.hip", "da_api.cpp", "dcn.hip",
-                     "dcn_api.cpp")]
+                     "dcn_api.cpp", "da_noalloc.hip")]
 HEADERS = [os.path.join(INCLUDE, "deformagg.h"), os.path.join(INCLUDE, "dcn.h")] + [
     os.path.join(CSRC, f) for f in ("da_internal.h", "da_device.h", "da_pack.h", "dcn_internal.h",
                                     "host_errors.h")]

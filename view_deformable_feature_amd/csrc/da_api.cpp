@@ -494,11 +494,14 @@ da_status gather_sizes(const da_problem* p, uint64_t& n_rows, uint64_t& n_sample
 
 enum class BwdMode { kGather, kGatherAccumulate, kScatter };
 
+// resolve_ws (may be NULL): supplies the workspace once every argument check has
+// passed, given the bytes the call needs (see da::WorkspaceResolver).
 da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                         const int32_t* shape, const int32_t* start, const float* loc,
                         const float* weights, const void* grad_out, float* grad_feat,
                         float* grad_loc, float* grad_weights, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream,
+                        da::WorkspaceResolver resolve_ws = nullptr) {
     Plan plan;
     da_status st = check_common(p, feat, shape, start, loc, weights, plan);
     if (st != DA_OK) return st;
@@ -533,6 +536,10 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             const bool det = p->flags & DA_FLAG_DETERMINISTIC;
             const WsLayout w = ws_layout(n_rows, n_samples, fusable ? (uint64_t)p->num_groups : 0,
                                          det ? det_bytes(p, n_samples) : 0, go32_bytes(p));
+            if (resolve_ws) {
+                st = resolve_ws(w.total, &workspace, &workspace_bytes);
+                if (st != DA_OK) return st;
+            }
             if (!workspace) return fail(DA_ERR_INVALID_ARG, "workspace is NULL");
             if (!aligned(workspace, 256))
                 return fail(DA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -804,6 +811,22 @@ da_status da_backward_atomic(const da_problem* p, const void* feat, const int32_
     return backward_impl(BwdMode::kScatter, p, feat, shape, start, loc, weights, grad_out,
                          grad_feat, grad_loc, grad_weights, nullptr, 0, stream);
 }
+
+}  // extern "C"
+
+namespace da {
+
+da_status backward_resolved(const da_problem* p, const void* feat, const int32_t* shape,
+                            const int32_t* start, const float* loc, const float* weights,
+                            const void* grad_out, float* grad_feat, float* grad_loc,
+                            float* grad_weights, void* stream, WorkspaceResolver resolve_ws) {
+    return backward_impl(BwdMode::kGather, p, feat, shape, start, loc, weights, grad_out,
+                         grad_feat, grad_loc, grad_weights, nullptr, 0, stream, resolve_ws);
+}
+
+}  // namespace da
+
+extern "C" {
 
 const char* da_status_string(da_status s) {
     switch (s) {
