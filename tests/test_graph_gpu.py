@@ -144,3 +144,60 @@ def test_dcn_graph_replays_match_eager(name, kw):
         assert_close(f"graph replay {r} grad_input", gi.cpu().numpy(),
                      ref[1].cpu().numpy().astype(np.float64), TOL_BWD)
     del graph
+
+
+def test_device_level_tables_are_copied_once_and_capture_cleanly():
+    """Level tables held as device tensors (as a model keeps them) are copied to the
+    host on first use only: the same unchanged tensor is served from the binding's
+    cache (no blocking copy, so the call can be captured), an in-place update through
+    torch is seen, and the results equal those of host tables bit for bit."""
+    from view_deformable_feature_amd.api import _host_i32
+    wl = W.custom("devtables", **RAGGED)
+    inp = W.make_inputs(wl)
+    dev = to_device(inp)
+    feat, loc, w, go = dev["feat"], dev["loc"], dev["weights"], dev["grad_out"]
+    d_shape = torch.from_numpy(inp["spatial_shape"]).cuda()
+    d_start = torch.from_numpy(inp["scale_start_index"]).cuda()
+    first = _host_i32(d_start)
+    assert _host_i32(d_start) is first and np.array_equal(first, inp["scale_start_index"])
+    bumped = d_start.clone()
+    bumped.add_(0)                                     # same values, new version
+    assert np.array_equal(_host_i32(bumped), first)
+    d_start.add_(1)
+    assert np.array_equal(_host_i32(d_start), inp["scale_start_index"] + 1)
+    d_start.sub_(1)
+
+    ref_out = vdf.da_forward(feat, inp["spatial_shape"], inp["scale_start_index"], loc, w)
+    ref_gf, ref_gl, ref_gw = vdf.da_backward(feat, inp["spatial_shape"], inp["scale_start_index"],
+                                             loc, w, go)
+    out = torch.empty_like(ref_out)
+    gf, gl, gw = torch.empty_like(ref_gf), torch.empty_like(ref_gl), torch.empty_like(ref_gw)
+    fws_n = vdf.forward_workspace_size(feat, inp["spatial_shape"], loc, w)
+    fws = torch.empty(fws_n, device="cuda", dtype=torch.uint8) if fws_n else None
+    bws = torch.empty(vdf.workspace_size(feat, inp["spatial_shape"], loc, w, deterministic=True),
+                      device="cuda", dtype=torch.uint8)
+
+    def step():
+        vdf.da_forward(feat, d_shape, d_start, loc, w, out=out, workspace=fws)
+        vdf.da_backward(feat, d_shape, d_start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                        grad_weights=gw, workspace=bws, deterministic=True)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                         # warms the table cache
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):                      # a blocking copy here would raise
+        step()
+    for _ in range(2):
+        out.fill_(float("nan"))
+        gf.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        assert torch.equal(gl, ref_gl) and torch.equal(gw, ref_gw)
+        assert_close("device tables grad_feat", gf.cpu().numpy(), ref_gf.cpu().numpy(), TOL_BWD)
+    del graph

@@ -203,6 +203,10 @@ RAGGED = [
                      loc_lo=-0.1, loc_hi=1.1)),
     ("clustered", dict(bs=2, num_cams=3, levels=((20, 50), (10, 25)), C=128, groups=4,
                        anchors=33, pts=13, loc_kind="clustered", loc_sigma=0.01)),
+    # a 150x130 level (19,500 rows: counted by two row tiles, the second ragged) next to
+    # a 70x70 one (4,900 rows, one tile) and a small one (LDS histogram)
+    ("c16_g2_row_tiles", dict(bs=2, num_cams=1, levels=((150, 130), (70, 70), (9, 11)), C=16,
+                              groups=2, anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05)),
 ]
 
 

@@ -14,6 +14,7 @@ device memory and the current stream.
 from __future__ import annotations
 
 import ctypes
+from collections import OrderedDict
 from typing import Optional, Sequence, Tuple, Union
 
 import numpy as np
@@ -32,10 +33,34 @@ _DTYPES = {torch.float32: _lib.DA_F32, torch.bfloat16: _lib.DA_BF16, torch.float
 _FLOATS = tuple(_DTYPES)
 
 
+# Host copies of device-resident level tables, keyed on the tensor's identity and
+# torch's version counter (bumped by every in-place update through torch).  Each
+# entry holds a reference to its tensor, so that its memory -- and so the key --
+# cannot be reused while cached.  A table that only kernels outside torch rewrite
+# in place would be served stale: level tables are constants in practice.
+_TABLE_CACHE: "OrderedDict[tuple, tuple]" = OrderedDict()
+_TABLE_CACHE_SIZE = 32
+
+
 def _host_i32(x: IntTable) -> np.ndarray:
-    """Level tables are read on the host; a device tensor is copied (synchronising)."""
+    """Level tables are read on the host.  A CPU tensor or array is converted; a device
+    tensor is copied to the host (one blocking copy) the first time it is seen, and
+    later calls with the same unchanged tensor reuse that copy without synchronising."""
     if isinstance(x, torch.Tensor):
-        x = x.detach().to("cpu").numpy()
+        if x.device.type == "cpu":
+            x = x.detach().numpy()
+        else:
+            key = (id(x), x.data_ptr(), x._version, tuple(x.shape), x.dtype, str(x.device))
+            hit = _TABLE_CACHE.get(key)
+            if hit is not None and hit[0] is x:
+                _TABLE_CACHE.move_to_end(key)
+                return hit[1]
+            host = np.ascontiguousarray(x.detach().to("cpu").numpy(), dtype=np.int32)
+            host.setflags(write=False)
+            _TABLE_CACHE[key] = (x, host)
+            while len(_TABLE_CACHE) > _TABLE_CACHE_SIZE:
+                _TABLE_CACHE.popitem(last=False)
+            return host
     return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
 
 

@@ -686,9 +686,11 @@ __device__ __forceinline__ uint32_t abs_max_bits(const float* p, int64_t n, int6
 // Small levels -- where many samples land on the same row, and same-address
 // global atomics would serialise -- are first counted in an LDS histogram of
 // the level; one global atomic per touched row then reserves the workgroup's
-// block of slots.  Large levels count straight into global memory.  The slot
+// block of slots.  Medium levels count straight into global memory, and levels
+// above kCountTileRows rows are left to count_tiles_kernel.  The slot
 // order inside a row is whatever order the atomics retire in.  The
-// deterministic form also takes the maxima of |weights| and |grad_out| here.
+// deterministic form also takes the maxima of |weights| and |grad_out| here
+// (in every workgroup, whatever its level).
 __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     __shared__ uint32_t hist[kCountLdsRows];
     const int lvl = blockIdx.y;
@@ -707,21 +709,27 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     const uint32_t q = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
     const uint32_t row0 = b * (uint32_t)a.num_feat;
 
+    if (!in_lds && nrow <= kCountTileRows) {
+        const Stencil st = make_stencil(a, (int64_t)ba, t);
+        uint32_t rk[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool hit = valid && st.row[c] >= 0;
+            rk[c] = hit ? atomicAdd(a.cnt + row0 + (uint32_t)st.row[c], 1u) : 0u;
+        }
+        if (valid)
+            *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
+    }
     if (in_lds) {
         for (int j = threadIdx.x; j < nrow; j += blockDim.x) hist[j] = 0u;
         __syncthreads();
-    }
-    const Stencil st = make_stencil(a, (int64_t)ba, t);
-    uint32_t rk[4];
+        const Stencil st = make_stencil(a, (int64_t)ba, t);
+        uint32_t rk[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const bool hit = valid && st.row[c] >= 0;
-        if (in_lds)
+        for (int c = 0; c < 4; ++c) {
+            const bool hit = valid && st.row[c] >= 0;
             rk[c] = hit ? atomicAdd(&hist[st.row[c] - start], 1u) : 0u;
-        else
-            rk[c] = hit ? atomicAdd(a.cnt + row0 + (uint32_t)st.row[c], 1u) : 0u;
-    }
-    if (in_lds) {
+        }
         // reserve each touched row's block of slots; every atomic is issued
         // before any result is needed
         constexpr int kPer = kCountLdsRows / kCountThreads;
@@ -747,9 +755,9 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             if (valid && st.row[c] >= 0) rk[c] += hist[st.row[c] - start];
+        if (valid)
+            *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
     }
-    if (valid)
-        *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
     if (a.det) {
         // bounds for the fixed point: this sample's weights and a share of
         // grad_out; the block's maxima go to bound_part (reduced by the scan)
@@ -780,6 +788,61 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
             a.bound_part[2 * fb + 1] = mw;
         }
     }
+}
+
+// Counting of the levels above kCountTileRows rows.  Workgroup (x, level, b) owns
+// rows [x, x + 1) * kCountTileRows of the level (in batch b) and scans every
+// (anchor, point) pair of the level: each inside corner that falls in its rows
+// takes the next slot of an LDS histogram, and the histogram is then stored as
+// those rows' counts.  Each row has one owner, so there is no global atomic;
+// every workgroup reads all of the level's locations (8 bytes per pair).  Blocks
+// of small levels, and tiles past a level's last row, return at once.
+__global__ void __launch_bounds__(kCountTileThreads) count_tiles_kernel(KArgs a) {
+    __shared__ uint32_t hist[kCountTileRows];
+    const int lvl = blockIdx.y;
+    const int32_t nrow = a.lv.H[lvl] * a.lv.W[lvl];
+    const int32_t r0 = (int32_t)blockIdx.x * kCountTileRows;
+    if (nrow <= kCountTileRows || r0 >= nrow) return;
+    const int32_t nr = min(kCountTileRows, nrow - r0);
+    const int k = lvl / a.S, s = lvl - k * a.S;
+    const int32_t lo = a.lv.start[lvl] + r0;          // first owned row in the batch image
+    const uint32_t b = blockIdx.z;
+    const uint32_t n_ap = (uint32_t)a.A * (uint32_t)a.P;
+    const uint32_t row0 = b * (uint32_t)a.num_feat;
+    for (int j = threadIdx.x; j < nr; j += blockDim.x) hist[j] = 0u;
+    __syncthreads();
+    // kU pairs per thread and step: their stencils (and so their location loads)
+    // are all formed before the first atomic or store, one memory latency per step
+    constexpr int kU = 4;
+    for (uint32_t ap0 = threadIdx.x; ap0 < n_ap; ap0 += kU * blockDim.x) {
+        Stencil st[kU];
+        uint32_t qs[kU];
+        bool ok[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const uint32_t ap = ap0 + (uint32_t)u * blockDim.x;
+            ok[u] = ap < n_ap;
+            const uint32_t apc = ok[u] ? ap : 0u;
+            const uint32_t ba = b * (uint32_t)a.A + apc / (uint32_t)a.P;
+            const int p = (int)(apc % (uint32_t)a.P);
+            const int t = (p * a.K + k) * a.S + s;
+            qs[u] = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
+            st[u] = make_stencil(a, (int64_t)ba, t);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // rows of the level outside the tile give a negative or too large
+                // index (outside corners have row -1: also rejected)
+                const int32_t j = st[u].row[c] - lo;
+                if (ok[u] && st[u].row[c] >= 0 && j >= 0 && j < nr)
+                    a.rank[(size_t)qs[u] * 4 + c] = atomicAdd(&hist[j], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nr; j += blockDim.x) a.cnt[row0 + (uint32_t)(lo + j)] = hist[j];
 }
 
 // Inclusive prefix sum of v over the 64 lanes of a wave.
@@ -1459,6 +1522,14 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     if (a.det && (uint64_t)cgrid.x * cgrid.y * cgrid.z != a.count_blocks) return hipErrorInvalidValue;
     hipLaunchKernelGGL(count_kernel, cgrid, dim3(kCountThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    int32_t max_rows = 0;
+    for (int l = 0; l < a.K * a.S; ++l) max_rows = std::max(max_rows, a.lv.H[l] * a.lv.W[l]);
+    if (max_rows > kCountTileRows) {
+        const dim3 tgrid((unsigned)((max_rows + kCountTileRows - 1) / kCountTileRows),
+                         (unsigned)(a.K * a.S), (unsigned)(a.n_anchors / (uint32_t)a.A));
+        hipLaunchKernelGGL(count_tiles_kernel, tgrid, dim3(kCountTileThreads), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     KArgs k = a;
