@@ -127,9 +127,11 @@ def effective_bytes(wl, out_bytes=4):
 
 def vector_memory_reference(reps=5):
     """GB/s that a plain streaming kernel of 16-byte loads (libbwprobe.so) reaches
-    when its buffer is resident in each CU's vector L1 (16 KiB buffer) and in each
-    XCD's L2 (2 MiB buffer, 64 KiB per pass, beyond L1): the rate at which the vector
-    memory path delivers cached bytes to the CUs, the roof of the effective bytes."""
+    when its buffer is resident in each CU's vector L1 (16 KiB buffer), in each XCD's
+    L2 (2 MiB buffer, 64 KiB per pass, beyond L1), in the Infinity Cache (64 MiB:
+    beyond the 8 x 4 MiB of L2, within the 256 MiB MALL) and in HBM only (1 GiB).  The
+    L1-resident rate is the fastest the vector memory path delivers bytes to the CUs:
+    the roof of the effective bytes."""
     import ctypes
     import torch
     from view_deformable_feature_amd.build import PROBE_PATH
@@ -142,7 +144,9 @@ def vector_memory_reference(reps=5):
     sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     res = {}
     for name, buf_bytes, chunk, passes in (("l1_resident", 16 << 10, 16 << 10, 256),
-                                           ("l2_resident", 2 << 20, 64 << 10, 64)):
+                                           ("l2_resident", 2 << 20, 64 << 10, 64),
+                                           ("mall_resident", 64 << 20, 64 << 10, 16),
+                                           ("hbm", 1 << 30, 64 << 10, 16)):
         buf = torch.ones(buf_bytes // 4, dtype=torch.float32, device="cuda")
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -163,8 +167,10 @@ def vector_memory_reference(reps=5):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         res[name] = round(blocks * chunk * passes / float(np.median(ts)) / 1e9, 1)
     return {"l1_resident_gbs": res["l1_resident"], "l2_resident_gbs": res["l2_resident"],
-            "unit": "GB/s", "kind": f"16-byte loads from a cache-resident buffer, {blocks} "
-                                    f"workgroups of 256 threads, median of {reps}"}
+            "mall_resident_gbs": res["mall_resident"], "hbm_gbs": res["hbm"],
+            "unit": "GB/s", "kind": f"16-byte loads streaming a 16 KiB / 2 MiB / 64 MiB / 1 GiB "
+                                    f"buffer, {blocks} workgroups of 256 threads, median of "
+                                    f"{reps}"}
 
 
 def effective_entry(bytes_, secs, vref):
