@@ -87,9 +87,11 @@ def copy_calibration(nbytes):
 
 
 FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
-BWD_KERNELS = ("da_backward call: prep_kernel, count_kernel, scan_tiles_kernel, "
-               "bucket_kernel (+ zeroing blocks), gather_kernel (+ group dot products), "
-               "finalize_kernel")
+BWD_KERNELS = ("da_backward call: prep_kernel, count_kernel (+ count_tiles_kernel for levels "
+               "above 16384 rows), scan_tiles_kernel, bucket_kernel (+ zeroing blocks), "
+               "gather_kernel (+ group dot products), finalize_kernel")
+BWD_ATOMIC_KERNELS = ("da_backward_atomic call: fill_zero_kernel, da_backward_anchor_kernel "
+                      "(binary32 atomics into grad_feat)")
 
 
 def compulsory_bytes(wl, out_bytes=4):
@@ -513,6 +515,10 @@ def main():
                     help="element type of out and grad_out (binary32 arithmetic throughout)")
     ap.add_argument("--deterministic", action="store_true",
                     help="run the backward in its deterministic (64-bit fixed-point) form")
+    ap.add_argument("--backward", default="gather", choices=("gather", "atomic"),
+                    help="gather: da_backward (row-sorted gather, the default); atomic: "
+                         "da_backward_atomic, the page's scatter of every feature-gradient "
+                         "term with a binary32 atomic")
     ap.add_argument("--launch", default="graph", choices=("graph", "eager"),
                     help="time the step as replays of one captured HIP graph (default) or as "
                          "eager calls; the per-call forward / backward times are eager either way")
@@ -568,8 +574,20 @@ def main():
     fws_n = vdf.forward_workspace_size(feat, shape, loc, w)
     fws = torch.empty(fws_n, device=dev, dtype=torch.uint8) if fws_n else None
     det = args.deterministic
-    bws = torch.empty(vdf.workspace_size(feat, shape, loc, w, deterministic=det,
-                                         grad_out_dtype=odt), device=dev, dtype=torch.uint8)
+    atomic = args.backward == "atomic"
+    if atomic and det:
+        raise SystemExit("the atomic backward has no deterministic form")
+    bws = None if atomic else torch.empty(vdf.workspace_size(feat, shape, loc, w, deterministic=det,
+                                                             grad_out_dtype=odt),
+                                          device=dev, dtype=torch.uint8)
+
+    def backward():
+        if atomic:
+            vdf.da_backward_atomic(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                                   grad_weights=gw)
+        else:
+            vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
+                            grad_weights=gw, workspace=bws, deterministic=det)
 
     def step(ev=None):
         if ev is not None:
@@ -577,8 +595,7 @@ def main():
         vdf.da_forward(feat, shape, start, loc, w, out=out, workspace=fws)
         if ev is not None:
             ev[1].record()
-        vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
-                        grad_weights=gw, workspace=bws, deterministic=det)
+        backward()
         if ev is not None:
             ev[2].record()
 
@@ -651,14 +668,17 @@ def main():
                                + f", C={wl.C}, groups={wl.groups}, anchors={wl.anchors}, "
                                  f"points={wl.pts}",
                    "sample_channels_per_step": sc, "out_dtype": args.out_dtype,
-                   "backward_form": "deterministic" if det else "default",
+                   "backward_form": ("atomic scatter (da_backward_atomic)" if atomic else
+                                     "deterministic" if det else "default"),
                    "launch": launch},
         "eager_ms_per_step": t_eager * 1e3,
         "forward": {"value": sc / fwd_s, "unit": "sample-channels/s", "avg_us": fwd_s * 1e6},
         "backward": {"avg_us": bwd_s * 1e6, "value": sc / bwd_s, "unit": "sample-channels/s"},
         "roofline": roof(b_bwd, e_bwd, bwd_s,
-                         BWD_KERNELS + (" (prep_kernel also converts grad_out)"
-                                        if args.out_dtype != "f32" else ""), "backward")
+                         (BWD_ATOMIC_KERNELS if atomic else BWD_KERNELS)
+                         + (" (prep_kernel also converts grad_out)"
+                            if args.out_dtype != "f32" and not atomic else ""),
+                         "backward_atomic" if atomic else "backward")
         if dominant == "backward" else roof(b_fwd, e_fwd, fwd_s, FWD_KERNELS, "forward"),
         "roofline_forward": roof(b_fwd, e_fwd, fwd_s, FWD_KERNELS, "forward"),
         "vector_memory_reference": vref,
@@ -677,8 +697,7 @@ def main():
             e[1].record()
             flush.fill_(1.0)
             e[2].record()
-            vdf.da_backward(feat, shape, start, loc, w, go, grad_feat=gf, grad_loc=gl,
-                            grad_weights=gw, workspace=bws, deterministic=det)
+            backward()
             e[3].record()
             torch.cuda.synchronize()
             cf.append(e[0].elapsed_time(e[1]) * 1e-3)

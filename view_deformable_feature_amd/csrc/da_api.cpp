@@ -410,13 +410,17 @@ bool fused_capable(const da_problem* p) {
 // locations (2.00 against 1.98 ms) and row-ordered wins by 12 % for clustered
 // ones (1.80 against 2.04 ms), which share rows more than the estimate says.
 // Below one corner per row each entry loads a row of its own.
-bool rows_reused(const da_problem* p, const da::KArgs& ka) {
-    if (p->flags & DA_FLAG_BWD_ROW_ORDER) return true;
+double min_corners_per_row(const da_problem* p, const da::KArgs& ka) {
     double worst = 1e30;
     for (int l = 0; l < ka.K * ka.S; ++l)
         worst = std::min(worst, 4.0 * (double)p->num_anchors * (double)p->num_pts /
                                     ((double)ka.lv.H[l] * (double)ka.lv.W[l]));
-    return worst >= 1.0;
+    return worst;
+}
+
+bool rows_reused(const da_problem* p, const da::KArgs& ka) {
+    if (p->flags & DA_FLAG_BWD_ROW_ORDER) return true;
+    return min_corners_per_row(p, ka) >= 1.0;
 }
 
 // Workspace of the gather form of the backward, each part 256-byte aligned.
@@ -579,6 +583,10 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
                     (uint32_t)((uint64_t)p->bs * p->num_feat * p->num_embeds * plan.elem);
                 ka.w_vec4 = p->num_groups % 4 == 0 && aligned(weights, 16) &&
                             aligned(grad_weights, 16);
+                // 16-bit rows with under two expected corners per row on the largest
+                // level: most entries load a row of their own, and deeper batches
+                // keep more of those loads in flight
+                ka.gather_deep = plan.elem == 2 && min_corners_per_row(p, ka) < 2.0 ? 1 : 0;
             } else {
                 plan_backward_sliced(p, plan);
             }

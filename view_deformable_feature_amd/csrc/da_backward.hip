@@ -1045,7 +1045,7 @@ __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
 // waves per SIMD 154 us per backward call, 4 entries at 5 waves 179 us).
 // SEG: lanes per weight group in the row-ordered form when fixed at compile time
 // (0: read from D), so that the group sums unroll to their DPP steps alone.
-template <typename T, int VEC, int NV, bool FUSED, bool DET, int SEG = 0>
+template <typename T, int VEC, int NV, bool FUSED, bool DET, int SEG = 0, int UB = 0>
 __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5) : (NV == 2 ? 4 : 1)) gather_kernel(KArgs a) {
     if (blockIdx.x >= a.gather_blocks) {
         loc_reduce_role(a);
@@ -1054,9 +1054,12 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
     // entries per batch, within the register budget.  One vector per lane: two
     // entries per batch in the row-ordered form (66 registers, 7 waves per SIMD)
     // and four in the plain form measured faster than larger batches at lower
-    // occupancy.
-    constexpr int U = FUSED ? (NV == 1 ? 2 : (NV >= 4 ? 1 : 4 / NV))
-                            : (NV == 1 ? 4 : (NV >= 8 ? 1 : 8 / NV));
+    // occupancy.  UB overrides the row-ordered form's batch where feature rows are
+    // sparse (most entries load a row of their own, and the wave waits on those
+    // loads): there more entries in flight per wave pay for the lower occupancy.
+    constexpr int U = UB ? UB
+                         : FUSED ? (NV == 1 ? 2 : (NV >= 4 ? 1 : 4 / NV))
+                                 : (NV == 1 ? 4 : (NV >= 8 ? 1 : 8 / NV));
     // FUSED: the feature row of the entry being added; a batch loads an entry's
     // row only where it differs from the previous entry's (else the load points
     // past the buffer: no memory request, zeros, and the row is kept here)
@@ -1432,8 +1435,12 @@ hipError_t gather_dispatch_det(const KArgs& a, const LaunchShape& s, dim3 grid, 
             if constexpr (FUSED) {
                 // 32 channels per weight group (C = 256 with G = 8, and the like)
                 if (a.D == 8 * VEC) {
-                    hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8>), grid, dim3(256), 0,
-                                       st, a);
+                    if (a.gather_deep)
+                        hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8, 4>), grid,
+                                           dim3(256), 0, st, a);
+                    else
+                        hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8>), grid,
+                                           dim3(256), 0, st, a);
                     break;
                 }
             }

@@ -117,6 +117,7 @@ struct KArgs {
     uint32_t feat_all_bytes;   // bs * num_feat * C * elem (< 2^32 on this path)
     float* dots;               // [n_samples, 4, G]: entry (q, corner) at (4q + corner) * G
     int32_t w_vec4;            // weights / grad_weights rows readable as float4
+    int32_t gather_deep;       // row-ordered gather: deeper batches (feature rows sparse)
     // Deterministic backward: feature-gradient sums in 64-bit fixed point
     int32_t det;
     long long* slots;          // [n_slots, C] accumulation rows of the long rows
