@@ -207,6 +207,10 @@ RAGGED = [
     # a 70x70 one (4,900 rows, one tile) and a small one (LDS histogram)
     ("c16_g2_row_tiles", dict(bs=2, num_cams=1, levels=((150, 130), (70, 70), (9, 11)), C=16,
                               groups=2, anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05)),
+    # 16,800 (anchor, point) pairs per image: levels counted in LDS take 8 samples per
+    # thread, 2048 per workgroup, the last chunk ragged
+    ("c16_g4_count_chunks", dict(bs=2, num_cams=1, levels=((40, 90), (30, 40), (9, 11)), C=16,
+                                 groups=4, anchors=2100, pts=8, loc_lo=-0.05, loc_hi=1.05)),
 ]
 
 

@@ -564,6 +564,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.long_rows = reinterpret_cast<uint32_t*>(ka.slots + (size_t)ka.n_slots * p->num_embeds);
             ka.bound_part = ka.long_rows + ka.n_slots;
             ka.count_blocks = (uint32_t)count_blocks(p);
+            ka.count_per = p->num_anchors * p->num_pts >= da::kCountChunkMinPairs ? da::kCountLdsPer : 1;
             if (p->out_dtype != DA_F32) {   // the gather reads binary32 grad_out rows
                 ka.go_src = grad_out;
                 ka.go_src_dtype = p->out_dtype;

@@ -681,8 +681,9 @@ __device__ __forceinline__ uint32_t abs_max_bits(const float* p, int64_t n, int6
 
 
 // Level-major counting.  Workgroup (x, level, b) takes 256 consecutive
-// (anchor, point) pairs of batch b at one (camera, scale) level, one thread per
-// sample, and gives every inside corner the next slot of its feature row.
+// (anchor, point) pairs of batch b at one (camera, scale) level (kCountLdsPer
+// times as many on levels counted in LDS), and gives every inside corner the
+// next slot of its feature row.
 // Small levels -- where many samples land on the same row, and same-address
 // global atomics would serialise -- are first counted in an LDS histogram of
 // the level; one global atomic per touched row then reserves the workgroup's
@@ -691,6 +692,7 @@ __device__ __forceinline__ uint32_t abs_max_bits(const float* p, int64_t n, int6
 // order inside a row is whatever order the atomics retire in.  The
 // deterministic form also takes the maxima of |weights| and |grad_out| here
 // (in every workgroup, whatever its level).
+template <int PER>
 __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     __shared__ uint32_t hist[kCountLdsRows];
     const int lvl = blockIdx.y;
@@ -720,16 +722,36 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
         if (valid)
             *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
     }
-    if (in_lds) {
+    // Levels of at most kCountLdsRows rows: PER samples per thread, so that the LDS
+    // histogram gathers many corners per row before the one global atomic per
+    // touched row (with one sample per thread a 4000-row level saw about one corner
+    // per row per workgroup, and the histogram saved almost no atomics).  Blocks
+    // past the level's last chunk have nothing to count.  PER is a template
+    // argument: its register arrays would otherwise cost the other paths occupancy.
+    const uint32_t i0 = blockIdx.x * (uint32_t)(PER * kCountThreads);
+    if (in_lds && i0 < n_ap) {
         for (int j = threadIdx.x; j < nrow; j += blockDim.x) hist[j] = 0u;
         __syncthreads();
-        const Stencil st = make_stencil(a, (int64_t)ba, t);
-        uint32_t rk[4];
+        int32_t rows[PER][4];               // level-relative rows of inside corners, else -1
+        uint32_t qs[PER];
+        // every sample's stencil (and so its location load) before the first atomic
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bool hit = valid && st.row[c] >= 0;
-            rk[c] = hit ? atomicAdd(&hist[st.row[c] - start], 1u) : 0u;
+        for (int u = 0; u < PER; ++u) {
+            const uint32_t iu = i0 + (uint32_t)u * kCountThreads + threadIdx.x;
+            const bool vu = iu < n_ap;
+            const uint32_t apu = vu ? iu : 0u;
+            const uint32_t bau = b * (uint32_t)a.A + apu / (uint32_t)a.P;
+            const int tu = ((int)(apu % (uint32_t)a.P) * a.K + k) * a.S + s;
+            qs[u] = vu ? bau * (uint32_t)(a.npk * a.S) + (uint32_t)tu : 0xffffffffu;
+            const Stencil st = make_stencil(a, (int64_t)bau, tu);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) rows[u][c] = (vu && st.row[c] >= 0) ? st.row[c] - start : -1;
         }
+        uint32_t rk[PER][4];
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) rk[u][c] = rows[u][c] >= 0 ? atomicAdd(&hist[rows[u][c]], 1u) : 0u;
         // reserve each touched row's block of slots; every atomic is issued
         // before any result is needed
         constexpr int kPer = kCountLdsRows / kCountThreads;
@@ -753,10 +775,14 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (valid && st.row[c] >= 0) rk[c] += hist[st.row[c] - start];
-        if (valid)
-            *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
+        for (int u = 0; u < PER; ++u) {
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2)
+                if (rows[u][c2] >= 0) rk[u][c2] += hist[rows[u][c2]];
+            if (qs[u] != 0xffffffffu)
+                *reinterpret_cast<uint4*>(a.rank + (size_t)qs[u] * 4) =
+                    make_uint4(rk[u][0], rk[u][1], rk[u][2], rk[u][3]);
+        }
     }
     if (a.det) {
         // bounds for the fixed point: this sample's weights and a share of
@@ -765,7 +791,19 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
         const uint32_t fb = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
         const uint32_t nb = gridDim.x * gridDim.y * gridDim.z;
         uint32_t mw = 0;
-        if (valid) mw = abs_max_bits(a.weights + (size_t)q * a.G, a.G, 0, 1);
+        if (in_lds) {
+            // the samples this block counted (PER per thread)
+            for (int u = 0; u < PER; ++u) {
+                const uint32_t iu = i0 + (uint32_t)u * kCountThreads + threadIdx.x;
+                if (iu >= n_ap) break;
+                const uint32_t bau = b * (uint32_t)a.A + iu / (uint32_t)a.P;
+                const int tu = ((int)(iu % (uint32_t)a.P) * a.K + k) * a.S + s;
+                const uint32_t qu = bau * (uint32_t)(a.npk * a.S) + (uint32_t)tu;
+                mw = max(mw, abs_max_bits(a.weights + (size_t)qu * a.G, a.G, 0, 1));
+            }
+        } else if (valid) {
+            mw = abs_max_bits(a.weights + (size_t)q * a.G, a.G, 0, 1);
+        }
         uint32_t mg = abs_max_bits(static_cast<const float*>(a.grad_out), (int64_t)a.n_anchors * a.C,
                                    (int64_t)fb * kCountThreads + threadIdx.x,
                                    (int64_t)nb * kCountThreads);
@@ -1524,10 +1562,16 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
                        const_cast<float*>(static_cast<const float*>(a.grad_out)), n_conv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the blocks of the atomic and tile paths take 256 samples each; the LDS path
+    // count_per (1 or kCountLdsPer) times as many, its blocks past the level's
+    // samples idle
     const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
     if (a.det && (uint64_t)cgrid.x * cgrid.y * cgrid.z != a.count_blocks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(count_kernel, cgrid, dim3(kCountThreads), 0, stream, a);
+    if (a.count_per == kCountLdsPer)
+        hipLaunchKernelGGL(count_kernel<kCountLdsPer>, cgrid, dim3(kCountThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(count_kernel<1>, cgrid, dim3(kCountThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t max_rows = 0;
     for (int l = 0; l < a.K * a.S; ++l) max_rows = std::max(max_rows, a.lv.H[l] * a.lv.W[l]);
