@@ -282,7 +282,8 @@ __device__ __forceinline__ DcnOm load_om(const DcnArgs& a, int pix, int g, int k
 // tile's window.  Tile sides are powers of two, and the flags are formed without
 // branches, so the records of several samples are formed side by side.
 __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t, int pix, int gy,
-                                             int gx, const DcnOm& o, bool home) {
+                                             int gx, const DcnOm& o, bool home, int TY, int TX,
+                                             int M) {
 #pragma clang fp contract(off)
     DcnRec r;
     r.pix = pix;
@@ -307,14 +308,14 @@ __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t,
     // (binary32 rounding of gy + dy is monotonic and gy +- M is exact), so gy lies
     // in the row window of the corner's tile; the same for x.  Only a sample with a
     // larger offset (or none at all) can have a far corner.
-    const float fm = (float)a.M;
+    const float fm = (float)M;
     if (home && !(o.dy >= -fm && o.dy <= fm && o.dx >= -fm && o.dx <= fm)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cy = r.y0 + (q >> 1), cx = r.x0 + (q & 1);
-            const int oy = cy & -a.TY, ox = cx & -a.TX;     // origin of the corner's tile
-            const bool reach = gy >= oy - a.M - 1 && gy <= oy + a.TY - 1 + a.M &&
-                               gx >= ox - a.M - 1 && gx <= ox + a.TX - 1 + a.M;
+            const int oy = cy & -TY, ox = cx & -TX;         // origin of the corner's tile
+            const bool reach = gy >= oy - M - 1 && gy <= oy + TY - 1 + M &&
+                               gx >= ox - M - 1 && gx <= ox + TX - 1 + M;
             const bool img = f >> (1 + q) & 1u, own = f >> (5 + q) & 1u;
             f |= (img && !own && !reach ? 1u : 0u) << (9 + q);
         }
@@ -603,12 +604,29 @@ __device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
 // 2^64, which leaves the exact sum of the rounded terms.
 constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;   // encoding of 1.5 * 2^52
 
-template <typename T, int VEC, int NVL, bool GOV>
+// Tile shape and lane layout of the tile kernel: from the arguments, or (FIXED = 1)
+// the compile-time shape that every group of 32 channels gets -- 8 x 16 pixels,
+// pixel stride 33 words, 4 lanes per sample, margin 4 -- which frees the scalar
+// registers those values and their products would hold.
+template <int FIXED>
+struct TileShape {
+    int TY, TX, Dp, Lg, log2Lg, M;
+    __device__ explicit TileShape(const DcnArgs& a)
+        : TY(a.TY), TX(a.TX), Dp(a.Dp), Lg(a.bLg), log2Lg(a.blog2Lg), M(a.M) {}
+};
+template <>
+struct TileShape<1> {
+    static constexpr int TY = 8, TX = 16, Dp = 33, Lg = 4, log2Lg = 2, M = 4;
+    __device__ explicit TileShape(const DcnArgs&) {}
+};
+
+template <typename T, int VEC, int NVL, bool GOV, int FIXED>
 __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int TY = a.TY, TX = a.TX;
+    const TileShape<FIXED> sh(a);
+    const int TY = sh.TY, TX = sh.TX;
     unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * a.Dp);        // [TY*TX][4]
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * sh.Dp);        // [TY*TX][4]
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     uint32_t* wl = cnt + TY * TX * 4 + wave * (kDcnListWords * kWave);
     const int E = dcn_fixed_exponent(a);
@@ -628,23 +646,23 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     t.Iy1 = min(t.Iy0 + TY, a.H);
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
-    for (int i = tid; i < TY * TX * a.Dp; i += kDcnTileThreads) acc[i] = 0ull;
+    for (int i = tid; i < TY * TX * sh.Dp; i += kDcnTileThreads) acc[i] = 0ull;
     for (int i = tid; i < TY * TX * 4; i += kDcnTileThreads) cnt[i] = 0u;
     __syncthreads();
 
-    const int jj = tid & (a.bLg - 1), slot = tid >> a.blog2Lg, spp = kDcnTileThreads >> a.blog2Lg;
+    const int jj = tid & (sh.Lg - 1), slot = tid >> sh.log2Lg, spp = kDcnTileThreads >> sh.log2Lg;
     int cl[NVL];             // channel offsets inside the group
     bool vv[NVL];
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
-        const int vi = jj + a.bLg * u;
+        const int vi = jj + sh.Lg * u;
         vv[u] = vi < a.Dv;
         cl[u] = vv[u] ? vi * VEC : 0;
     }
     const uint32_t gD = (uint32_t)(t.g * a.D);
     const __amdgpu_buffer_rsrc_t r_in = make_rsrc(a.input, a.in_bytes);
     constexpr int kElem = (int)sizeof(T);
-    const bool last = jj == a.bLg - 1;
+    const bool last = jj == sh.Lg - 1;
     // byte steps from corner 0 to corner q, and of the lane's vectors
     const uint32_t cq[4] = {0u, (uint32_t)(a.C * kElem), (uint32_t)(a.W * a.C * kElem),
                             (uint32_t)((a.W + 1) * a.C * kElem)};
@@ -659,10 +677,10 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     // in binary64 (idle vectors add nothing)
     // tile-pixel and sum-row steps from corner 0 to corner q
     const int dpq[4] = {0, 1, TX, TX + 1};
-    const int dpr[4] = {0, a.Dp, TX * a.Dp, (TX + 1) * a.Dp};
+    const int dpr[4] = {0, sh.Dp, TX * sh.Dp, (TX + 1) * sh.Dp};
     auto add_tile = [&](const DcnRec& R, const float (&cw)[4], const double (&gd)[NVL][VEC]) {
         const int pb = (R.y0 - t.Iy0) * TX + (R.x0 - t.Ix0);   // corner 0 (may lie outside)
-        const int rb = pb * a.Dp;
+        const int rb = pb * sh.Dp;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (!(R.flags >> (5 + q) & 1u)) continue;
@@ -699,7 +717,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
             divmod_small(idx, nw, inv_nw, oh, ow);
             const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
             const DcnRec R = dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox,
-                                        load_om(a, pix, t.g, k), true);
+                                        load_om(a, pix, t.g, k), true, TY, TX, sh.M);
             if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
                 const uint32_t sid = ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
                                          (uint32_t)a.K + (uint32_t)k;
@@ -741,7 +759,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
                     for (int q = 0; q < 4; ++q) S[q] += g * v[u][q][e];
                 }
             }
-            group_sum4(S, a.bLg);
+            group_sum4(S, sh.Lg);
             if (last) {
                 const bool live = R.flags & 1u;
                 const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
@@ -759,8 +777,8 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     }
 
     // ---- ring: other tiles' samples whose grid point lies in this tile's window ----
-    const int gpw = kWave >> a.blog2Lg;              // lane groups per wave
-    const int grp = lane >> a.blog2Lg;
+    const int gpw = kWave >> sh.log2Lg;              // lane groups per wave
+    const int grp = lane >> sh.log2Lg;
     // The wave's list collects the accepted candidates of every tap and is drained
     // (each lane group taking listed samples one at a time) only when the next batch
     // would not fit, and once at the end: one tap accepts only a few candidates per
@@ -804,8 +822,8 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
         int h0, h1, w0, w1;
-        out_range(t.Iy0 - a.M - 1, t.Iy0 + TY - 1 + a.M, a.SH, a.PH, ki * a.DH, a.Ho, h0, h1);
-        out_range(t.Ix0 - a.M - 1, t.Ix0 + TX - 1 + a.M, a.SW, a.PW, kj * a.DW, a.Wo, w0, w1);
+        out_range(t.Iy0 - sh.M - 1, t.Iy0 + TY - 1 + sh.M, a.SH, a.PH, ki * a.DH, a.Ho, h0, h1);
+        out_range(t.Ix0 - sh.M - 1, t.Ix0 + TX - 1 + sh.M, a.SW, a.PW, kj * a.DW, a.Wo, w0, w1);
         const int nw = w1 - w0 + 1;
         const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
         const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
@@ -818,7 +836,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
             const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
             const bool cand = idx < nh && !(cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1);
             const DcnOm o = cand ? load_om(a, pix, t.g, k) : DcnOm{0.0f, 0.0f, 0.0f};
-            const DcnRec R = dcn_record(a, t, pix, gy, gx, o, false);
+            const DcnRec R = dcn_record(a, t, pix, gy, gx, o, false, TY, TX, sh.M);
             const bool take = cand && (R.flags >> 5) != 0u;
             const unsigned long long mask = __ballot(take);
             const int n_take = __popcll(mask);
@@ -849,9 +867,9 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
         const int py = p / cols, px = p - (p / cols) * cols;
         const int tp = py * TX + px;
         const long long code =
-            (long long)(acc[tp * a.Dp + c] -
+            (long long)(acc[tp * sh.Dp + c] -
                         (unsigned long long)((cnt[4 * tp] + cnt[4 * tp + 1] + cnt[4 * tp + 2] +
-                                              cnt[4 * tp + 3]) >> a.blog2Lg) * kFixMagicBits);
+                                              cnt[4 * tp + 3]) >> sh.log2Lg) * kFixMagicBits);
         a.grad_input[(((int64_t)t.n * a.H + t.Iy0 + py) * a.W + t.Ix0 + px) * a.C + gD + c] =
             (float)((double)code * inv);
     }
@@ -879,7 +897,8 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
         const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         TileCtx t{n, g, 0, 0, 0, 0};            // empty tile: no corner counts as owned
         const DcnRec R = dcn_record(a, t, pix, ho * a.SH - a.PH + ki * a.DH,
-                                    wo * a.SW - a.PW + kj * a.DW, load_om(a, pix, g, k), false);
+                                    wo * a.SW - a.PW + kj * a.DW, load_om(a, pix, g, k), false,
+                                    a.TY, a.TX, a.M);
         float cw[4];
         corner_weights(R, cw);
         const float w = cw[q] * R.m;
@@ -925,7 +944,13 @@ hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
     hipLaunchKernelGGL(dcn_bound_kernel, dim3(kBoundGrid), dim3(kBoundThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV>), dim3(blocks), dim3(kDcnTileThreads), lds, st, a);
+    if (a.TY == TileShape<1>::TY && a.TX == TileShape<1>::TX && a.Dp == TileShape<1>::Dp &&
+        a.bLg == TileShape<1>::Lg && a.blog2Lg == TileShape<1>::log2Lg && a.M == TileShape<1>::M)
+        hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV, 1>), dim3(blocks),
+                           dim3(kDcnTileThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV, 0>), dim3(blocks),
+                           dim3(kDcnTileThreads), lds, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dcn_far_kernel<T, VEC, NVL, GOV>), dim3(1024), dim3(kDcnThreads), 0, st, a);
