@@ -1262,7 +1262,9 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
     // entries at positions p0 .. p0+U-1 of window `win` (p0 a multiple of U);
     // row_before: the row of the entry before the window (kNone for the first
     // window, so that the first entry a wave takes always loads its row)
-    auto issue = [&](const uint4& win, uint32_t row_before, int p0, Batch& B) {
+    // with_rows = false: the entries are only added where they continue the
+    // current row, whose feature row is loaded already
+    auto issue = [&](const uint4& win, uint32_t row_before, int p0, Batch& B, bool with_rows) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = p0 + u;
@@ -1283,7 +1285,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
                     u > 0 ? B.row[u > 0 ? u - 1 : 0]
                           : (p0 > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)win.x, p0 > 0 ? p0 - 1 : 0)
                                     : row_before);
-                B.fnew[u] = B.row[u] != prev;
+                B.fnew[u] = with_rows && B.row[u] != prev;
                 if (B.fnew[u]) {
                     const uint32_t rb = (B.row[u] & ~kEntryLongRow) * (uint32_t)a.row_bytes;
 #pragma unroll
@@ -1328,10 +1330,10 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
     {
         const int first = sp - sp % U;
         int p = first;
-        issue(win0, kNone, p, A);
+        issue(win0, kNone, p, A, true);
         while (true) {
             const int pn = min(p + U, kWave - U);
-            issue(win0, kNone, pn, B);
+            issue(win0, kNone, pn, B, true);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pos = p + u;
@@ -1346,7 +1348,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
             p += U;
             if (p >= n1) break;
             const int pn2 = min(p + U, kWave - U);
-            issue(win0, kNone, pn2, A);
+            issue(win0, kNone, pn2, A, true);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pos = p + u;
@@ -1363,18 +1365,51 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
         }
     }
     // phase 2: a short row that runs past the range end is finished here (it can
-    // only continue into win1: a range that ends early ends at the last entry)
+    // only continue into win1: a range that ends early ends at the last entry).
+    // Its entries continue the current row, whose feature row is loaded already.
+    // Batches of up to 2 entries keep the two-batch pipeline; with deeper batches
+    // the batch it prefetches past the row's end cost more than the overlap saves.
     if (n1 == kWave && !(cur & kEntryLongRow)) {
         bool done = false;
-        for (int p = 0; p < kWave && !done; p += U) {
-            issue(win1, last0, p, A);
+        if constexpr (U <= 2) {
+            int p = 0;
+            issue(win1, last0, 0, A, false);
+            while (true) {
+                issue(win1, last0, min(p + U, kWave - U), B, false);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!done) {
-                    if (A.row[u] != cur) {   // row ended (kNone past the last entry)
-                        done = true;
-                    } else {
-                        add(A, u);
+                for (int u = 0; u < U; ++u) {
+                    if (!done) {
+                        if (A.row[u] != cur)   // row ended (kNone past the last entry)
+                            done = true;
+                        else
+                            add(A, u);
+                    }
+                }
+                p += U;
+                if (done || p >= kWave) break;
+                issue(win1, last0, min(p + U, kWave - U), A, false);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (!done) {
+                        if (B.row[u] != cur)
+                            done = true;
+                        else
+                            add(B, u);
+                    }
+                }
+                p += U;
+                if (done || p >= kWave) break;
+            }
+        } else {
+            for (int p = 0; p < kWave && !done; p += U) {
+                issue(win1, last0, p, A, false);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (!done) {
+                        if (A.row[u] != cur)
+                            done = true;
+                        else
+                            add(A, u);
                     }
                 }
             }
@@ -1475,26 +1510,26 @@ hipError_t gather_dispatch_det(const KArgs& a, const LaunchShape& s, dim3 grid, 
                 if (a.D == 8 * VEC) {
                     if (a.gather_deep)
                         hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8, 4>), grid,
-                                           dim3(256), 0, st, a);
+                                           dim3(kGatherThreads), 0, st, a);
                     else
                         hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET, 8>), grid,
-                                           dim3(256), 0, st, a);
+                                           dim3(kGatherThreads), 0, st, a);
                     break;
                 }
             }
-            hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((gather_kernel<T, VEC, 1, FUSED, DET>), grid, dim3(kGatherThreads), 0, st, a);
             break;
-        case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED, DET>), grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED, DET>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gather_kernel<T, VEC, 2, FUSED, DET>), grid, dim3(kGatherThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gather_kernel<T, VEC, 4, FUSED, DET>), grid, dim3(kGatherThreads), 0, st, a); break;
         case 8:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<T, 1, 8, false, DET>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 8, false, DET>), grid, dim3(kGatherThreads), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
         case 16:
             if constexpr (VEC == 1) {
-                hipLaunchKernelGGL((gather_kernel<T, 1, 16, false, DET>), grid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((gather_kernel<T, 1, 16, false, DET>), grid, dim3(kGatherThreads), 0, st, a);
                 break;
             }
             return hipErrorInvalidValue;
@@ -1596,7 +1631,7 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         hipLaunchKernelGGL(bucket_kernel, dim3((unsigned)(k.anchor_blocks + blocks_for(zwaves, 256 / kWave))),
                            dim3(256), 0, stream, k);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k.gather_blocks = blocks_for(waves, 256 / kWave);
+        k.gather_blocks = blocks_for(waves, kGatherThreads / kWave);
         const dim3 ggrid(k.gather_blocks);
         e = with_elem(feat_dtype, [&](auto t) {
             return gather_dispatch<decltype(t), 4, true>(k, s, ggrid, stream);
@@ -1629,8 +1664,8 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
         // gather: one wave per chunk of the largest possible entry count (4 per
         // sample; waves past the real total return at once), followed in the
         // sliced form by blocks that add up the location partials
-        k.gather_blocks = blocks_for(waves, 256 / kWave);
-        const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, 256) : 0;
+        k.gather_blocks = blocks_for(waves, kGatherThreads / kWave);
+        const int64_t lr = a.sliced ? blocks_for((int64_t)a.n_anchors * a.npk, kGatherThreads) : 0;
         const dim3 ggrid((unsigned)(k.gather_blocks + lr));
         e = a.gather_vec == 4 ? gather_dispatch<float, 4, false>(k, s, ggrid, stream)
                               : gather_dispatch<float, 1, false>(k, s, ggrid, stream);
