@@ -238,6 +238,15 @@ void plan_forward_sliced(const da_problem* p, Plan& plan) {
     ka.sliced = 1;
     s.waves = waves;
     s.lds_bytes = lds;
+    // the sweep form (one wave per anchor and slice, samples in y order) where a
+    // wave holds two or more samples per step and a slice's samples fit one wave
+    const size_t sweep_lds =
+        (size_t)(da::kWave + 1) * da::kFwdDescBytes + (size_t)da::kWave * ka.G * 4;
+    if (spw >= 2 && n <= da::kWave && sweep_lds <= (size_t)da::kLdsBudget) {
+        ka.fwd_sweep = 1;
+        s.waves = 1;
+        s.lds_bytes = sweep_lds;
+    }
 }
 
 // Switch a planned gather backward to level slices when wanted and supported.

@@ -296,6 +296,118 @@ da_forward_sliced_kernel(KArgs a) {
     }
 }
 
+// Sweep form of the sliced forward: one wave per (anchor, slice).  Each wave
+// sorts its slice's samples (at most 64) by normalised y and walks them in that
+// order, so the waves resident together read the rows of about one band of
+// every level at a time instead of the whole slice: fewer L2 misses where a
+// slice's levels exceed an XCD's L2.  Taken where a wave holds at least two
+// samples per step (two or more row groups); with one, the wave's chain of
+// samples is twice as long and the form measured slower.  The partial is a sum
+// in y order (ties and NaN by sample order): fixed for given inputs.
+template <typename T, int VEC, int NV>
+__global__ void __launch_bounds__(kWave) da_forward_sweep_kernel(KArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int x = (int)(blockIdx.x % (uint32_t)kSlices);
+    const int64_t ba = blockIdx.x / (uint32_t)kSlices;
+    const int64_t b = ba / a.A;
+    const int lane = threadIdx.x;
+    const int L = a.L;
+    const int rg = lane >> a.log2L;
+    const int n_rg = kWave >> a.log2L;
+    const int li = lane & (L - 1);
+    constexpr int kElem = (int)sizeof(T);
+
+    FwdDesc* desc = reinterpret_cast<FwdDesc*>(smem);          // [kWave + 1]
+    float* wts = reinterpret_cast<float*>(smem + (size_t)(kWave + 1) * sizeof(FwdDesc));
+
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(
+        static_cast<const unsigned char*>(a.feat) + b * a.feat_batch_bytes, a.feat_image_bytes);
+    const int v0 = blockIdx.y * NV;
+    const uint32_t lane_off = (uint32_t)(li * VEC * kElem);
+    uint32_t soff[NV];
+    int gi[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        soff[i] = (uint32_t)(L * (v0 + i) * VEC * kElem);
+        gi[i] = (li + L * (v0 + i)) * VEC / a.D;
+    }
+    float acc[NV][VEC];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[i][e] = 0.0f;
+
+    const int m = a.lv.slice_nlev[x];
+    const int n = a.P * m;                        // <= kWave (the host checks)
+    __shared__ int32_t lvl_lds[3 * kMaxLevels + kMaxSliceLevels];
+    int32_t* slice_lv = lvl_lds + 3 * kMaxLevels;
+    if (lane < m) slice_lv[lane] = a.lv.slice_level[x][lane];
+    const LevelsLds lv = stage_levels(a, lvl_lds);
+
+    // lane j stages sample j at its rank in y order
+    int t = 0;
+    float key = __builtin_huge_valf();
+    if (lane < n) {
+        t = slice_sample(a, slice_lv, m, lane);
+        const float y = a.loc[(ba * a.npk + t / a.S) * 2 + 1];
+        key = y == y ? y : 2.0f;
+    }
+    int rank = 0;
+    for (int i = 0; i < kWave; ++i) {
+        const float ki = __shfl(key, i, kWave);
+        rank += (ki < key || (ki == key && i < lane)) ? 1 : 0;
+    }
+    if (lane < n) {
+        const Stencil st = make_stencil(a, ba, t, lv);
+        FwdDesc d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d.off[i] = st.row[i] >= 0 ? (uint32_t)st.row[i] * (uint32_t)a.row_bytes
+                                      : a.feat_image_bytes;
+            d.cw[i] = st.cw[i];
+        }
+        desc[rank] = d;
+        const float* wsrc = a.weights + (ba * (int64_t)a.npk * a.S + t) * a.G;
+        for (int g = 0; g < a.G; ++g) wts[rank * a.G + g] = wsrc[g];
+    }
+    if (lane == 0) desc[kWave] = null_fwd_desc(a.feat_image_bytes);
+    __syncthreads();
+
+    int s = rg;
+    if (s < n) {
+        FwdDesc dA = desc[s], dB;
+        float vA[NV][4][VEC], vB[NV][4][VEC];
+        fwd_load<T, VEC, NV>(rsrc, dA, lane_off, soff, vA);
+        while (true) {
+            int sn = s + n_rg;
+            dB = desc[sn < n ? sn : kWave];
+            fwd_load<T, VEC, NV>(rsrc, dB, lane_off, soff, vB);
+            fwd_accumulate<VEC, NV>(dA, wts + s * a.G, gi, vA, acc);
+            if (sn >= n) break;
+            s = sn;
+            sn = s + n_rg;
+            dA = desc[sn < n ? sn : kWave];
+            fwd_load<T, VEC, NV>(rsrc, dA, lane_off, soff, vA);
+            fwd_accumulate<VEC, NV>(dB, wts + s * a.G, gi, vB, acc);
+            if (sn >= n) break;
+            s = sn;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            for (int mk = L; mk < kWave; mk <<= 1) acc[i][e] += xor_shfl(acc[i][e], mk);
+    if (lane < L) {
+        float* prow = a.fwd_part + ((int64_t)x * a.n_anchors + ba) * a.C + (int64_t)v0 * L * VEC;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) prow[(li + L * i) * VEC + e] = acc[i][e];
+    }
+}
+
 // out = sum of the 8 slice partials, added in slice order.
 __global__ void __launch_bounds__(256) fwd_reduce_kernel(KArgs a) {
     const int64_t n = (int64_t)a.n_anchors * a.C;
@@ -310,8 +422,12 @@ __global__ void __launch_bounds__(256) fwd_reduce_kernel(KArgs a) {
 
 template <typename T, int VEC, int NV>
 hipError_t fwd_sliced_launch(const KArgs& a, const LaunchShape& s, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((da_forward_sliced_kernel<T, VEC, NV>), grid, dim3(kWave * s.waves),
-                       s.lds_bytes, st, a);
+    if (a.fwd_sweep)
+        hipLaunchKernelGGL((da_forward_sweep_kernel<T, VEC, NV>), grid, dim3(kWave), s.lds_bytes,
+                           st, a);
+    else
+        hipLaunchKernelGGL((da_forward_sliced_kernel<T, VEC, NV>), grid, dim3(kWave * s.waves),
+                           s.lds_bytes, st, a);
     return hipGetLastError();
 }
 

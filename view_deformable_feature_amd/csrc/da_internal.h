@@ -116,6 +116,7 @@ struct KArgs {
     int32_t sliced;            // 1: 8 workgroups per anchor, one per level slice
     int32_t max_slice_samples; // P * max over slices of the slice's level count
     int32_t sample_chunk;      // sliced kernels: samples staged in LDS at once
+    int32_t fwd_sweep;         // sliced forward: one wave per (anchor, slice), samples in y order
     // Blocks past anchor_blocks of a gather-form per-anchor launch zero the
     // feature-gradient rows that need it; blocks past gather_blocks of the
     // gather launch add up the location partials (sliced form).
