@@ -203,10 +203,14 @@ RAGGED = [
                      loc_lo=-0.1, loc_hi=1.1)),
     ("clustered", dict(bs=2, num_cams=3, levels=((20, 50), (10, 25)), C=128, groups=4,
                        anchors=33, pts=13, loc_kind="clustered", loc_sigma=0.01)),
-    # a 150x130 level (19,500 rows: counted by two row tiles, the second ragged) next to
-    # a 70x70 one (4,900 rows, one tile) and a small one (LDS histogram)
+    # a 150x130 level (19,500 rows: counted by two row tiles) next to a 70x70 one
+    # (4,900 rows: also two tiles, since tiles run) and a small one (LDS histogram)
     ("c16_g2_row_tiles", dict(bs=2, num_cams=1, levels=((150, 130), (70, 70), (9, 11)), C=16,
                               groups=2, anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05)),
+    # the same with odd row counts: 19,781 rows in two tiles of 9,891 and 9,890 rows,
+    # 4,899 in two of 2,450 and 2,449 (every tiled level is cut into as many tiles)
+    ("c16_g2_row_tiles_odd", dict(bs=2, num_cams=1, levels=((151, 131), (71, 69), (9, 11)), C=16,
+                                  groups=2, anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05)),
     # 16,800 (anchor, point) pairs per image: levels counted in LDS take 8 samples per
     # thread, 2048 per workgroup, the last chunk ragged
     ("c16_g4_count_chunks", dict(bs=2, num_cams=1, levels=((40, 90), (30, 40), (9, 11)), C=16,
@@ -455,6 +459,9 @@ DET_CASES = [
                       pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)),
     ("c96_g3_bf16", dict(bs=2, num_cams=3, levels=((13, 29), (7, 15), (3, 8)), C=96, groups=3,
                          anchors=37, pts=5, loc_lo=-0.1, loc_hi=1.1, feat_dtype="bf16", seed=7)),
+    # levels counted by row tiles (two per tiled level, ragged) beside an LDS-counted one
+    ("row_tiles", dict(bs=2, num_cams=1, levels=((151, 131), (71, 69), (9, 11)), C=16, groups=2,
+                       anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05, seed=62)),
 ]
 
 

@@ -688,7 +688,7 @@ __device__ __forceinline__ uint32_t abs_max_bits(const float* p, int64_t n, int6
 // global atomics would serialise -- are first counted in an LDS histogram of
 // the level; one global atomic per touched row then reserves the workgroup's
 // block of slots.  Medium levels count straight into global memory, and levels
-// above kCountTileRows rows are left to count_tiles_kernel.  The slot
+// above count_tile_rows rows are left to count_tiles_kernel.  The slot
 // order inside a row is whatever order the atomics retire in.  The
 // deterministic form also takes the maxima of |weights| and |grad_out| here
 // (in every workgroup, whatever its level).
@@ -711,7 +711,7 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     const uint32_t q = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
     const uint32_t row0 = b * (uint32_t)a.num_feat;
 
-    if (!in_lds && nrow <= kCountTileRows) {
+    if (!in_lds && nrow <= a.count_tile_rows) {
         const Stencil st = make_stencil(a, (int64_t)ba, t);
         uint32_t rk[4];
 #pragma unroll
@@ -828,8 +828,8 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
     }
 }
 
-// Counting of the levels above kCountTileRows rows.  Workgroup (x, level, b) owns
-// rows [x, x + 1) * kCountTileRows of the level (in batch b) and scans every
+// Counting of the levels above count_tile_rows rows.  Workgroup (x, level, b) owns
+// tile x of the level's rows (in batch b) and scans every
 // (anchor, point) pair of the level: each inside corner that falls in its rows
 // takes the next slot of an LDS histogram, and the histogram is then stored as
 // those rows' counts.  Each row has one owner, so there is no global atomic;
@@ -839,9 +839,14 @@ __global__ void __launch_bounds__(kCountTileThreads) count_tiles_kernel(KArgs a)
     __shared__ uint32_t hist[kCountTileRows];
     const int lvl = blockIdx.y;
     const int32_t nrow = a.lv.H[lvl] * a.lv.W[lvl];
-    const int32_t r0 = (int32_t)blockIdx.x * kCountTileRows;
-    if (nrow <= kCountTileRows || r0 >= nrow) return;
-    const int32_t nr = min(kCountTileRows, nrow - r0);
+    // every tiled level is cut into the same gridDim.x tiles (of at most
+    // kCountTileRows rows: the grid is sized for the largest level), so that each
+    // workgroup counts about the same number of corners -- every level has the
+    // same samples
+    const int32_t tr = (nrow + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
+    const int32_t r0 = (int32_t)blockIdx.x * tr;
+    if (nrow <= a.count_tile_rows || r0 >= nrow) return;
+    const int32_t nr = min(tr, nrow - r0);
     const int k = lvl / a.S, s = lvl - k * a.S;
     const int32_t lo = a.lv.start[lvl] + r0;          // first owned row in the batch image
     const uint32_t b = blockIdx.z;
@@ -1603,17 +1608,23 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     const dim3 cgrid(blocks_for((int64_t)a.A * a.P, kCountThreads), (unsigned)(a.K * a.S),
                      (unsigned)(a.n_anchors / (uint32_t)a.A));
     if (a.det && (uint64_t)cgrid.x * cgrid.y * cgrid.z != a.count_blocks) return hipErrorInvalidValue;
-    if (a.count_per == kCountLdsPer)
-        hipLaunchKernelGGL(count_kernel<kCountLdsPer>, cgrid, dim3(kCountThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(count_kernel<1>, cgrid, dim3(kCountThreads), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // Row tiles take the levels above kCountTileRows rows.  Once they run, they also
+    // take every level above the LDS histogram's kCountLdsRows: each tile workgroup
+    // scans a whole level's pairs whatever its rows, so the extra levels' workgroups
+    // run beside the others at no cost in time, and their returning atomics go.
     int32_t max_rows = 0;
     for (int l = 0; l < a.K * a.S; ++l) max_rows = std::max(max_rows, a.lv.H[l] * a.lv.W[l]);
+    KArgs ca = a;
+    ca.count_tile_rows = max_rows > kCountTileRows ? kCountLdsRows : kCountTileRows;
+    if (a.count_per == kCountLdsPer)
+        hipLaunchKernelGGL(count_kernel<kCountLdsPer>, cgrid, dim3(kCountThreads), 0, stream, ca);
+    else
+        hipLaunchKernelGGL(count_kernel<1>, cgrid, dim3(kCountThreads), 0, stream, ca);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (max_rows > kCountTileRows) {
         const dim3 tgrid((unsigned)((max_rows + kCountTileRows - 1) / kCountTileRows),
                          (unsigned)(a.K * a.S), (unsigned)(a.n_anchors / (uint32_t)a.A));
-        hipLaunchKernelGGL(count_tiles_kernel, tgrid, dim3(kCountTileThreads), 0, stream, a);
+        hipLaunchKernelGGL(count_tiles_kernel, tgrid, dim3(kCountTileThreads), 0, stream, ca);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);

@@ -138,6 +138,7 @@ struct KArgs {
     uint32_t* bound_part;      // [count_kernel blocks][2] each block's max |grad_out|, max |w|
     uint32_t count_blocks;
     int32_t count_per;         // count_kernel: samples per thread on levels counted in LDS
+    int32_t count_tile_rows;   // levels of more rows are counted by count_tiles_kernel
     int64_t feat_batch_bytes;  // num_feat * C * elem: byte stride between batch images
     int64_t gfeat_batch_bytes; // num_feat * C * 4
     uint32_t feat_image_bytes; // buffer range of one feature image; also the "outside" offset
