@@ -189,7 +189,7 @@ DA_API da_status da_forward(const da_problem* problem,
  * another (8 * C + 4) * (4 * bs*A*P*K*S / 65 + 1) + 8 * bs*K*S * ceil(A*P / 256);
  * with a 16-bit out_dtype another 4 * bs*A*C (grad_out converted to binary32).
  * Only the sizes and flags in `problem` are read.  Returns DA_ERR_UNSUPPORTED when bs * num_feat
- * >= 2^31, the sample count bs*A*P*K*S >= 2^30, or grad_out or weights exceed
+ * >= 2^31, the sample count bs*A*P*K*S >= 2^29, or grad_out or weights exceed
  * 2^32 - 1 bytes (da_backward_atomic still works).
  */
 DA_API da_status da_backward_workspace_size(const da_problem* problem, size_t* bytes);

@@ -272,6 +272,19 @@ def test_forward_workspace_size_follows_the_slicing_rule(lib):
     assert lib.da_forward_workspace_size(ctypes.byref(_prob()), None) == 1
 
 
+def test_backward_sample_limit(lib):
+    # the gather form keeps entry positions (4 per sample) below 2^31: a flag takes
+    # their top bit, so 2^29 samples are refused and one fewer is sized
+    n = ctypes.c_size_t(0)
+    # 4 channels: grad_out (2 GiB) and weights (2 GiB) stay under the 4 GiB buffer range
+    below = _prob(num_anchors=(1 << 27) - 1, num_pts=4, num_embeds=4)   # 2^29 - 4 samples
+    assert lib.da_backward_workspace_size(ctypes.byref(below), ctypes.byref(n)) == 0
+    assert n.value > 88 * ((1 << 29) - 4)
+    at = _prob(num_anchors=1 << 27, num_pts=4, num_embeds=4)            # 2^29 samples
+    assert lib.da_backward_workspace_size(ctypes.byref(at), ctypes.byref(n)) == 2
+    assert "sample count" in _msg(lib)
+
+
 def test_forward_workspace_checks(lib):
     p = _prob(flags=1)
     need = 8 * 8 * 32 * 4

@@ -497,7 +497,8 @@ da_status gather_sizes(const da_problem* p, uint64_t& n_rows, uint64_t& n_sample
                     "backward: grad_out (%llu bytes) or weights (%llu bytes) exceed 4 GiB for the "
                     "gather workspace (use da_backward_atomic)",
                     (unsigned long long)go_bytes, (unsigned long long)w_bytes);
-    if (n_rows >= (1ull << 31) || n_samples >= (1ull << 30))
+    // (entry positions, 4 per sample, stay below 2^31: their top bit is a flag)
+    if (n_rows >= (1ull << 31) || n_samples >= (1ull << 29))
         return fail(DA_ERR_UNSUPPORTED,
                     "backward: bs * num_feat (%llu) or the sample count (%llu) is too large for the "
                     "gather workspace (use da_backward_atomic)",

@@ -113,18 +113,19 @@ __device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st,
     const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)q * 4);
     const uint32_t rks[4] = {rk.x, rk.y, rk.z, rk.w};
     const uint32_t base = (uint32_t)b * (uint32_t)a.num_feat;
-    uint32_t fr[4], cn[4], first[4];
+    uint32_t fr[4], ls[4], first[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fr[i] = base + (uint32_t)(st.row[i] >= 0 ? st.row[i] : 0);
+    // local_start carries the row's long flag in its top bit (set by the scan)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        cn[i] = a.cnt[fr[i]];
-        first[i] = a.tile_prefix[fr[i] / (uint32_t)kScanTile] + a.local_start[fr[i]];
+        ls[i] = a.local_start[fr[i]];
+        first[i] = a.tile_prefix[fr[i] / (uint32_t)kScanTile] + (ls[i] & ~kEntryLongRow);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         Entry e;
-        e.row = fr[i] | (cn[i] > (uint32_t)kGatherLong ? kEntryLongRow : 0u);
+        e.row = fr[i] | (ls[i] & kEntryLongRow);
         e.w_off = q * (uint32_t)a.G * 4u;
         e.cw = st.cw[i];
         e.go_off = (uint32_t)ba * (uint32_t)a.C * 4u + (uint32_t)i;
@@ -186,7 +187,7 @@ __device__ __forceinline__ void store_grad_weights(float (&gwp)[NV], const int (
 
 // First entry of a row in the row-sorted list.
 __device__ __forceinline__ uint32_t first_entry(const KArgs& a, uint32_t row) {
-    return a.tile_prefix[row / (uint32_t)kScanTile] + a.local_start[row];
+    return a.tile_prefix[row / (uint32_t)kScanTile] + (a.local_start[row] & ~kEntryLongRow);
 }
 
 // Zero the feature-gradient rows r0 .. r0+63 (r0 = 64 w) that have no entry,
@@ -922,13 +923,17 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j) v[j] = (base + j < n) ? a.cnt[base + j] : 0u;
     }
-    uint32_t tot = 0, vmax = 0;
+    // v becomes the exclusive prefix; lng marks the long rows (more than
+    // kGatherLong entries), whose flag goes into local_start's top bit (the
+    // prefix inside a tile stays below 2^31: the host caps the sample count)
+    uint32_t tot = 0, vmax = 0, lng = 0;
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
         const uint32_t c = v[j];
         v[j] = tot;
         tot += c;
         vmax = max(vmax, c);
+        lng |= (c > (uint32_t)kGatherLong ? 1u : 0u) << j;
     }
     if (a.det) {   // the longest row bounds every row sum of the deterministic form
         for (int m = 1; m < kWave; m <<= 1)
@@ -944,14 +949,15 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
     const uint32_t excl = before + incl - tot;
     if (base + kScanItems <= n) {
         uint4* dst = reinterpret_cast<uint4*>(a.local_start + base);
+        auto f = [&](int j) { return (excl + v[j]) | (lng >> j & 1u ? kEntryLongRow : 0u); };
 #pragma unroll
         for (int j = 0; j < kScanItems / 4; ++j)
-            dst[j] = make_uint4(excl + v[4 * j], excl + v[4 * j + 1], excl + v[4 * j + 2],
-                                excl + v[4 * j + 3]);
+            dst[j] = make_uint4(f(4 * j), f(4 * j + 1), f(4 * j + 2), f(4 * j + 3));
     } else {
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j)
-            if (base + j < n) a.local_start[base + j] = excl + v[j];
+            if (base + j < n)
+                a.local_start[base + j] = (excl + v[j]) | (lng >> j & 1u ? kEntryLongRow : 0u);
     }
     if (threadIdx.x == kScanThreads - 1) a.tile_prefix[blockIdx.x] = excl + tot;
 }

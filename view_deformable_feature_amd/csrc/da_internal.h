@@ -106,7 +106,8 @@ struct KArgs {
     // feature-gradient gather workspace
     uint32_t* scan_done;       // control words (kCtrl*), zeroed with cnt, which follows them
     uint32_t* cnt;             // [n_rows] entries per row, then per-row rank source
-    uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile
+    uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile, with
+                               // kEntryLongRow set for rows of more than kGatherLong entries
     uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
     uint32_t* rank;            // [4 * n_samples] rank of (sample, corner) inside its row
     Entry* entries;            // [4 * n_samples] row-sorted entries
