@@ -490,6 +490,11 @@ da_backward_sliced_kernel(KArgs a) {
 // One thread per sample: its stencil, and its inside corners into the row-sorted
 // entry list.  Blocks past anchor_blocks zero the rows the gather does not
 // store whole.
+// Workgroups in (batch image, level, chunk of 256 anchor-point pairs) order,
+// that list cut into kSlices contiguous parts and part x given to the
+// workgroups on XCD x (ids congruent to x): each XCD then writes one contiguous
+// stretch of the row-sorted entries and reads one stretch of local_start, in its
+// own L2, instead of every XCD touching every level's lines.
 __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
     if (blockIdx.x >= a.anchor_blocks) {
         zero_rows_role(a);
@@ -497,12 +502,22 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
     }
     __shared__ int32_t lvl_lds[3 * kMaxLevels];
     const LevelsLds lv = stage_levels(a, lvl_lds);
-    const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.n_samples) return;
-    const uint32_t per_anchor = (uint32_t)(a.npk * a.S);
-    const uint32_t ba = q / per_anchor;
-    const int t = (int)(q - ba * per_anchor);
-    const uint32_t b = ba / (uint32_t)a.A;
+    const uint32_t n_ap = (uint32_t)a.A * (uint32_t)a.P;
+    const uint32_t nlev = (uint32_t)(a.K * a.S);
+    const uint32_t cpl = (n_ap + 255u) / 256u;                      // chunks per level
+    const uint32_t total = (a.n_anchors / (uint32_t)a.A) * nlev * cpl;
+    const uint32_t per_x = a.anchor_blocks / (uint32_t)kSlices;
+    const uint32_t tri = (blockIdx.x % (uint32_t)kSlices) * per_x + blockIdx.x / (uint32_t)kSlices;
+    if (tri >= total) return;
+    const uint32_t b = tri / (nlev * cpl);
+    const uint32_t rem = tri - b * nlev * cpl;
+    const uint32_t lvl = rem / cpl;
+    const uint32_t ap = (rem - lvl * cpl) * 256u + threadIdx.x;
+    if (ap >= n_ap) return;
+    const int k = (int)lvl / a.S, s = (int)lvl - ((int)lvl / a.S) * a.S;
+    const uint32_t ba = b * (uint32_t)a.A + ap / (uint32_t)a.P;
+    const int t = ((int)(ap % (uint32_t)a.P) * a.K + k) * a.S + s;
+    const uint32_t q = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
     const Stencil st = make_stencil(a, (int64_t)ba, t, lv);
     bucket_sample(a, st, (int64_t)b, (int64_t)ba, q);
 }
@@ -1645,7 +1660,12 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     if (a.fused) {
         // bucketing (+ zeroing blocks), the gather with the dot products, then
         // the per-sample gradients
-        k.anchor_blocks = blocks_for((int64_t)a.n_samples, 256);
+        {
+            // kSlices equal parts of the (image, level, 256-pair chunk) list
+            const int64_t triples = (int64_t)(a.n_anchors / (uint32_t)a.A) * a.K * a.S *
+                                    blocks_for((int64_t)a.A * a.P, 256);
+            k.anchor_blocks = (uint32_t)(kSlices * ((triples + kSlices - 1) / kSlices));
+        }
         hipLaunchKernelGGL(bucket_kernel, dim3((unsigned)(k.anchor_blocks + blocks_for(zwaves, 256 / kWave))),
                            dim3(256), 0, stream, k);
         if ((e = hipGetLastError()) != hipSuccess) return e;
