@@ -108,9 +108,21 @@ __device__ __forceinline__ BwdDesc bwd_desc(const KArgs& a, const Stencil& st) {
 // each goes to its row's slot rank[q][corner] (taken by count_kernel).  All
 // lookups are issued before any store (outside corners read row 0 and store
 // nothing), so a thread waits for one round of loads, not one per corner.
+// Rank slot of sample t of anchor ba (in batch image b).  The ranks are stored
+// level-major -- [image][level][anchor-point] -- the order in which the counting
+// kernels write them and the bucket kernel reads them.
+__device__ __forceinline__ uint32_t rank_slot(const KArgs& a, uint32_t b, uint32_t ba, int t) {
+    const int pk = t / a.S, s = t - pk * a.S;
+    const int p = pk / a.K, k = pk - p * a.K;
+    const uint32_t n_ap = (uint32_t)a.A * (uint32_t)a.P;
+    const uint32_t ap = (ba - b * (uint32_t)a.A) * (uint32_t)a.P + (uint32_t)p;
+    return (b * (uint32_t)(a.K * a.S) + (uint32_t)(k * a.S + s)) * n_ap + ap;
+}
+
+// q: the flat sample index (its weight row); rs: its rank slot.
 __device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st, int64_t b,
-                                              int64_t ba, uint32_t q) {
-    const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)q * 4);
+                                              int64_t ba, uint32_t q, uint32_t rs) {
+    const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)rs * 4);
     const uint32_t rks[4] = {rk.x, rk.y, rk.z, rk.w};
     const uint32_t base = (uint32_t)b * (uint32_t)a.num_feat;
     uint32_t fr[4], ls[4], first[4];
@@ -304,7 +316,9 @@ da_backward_anchor_kernel(KArgs a) {
         for (int t = x.tid; t < ns; t += x.nthreads) {
             const Stencil st = make_stencil(a, ba, pk0 * S + t);
             desc[t] = bwd_desc(a, st);
-            if (!SCATTER) bucket_sample(a, st, b, ba, q_anchor + (uint32_t)(pk0 * S + t));
+            if (!SCATTER)
+                bucket_sample(a, st, b, ba, q_anchor + (uint32_t)(pk0 * S + t),
+                              rank_slot(a, (uint32_t)b, (uint32_t)ba, pk0 * S + t));
         }
         const float* wsrc = a.weights + wbase + (int64_t)pk0 * S * a.G;
         for (int i = x.tid; i < ns * a.G; i += x.nthreads) wts[i] = wsrc[i];
@@ -439,7 +453,8 @@ da_backward_sliced_kernel(KArgs a) {
             const Stencil st = make_stencil(a, ba, t);
             desc[jj] = bwd_desc(a, st);
             tix[jj] = t;
-            bucket_sample(a, st, b, ba, q_anchor + (uint32_t)t);
+            bucket_sample(a, st, b, ba, q_anchor + (uint32_t)t,
+                          rank_slot(a, (uint32_t)b, (uint32_t)ba, t));
         }
         for (int i = tid; i < nsc * a.G; i += nthreads) {
             const int jj = i / a.G;
@@ -519,7 +534,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
     const int t = ((int)(ap % (uint32_t)a.P) * a.K + k) * a.S + s;
     const uint32_t q = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
     const Stencil st = make_stencil(a, (int64_t)ba, t, lv);
-    bucket_sample(a, st, (int64_t)b, (int64_t)ba, q);
+    bucket_sample(a, st, (int64_t)b, (int64_t)ba, q, (b * nlev + lvl) * n_ap + ap);
 }
 
 constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot products for G <= 8
@@ -736,7 +751,8 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
             rk[c] = hit ? atomicAdd(a.cnt + row0 + (uint32_t)st.row[c], 1u) : 0u;
         }
         if (valid)
-            *reinterpret_cast<uint4*>(a.rank + (size_t)q * 4) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
+            *reinterpret_cast<uint4*>(a.rank + ((size_t)(b * (uint32_t)(a.K * a.S) + (uint32_t)lvl) * n_ap + i) * 4) =
+                make_uint4(rk[0], rk[1], rk[2], rk[3]);
     }
     // Levels of at most kCountLdsRows rows: PER samples per thread, so that the LDS
     // histogram gathers many corners per row before the one global atomic per
@@ -758,7 +774,7 @@ __global__ void __launch_bounds__(kCountThreads) count_kernel(KArgs a) {
             const uint32_t apu = vu ? iu : 0u;
             const uint32_t bau = b * (uint32_t)a.A + apu / (uint32_t)a.P;
             const int tu = ((int)(apu % (uint32_t)a.P) * a.K + k) * a.S + s;
-            qs[u] = vu ? bau * (uint32_t)(a.npk * a.S) + (uint32_t)tu : 0xffffffffu;
+            qs[u] = vu ? (b * (uint32_t)(a.K * a.S) + (uint32_t)lvl) * n_ap + iu : 0xffffffffu;   // rank slot
             const Stencil st = make_stencil(a, (int64_t)bau, tu);
 #pragma unroll
             for (int c = 0; c < 4; ++c) rows[u][c] = (vu && st.row[c] >= 0) ? st.row[c] - start : -1;
@@ -885,7 +901,7 @@ __global__ void __launch_bounds__(kCountTileThreads) count_tiles_kernel(KArgs a)
             const uint32_t ba = b * (uint32_t)a.A + apc / (uint32_t)a.P;
             const int p = (int)(apc % (uint32_t)a.P);
             const int t = (p * a.K + k) * a.S + s;
-            qs[u] = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
+            qs[u] = (b * (uint32_t)(a.K * a.S) + (uint32_t)lvl) * n_ap + apc;   // rank slot
             st[u] = make_stencil(a, (int64_t)ba, t);
         }
 #pragma unroll

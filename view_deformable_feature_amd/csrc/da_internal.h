@@ -109,7 +109,7 @@ struct KArgs {
     uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile, with
                                // kEntryLongRow set for rows of more than kGatherLong entries
     uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
-    uint32_t* rank;            // [4 * n_samples] rank of (sample, corner) inside its row
+    uint32_t* rank;            // [bs, K*S, A*P, 4] rank of (sample, corner) inside its row
     Entry* entries;            // [4 * n_samples] row-sorted entries
     // sliced per-anchor kernels
     float* fwd_part;           // [kSlices, bs*A, C] forward partial sums, one per slice
