@@ -538,7 +538,10 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
 }
 
 constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot products for G <= 8
-constexpr int kFinalizeThreads = 256;
+// Three waves per workgroup: with G = 8 a workgroup stages 26 KB of dot products,
+// so six fit a CU and 280,800 samples run in one round (at 256 threads, 35 KB,
+// four fit and the last 7 % of the workgroups ran as a second round).
+constexpr int kFinalizeThreads = 192;
 
 // One thread per sample q: from the per-corner group dot products
 // d[c][g] = sum over the channels of group g of grad_out * corner value c (formed
