@@ -467,8 +467,8 @@ WsLayout ws_layout(uint64_t n_rows, uint64_t n_samples, uint64_t dot_groups, uin
     off += align256(n_rows * 4);
     w.local_start = off;
     off += align256(n_rows * 4);
-    w.tile_prefix = off;
-    off += align256((n_tiles + 1) * 4);
+    w.tile_prefix = off;                  // then the n_tiles tile totals
+    off += align256((2 * n_tiles + 1) * 4);
     w.rank = off;
     off += align256(n_samples * 16);
     w.entries = off;
@@ -565,6 +565,7 @@ da_status backward_impl(BwdMode mode, const da_problem* p, const void* feat,
             ka.cnt = reinterpret_cast<uint32_t*>(base + w.cnt);
             ka.local_start = reinterpret_cast<uint32_t*>(base + w.local_start);
             ka.tile_prefix = reinterpret_cast<uint32_t*>(base + w.tile_prefix);
+            ka.tile_tot = ka.tile_prefix + (n_rows + da::kScanTile - 1) / da::kScanTile + 1;
             ka.rank = reinterpret_cast<uint32_t*>(base + w.rank);
             ka.entries = reinterpret_cast<da::Entry*>(base + w.entries);
             ka.loc_part = reinterpret_cast<float*>(base + w.loc_part);

@@ -108,6 +108,72 @@ __device__ __forceinline__ BwdDesc bwd_desc(const KArgs& a, const Stencil& st) {
 // each goes to its row's slot rank[q][corner] (taken by count_kernel).  All
 // lookups are issued before any store (outside corners read row 0 and store
 // nothing), so a thread waits for one round of loads, not one per corner.
+// Inclusive prefix sum of v over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix of the tile totals into tp[0 .. n_tiles), the grand total in
+// tp[n_tiles] (every thread of the block calls this; tp in LDS or global memory).
+__device__ __forceinline__ void tile_totals_prefix(const KArgs& a, uint32_t* tp) {
+    __shared__ uint32_t wsum[kScanThreads / kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int nw = (int)blockDim.x / kWave;
+    uint32_t carry = 0;
+    for (uint32_t b0 = 0; b0 < a.n_tiles; b0 += blockDim.x) {
+        const uint32_t i = b0 + threadIdx.x;
+        const uint32_t t = i < a.n_tiles ? a.tile_tot[i] : 0u;
+        const uint32_t inc = wave_inclusive_scan(t, lane);
+        __syncthreads();                       // wsum of the previous round is read
+        if (lane == kWave - 1) wsum[wave] = inc;
+        __syncthreads();
+        uint32_t pre = 0, all = 0;
+        for (int w2 = 0; w2 < nw; ++w2) {
+            if (w2 < wave) pre += wsum[w2];
+            all += wsum[w2];
+        }
+        if (i < a.n_tiles) tp[i] = carry + pre + inc - t;
+        carry += all;
+    }
+    if (threadIdx.x == 0) tp[a.n_tiles] = carry;
+    __syncthreads();
+}
+
+// Deterministic form: the count blocks' maxima of |grad_out| and |w| into the
+// control words (one block).
+__device__ __forceinline__ void reduce_det_bounds(const KArgs& a) {
+    __shared__ uint32_t red[2][kScanThreads / kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int nw = (int)blockDim.x / kWave;
+    uint32_t mg = 0, mw = 0;
+    for (uint32_t i = threadIdx.x; i < a.count_blocks; i += blockDim.x) {
+        mg = max(mg, a.bound_part[2 * i]);
+        mw = max(mw, a.bound_part[2 * i + 1]);
+    }
+    for (int m = 1; m < kWave; m <<= 1) {
+        mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
+        mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
+    }
+    if (lane == 0) {
+        red[0][wave] = mg;
+        red[1][wave] = mw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w2 = 1; w2 < nw; ++w2) {
+            mg = max(mg, red[0][w2]);
+            mw = max(mw, red[1][w2]);
+        }
+        a.scan_done[kCtrlMaxGo] = mg;
+        a.scan_done[kCtrlMaxW] = mw;
+    }
+}
+
 // Rank slot of sample t of anchor ba (in batch image b).  The ranks are stored
 // level-major -- [image][level][anchor-point] -- the order in which the counting
 // kernels write them and the bucket kernel reads them.
@@ -121,7 +187,8 @@ __device__ __forceinline__ uint32_t rank_slot(const KArgs& a, uint32_t b, uint32
 
 // q: the flat sample index (its weight row); rs: its rank slot.
 __device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st, int64_t b,
-                                              int64_t ba, uint32_t q, uint32_t rs) {
+                                              int64_t ba, uint32_t q, uint32_t rs,
+                                              const uint32_t* tprefix) {
     const uint4 rk = *reinterpret_cast<const uint4*>(a.rank + (size_t)rs * 4);
     const uint32_t rks[4] = {rk.x, rk.y, rk.z, rk.w};
     const uint32_t base = (uint32_t)b * (uint32_t)a.num_feat;
@@ -132,7 +199,7 @@ __device__ __forceinline__ void bucket_sample(const KArgs& a, const Stencil& st,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ls[i] = a.local_start[fr[i]];
-        first[i] = a.tile_prefix[fr[i] / (uint32_t)kScanTile] + (ls[i] & ~kEntryLongRow);
+        first[i] = tprefix[fr[i] / (uint32_t)kScanTile] + (ls[i] & ~kEntryLongRow);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -198,14 +265,17 @@ __device__ __forceinline__ void store_grad_weights(float (&gwp)[NV], const int (
 }
 
 // First entry of a row in the row-sorted list.
-__device__ __forceinline__ uint32_t first_entry(const KArgs& a, uint32_t row) {
-    return a.tile_prefix[row / (uint32_t)kScanTile] + (a.local_start[row] & ~kEntryLongRow);
+// tprefix: the exclusive prefix of the tile totals (a.tile_prefix, or a copy in LDS)
+__device__ __forceinline__ uint32_t first_entry(const KArgs& a, const uint32_t* tprefix,
+                                                uint32_t row) {
+    return tprefix[row / (uint32_t)kScanTile] + (a.local_start[row] & ~kEntryLongRow);
 }
 
 // Zero the feature-gradient rows r0 .. r0+63 (r0 = 64 w) that have no entry,
 // and the long rows that gather_kernel adds to range by range.
 template <int ZVEC>
-__device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int lane) {
+__device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int lane,
+                                               const uint32_t* tprefix) {
     const uint32_t r0 = w * (uint32_t)kWave;
     if (r0 >= a.n_rows) return;
     const uint32_t r = r0 + (uint32_t)lane;
@@ -239,7 +309,7 @@ __device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int l
             if (long_row && base + rank < a.n_slots) a.long_rows[base + rank] = r;
         }
         // every lane looks up its own long row's slot before the loop
-        const uint32_t slot_id = long_row ? first_entry(a, r) / kSlotStride : 0u;
+        const uint32_t slot_id = long_row ? first_entry(a, tprefix, r) / kSlotStride : 0u;
         while (m) {
             const int l = __ffsll((unsigned long long)m) - 1;
             m &= m - 1;
@@ -256,13 +326,13 @@ __device__ __forceinline__ void zero_rows_wave(const KArgs& a, uint32_t w, int l
 }
 
 // The zeroing role of the blocks past anchor_blocks: 64 rows per wave.
-__device__ __forceinline__ void zero_rows_role(const KArgs& a) {
+__device__ __forceinline__ void zero_rows_role(const KArgs& a, const uint32_t* tprefix) {
     const uint32_t w = (blockIdx.x - a.anchor_blocks) * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     if (a.gather_vec == 4)
-        zero_rows_wave<4>(a, w, lane);
+        zero_rows_wave<4>(a, w, lane, tprefix);
     else
-        zero_rows_wave<1>(a, w, lane);
+        zero_rows_wave<1>(a, w, lane, tprefix);
 }
 
 template <typename T, int VEC, int NV, bool SCATTER>
@@ -270,7 +340,7 @@ __global__ void __launch_bounds__(kWave * kMaxWaves)
 da_backward_anchor_kernel(KArgs a) {
     if constexpr (!SCATTER) {
         if (blockIdx.x >= a.anchor_blocks) {
-            zero_rows_role(a);
+            zero_rows_role(a, a.tile_prefix);
             return;
         }
     }
@@ -318,7 +388,7 @@ da_backward_anchor_kernel(KArgs a) {
             desc[t] = bwd_desc(a, st);
             if (!SCATTER)
                 bucket_sample(a, st, b, ba, q_anchor + (uint32_t)(pk0 * S + t),
-                              rank_slot(a, (uint32_t)b, (uint32_t)ba, pk0 * S + t));
+                              rank_slot(a, (uint32_t)b, (uint32_t)ba, pk0 * S + t), a.tile_prefix);
         }
         const float* wsrc = a.weights + wbase + (int64_t)pk0 * S * a.G;
         for (int i = x.tid; i < ns * a.G; i += x.nthreads) wts[i] = wsrc[i];
@@ -402,7 +472,7 @@ template <typename T, int VEC, int NV>
 __global__ void __launch_bounds__(kWave * kMaxWaves)
 da_backward_sliced_kernel(KArgs a) {
     if (blockIdx.x >= a.anchor_blocks) {
-        zero_rows_role(a);
+        zero_rows_role(a, a.tile_prefix);
         return;
     }
     extern __shared__ __align__(16) unsigned char smem[];
@@ -454,7 +524,7 @@ da_backward_sliced_kernel(KArgs a) {
             desc[jj] = bwd_desc(a, st);
             tix[jj] = t;
             bucket_sample(a, st, b, ba, q_anchor + (uint32_t)t,
-                          rank_slot(a, (uint32_t)b, (uint32_t)ba, t));
+                          rank_slot(a, (uint32_t)b, (uint32_t)ba, t), a.tile_prefix);
         }
         for (int i = tid; i < nsc * a.G; i += nthreads) {
             const int jj = i / a.G;
@@ -510,9 +580,24 @@ da_backward_sliced_kernel(KArgs a) {
 // workgroups on XCD x (ids congruent to x): each XCD then writes one contiguous
 // stretch of the row-sorted entries and reads one stretch of local_start, in its
 // own L2, instead of every XCD touching every level's lines.
+//
+// tot_in_bucket: every workgroup first forms the prefix of the scan's tile
+// totals in LDS (at most kBucketLdsTiles of them), and workgroup 0 also stores
+// it as tile_prefix and reduces the deterministic form's bounds, for the
+// kernels that follow: one launch fewer than a separate scan of the totals.
 __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
+    __shared__ uint32_t tp_lds[kBucketLdsTiles + 1];
+    const uint32_t* tprefix = a.tile_prefix;
+    if (a.tot_in_bucket) {
+        tile_totals_prefix(a, tp_lds);
+        if (blockIdx.x == 0) {
+            for (uint32_t i = threadIdx.x; i <= a.n_tiles; i += blockDim.x) a.tile_prefix[i] = tp_lds[i];
+            if (a.det) reduce_det_bounds(a);
+        }
+        tprefix = tp_lds;
+    }
     if (blockIdx.x >= a.anchor_blocks) {
-        zero_rows_role(a);
+        zero_rows_role(a, tprefix);
         return;
     }
     __shared__ int32_t lvl_lds[3 * kMaxLevels];
@@ -534,7 +619,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(KArgs a) {
     const int t = ((int)(ap % (uint32_t)a.P) * a.K + k) * a.S + s;
     const uint32_t q = ba * (uint32_t)(a.npk * a.S) + (uint32_t)t;
     const Stencil st = make_stencil(a, (int64_t)ba, t, lv);
-    bucket_sample(a, st, (int64_t)b, (int64_t)ba, q, (b * nlev + lvl) * n_ap + ap);
+    bucket_sample(a, st, (int64_t)b, (int64_t)ba, q, (b * nlev + lvl) * n_ap + ap, tprefix);
 }
 
 constexpr int kFinalizeLdsGroups = 8;   // finalize_kernel stages the dot products for G <= 8
@@ -923,16 +1008,6 @@ __global__ void __launch_bounds__(kCountTileThreads) count_tiles_kernel(KArgs a)
     for (int j = threadIdx.x; j < nr; j += blockDim.x) a.cnt[row0 + (uint32_t)(lo + j)] = hist[j];
 }
 
-// Inclusive prefix sum of v over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
 // Exclusive prefix sum of cnt inside tiles of kScanTile rows, tile totals to
 // tile_prefix[tile]; scan_totals_kernel then turns those into their exclusive
 // prefix.  (A last-workgroup-finishes pattern in one launch needs a device-scope
@@ -993,57 +1068,16 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(KArgs a) {
             if (base + j < n)
                 a.local_start[base + j] = (excl + v[j]) | (lng >> j & 1u ? kEntryLongRow : 0u);
     }
-    if (threadIdx.x == kScanThreads - 1) a.tile_prefix[blockIdx.x] = excl + tot;
+    if (threadIdx.x == kScanThreads - 1) a.tile_tot[blockIdx.x] = excl + tot;
 }
 
-// One workgroup: tile_prefix[0 .. n_tiles) becomes the exclusive prefix of the
-// tile totals, with the grand total in tile_prefix[n_tiles]; the deterministic
-// form also reduces the count blocks' maxima of |grad_out| and |w|.
+// One workgroup: tile_prefix becomes the exclusive prefix of the tile totals
+// (with the grand total in tile_prefix[n_tiles]), and the deterministic form's
+// bounds are reduced.  The row-ordered backward leaves both to bucket_kernel
+// where the tiles are few.
 __global__ void __launch_bounds__(kScanThreads) scan_totals_kernel(KArgs a) {
-    __shared__ uint32_t wave_tot[kScanThreads / kWave], wave_tot2[kScanThreads / kWave];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    uint32_t carry = 0;
-    for (uint32_t b0 = 0; b0 < a.n_tiles; b0 += kScanThreads) {
-        const uint32_t i = b0 + threadIdx.x;
-        const uint32_t t = i < a.n_tiles ? a.tile_prefix[i] : 0u;
-        const uint32_t inc = wave_inclusive_scan(t, lane);
-        __syncthreads();                       // wave_tot of the previous round is read
-        if (lane == kWave - 1) wave_tot[wave] = inc;
-        __syncthreads();
-        uint32_t pre = 0, all = 0;
-        for (int w2 = 0; w2 < kScanThreads / kWave; ++w2) {
-            if (w2 < wave) pre += wave_tot[w2];
-            all += wave_tot[w2];
-        }
-        if (i < a.n_tiles) a.tile_prefix[i] = carry + pre + inc - t;
-        carry += all;
-    }
-    if (threadIdx.x == 0) a.tile_prefix[a.n_tiles] = carry;
-    if (a.det) {
-        uint32_t mg = 0, mw = 0;
-        for (uint32_t i = threadIdx.x; i < a.count_blocks; i += kScanThreads) {
-            mg = max(mg, a.bound_part[2 * i]);
-            mw = max(mw, a.bound_part[2 * i + 1]);
-        }
-        for (int m = 1; m < kWave; m <<= 1) {
-            mg = max(mg, (uint32_t)__shfl_xor((int)mg, m, kWave));
-            mw = max(mw, (uint32_t)__shfl_xor((int)mw, m, kWave));
-        }
-        __syncthreads();                       // wave_tot is reused
-        if (lane == 0) {
-            wave_tot[wave] = mg;
-            wave_tot2[wave] = mw;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int w2 = 1; w2 < kScanThreads / kWave; ++w2) {
-                mg = max(mg, wave_tot[w2]);
-                mw = max(mw, wave_tot2[w2]);
-            }
-            a.scan_done[kCtrlMaxGo] = mg;
-            a.scan_done[kCtrlMaxW] = mw;
-        }
-    }
+    tile_totals_prefix(a, a.tile_prefix);
+    if (a.det) reduce_det_bounds(a);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1090,7 +1124,7 @@ __global__ void __launch_bounds__(256) long_rows_kernel(KArgs a) {
     if (w >= min(a.scan_done[kCtrlLongRows], a.n_slots)) return;
     const int E = det_exponent(a);
     const uint32_t row = a.long_rows[w];
-    const long long* slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * a.C;
+    const long long* slot = a.slots + (size_t)(first_entry(a, a.tile_prefix, row) / kSlotStride) * a.C;
     float* out = a.grad_feat + (size_t)row * a.C;
     for (int c = lane; c < a.C; c += kWave) {
         const float v = from_fixed(slot[c], E);
@@ -1243,7 +1277,7 @@ __global__ void __launch_bounds__(256, NV == 1 ? (DET && sizeof(T) == 4 ? 4 : 5)
         long long* slot = nullptr;
         if constexpr (DET) {
             if (row_bits & kEntryLongRow)
-                slot = a.slots + (size_t)(first_entry(a, row) / kSlotStride) * C;
+                slot = a.slots + (size_t)(first_entry(a, a.tile_prefix, row) / kSlotStride) * C;
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -1668,9 +1702,13 @@ hipError_t launch_backward_gather(const KArgs& a, const LaunchShape& s, int64_t 
     }
     hipLaunchKernelGGL(scan_tiles_kernel, dim3(a.n_tiles), dim3(kScanThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     KArgs k = a;
+    // the row-ordered form's bucket kernel adds up the tile totals itself
+    k.tot_in_bucket = a.fused && a.n_tiles <= (uint32_t)kBucketLdsTiles ? 1 : 0;
+    if (!k.tot_in_bucket) {
+        hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t row_waves = ((int64_t)a.n_rows + kWave - 1) / kWave;
     // rows to zero before the gather: none when accumulating, unless long rows
     // need their 64-bit accumulation rows zeroed

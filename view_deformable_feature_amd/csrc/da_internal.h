@@ -18,6 +18,13 @@ constexpr int kLdsBudget = 48 * 1024;
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr int kScanTile = kScanThreads * kScanItems;   // 4096
+// The row-ordered backward's bucket kernel forms the prefix of the tile totals
+// itself (in LDS, every workgroup) where there are at most this many tiles --
+// one pass of its 256 threads.  Measured: 22 tiles (nuScenes shape) save the
+// separate launch (step -0.9 us, deterministic -4.3 us); with 498 tiles (4 x
+// 510k rows) every one of ~9,750 workgroups repeating a two-pass prefix cost
+// more (+4 us) than the launch.
+constexpr int kBucketLdsTiles = 256;
 // Levels with at most this many rows are counted in an LDS histogram first
 // (measured: merging pays even when a workgroup's 1024 corners spread over
 // 2816 rows, against same-address traffic from every XCD).
@@ -109,6 +116,8 @@ struct KArgs {
     uint32_t* local_start;     // [n_rows] exclusive prefix of cnt inside its scan tile, with
                                // kEntryLongRow set for rows of more than kGatherLong entries
     uint32_t* tile_prefix;     // [n_tiles + 1] exclusive prefix of tile totals; [n_tiles] = total
+    uint32_t* tile_tot;        // [n_tiles] the scan tiles' totals
+    int32_t tot_in_bucket;     // 1: bucket_kernel forms tile_prefix (no scan_totals_kernel)
     uint32_t* rank;            // [bs, K*S, A*P, 4] rank of (sample, corner) inside its row
     Entry* entries;            // [4 * n_samples] row-sorted entries
     // sliced per-anchor kernels
