@@ -218,6 +218,18 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("rows_h", [1024, 1025])
+def test_row_order_scan_tile_boundary(rows_h):
+    """1024 x 1024 rows are 256 scan tiles, whose totals every bucket workgroup
+    adds up itself; 1025 x 1024 rows are 257 tiles, added up by a separate launch.
+    Row-ordered form, 1,600 samples over a million rows (most rows zeroed, the
+    level counted by 64 row tiles)."""
+    wl = W.custom(f"tiles_{rows_h}", bs=1, num_cams=1, levels=((rows_h, 1024),), C=4, groups=1,
+                  anchors=200, pts=8, loc_lo=0.0, loc_hi=1.0, seed=90 + rows_h % 7)
+    inp = W.make_inputs(wl)
+    _full_check(inp, TOL_FWD, TOL_BWD, wl.name, *MODES["roworder"])
+
+
 @pytest.mark.parametrize("name, kw", RAGGED, ids=[r[0] for r in RAGGED])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["auto", "sliced", "roworder", "regather_sliced"])
@@ -459,6 +471,9 @@ DET_CASES = [
                       pts=8, loc_lo=0.0, loc_hi=1.0, seed=61)),
     ("c96_g3_bf16", dict(bs=2, num_cams=3, levels=((13, 29), (7, 15), (3, 8)), C=96, groups=3,
                          anchors=37, pts=5, loc_lo=-0.1, loc_hi=1.1, feat_dtype="bf16", seed=7)),
+    # 256 scan tiles: the bucket kernel adds up the tile totals and reduces the bounds
+    ("tiles_256", dict(bs=1, num_cams=1, levels=((1024, 1024),), C=4, groups=1, anchors=200,
+                       pts=8, loc_lo=0.0, loc_hi=1.0, seed=63)),
     # levels counted by row tiles (two per tiled level, ragged) beside an LDS-counted one
     ("row_tiles", dict(bs=2, num_cams=1, levels=((151, 131), (71, 69), (9, 11)), C=16, groups=2,
                        anchors=300, pts=12, loc_lo=-0.05, loc_hi=1.05, seed=62)),
