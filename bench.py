@@ -88,7 +88,8 @@ def copy_calibration(nbytes):
 
 FWD_KERNELS = "da_forward call: da_forward_sliced_kernel, fwd_reduce_kernel"
 BWD_KERNELS = ("da_backward call: prep_kernel, count_kernel (+ count_tiles_kernel for levels "
-               "above 16384 rows), scan_tiles_kernel, scan_totals_kernel, bucket_kernel (+ zeroing blocks), "
+               "above 16384 rows), scan_tiles_kernel (+ scan_totals_kernel above 256 tiles), "
+               "bucket_kernel (+ zeroing blocks), "
                "gather_kernel (+ group dot products), finalize_kernel")
 BWD_ATOMIC_KERNELS = ("da_backward_atomic call: fill_zero_kernel, da_backward_anchor_kernel "
                       "(binary32 atomics into grad_feat)")
