@@ -167,7 +167,41 @@ __global__ void __launch_bounds__(kDcnThreads) dcn_forward_kernel(DcnArgs a) {
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[i][e] = 0.0f;
-    if (a.K == 9) {
+    if (a.K == 9 && NV == 1 && a.Lg >= 7) {
+        // 3x3 kernel, a group spanning 7 lanes or more: lane j of the group loads
+        // 16-byte chunk j of the group's 27 offsets and scalars (lanes 7 and up
+        // none), and each tap takes its three values from the lanes holding them
+        // (cross-lane permutes) -- the record is read once per group, not once per
+        // lane.  Lanes of one group belong to one pixel, so all are active together.
+        const __amdgpu_buffer_rsrc_t r_om = make_rsrc(a.om, a.om_bytes);
+        const int lane = threadIdx.x % kWave;
+        const int jg = lane & (a.Lg - 1), gbase = lane - jg;
+        const uint32_t ro = ((uint32_t)L.pix * (uint32_t)a.G + (uint32_t)L.gq[0]) * 108u;
+        float q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (jg < 7) {
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(r_om, ro + 16u * (uint32_t)jg, 0u, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) q4[c] = __uint_as_float(q[c]);
+        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            const int ki = k / 3, kj = k % 3;
+            const int gy = L.ho * a.SH - a.PH + ki * a.DH;
+            const int gx = L.wo * a.SW - a.PW + kj * a.DW;
+            const float dx = __shfl(q4[(2 * k) % 4], gbase + (2 * k) / 4, kWave);
+            const float dy = __shfl(q4[(2 * k + 1) % 4], gbase + (2 * k + 1) / 4, kWave);
+            const float m = __shfl(q4[(18 + k) % 4], gbase + (18 + k) / 4, kWave);
+            const DcnStencil st = dcn_stencil(a, L.n, gy, gx, dy, dx, L.c0[0], kElem);
+            float v[4][VEC];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                VecLoad<T, VEC>::run(r_in, L.valid[0] ? st.off[qq] : a.in_bytes, 0u, v[qq]);
+            const float w0 = m * st.cw[0], w1 = m * st.cw[1], w2 = m * st.cw[2], w3 = m * st.cw[3];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                acc[0][e] += w0 * v[0][e] + w1 * v[1][e] + w2 * v[2][e] + w3 * v[3][e];
+        }
+    } else if (a.K == 9) {
         // 3x3 kernel: a group's 27 offsets and scalars in seven 16-byte loads (the
         // 28th float is the next record's, or outside the buffer: zero), one group
         // at a time; each group's sum still runs over the taps in order
