@@ -284,8 +284,10 @@ struct DcnRec {
     float ly, lx;       // fractions over the low corner
     int32_t y0, x0;     // low corner (meaningful when inside)
     uint32_t flags;     // bit 0 inside; bit 1 + q: corner q in the image; bit 5 + q: in this
-                        // tile; bit 9 + q: far (no tile's ring reaches it; home samples only)
+                        // tile; bit 9 + q: far (no tile's ring reaches it; home samples only);
+                        // kRecHome: a home sample to take (records shared within a quad)
 };
+constexpr uint32_t kRecHome = 1u << 31;
 
 // Output indices o in [0, O) whose grid coordinate o*S - P + off lies in [lo, hi].
 __device__ __forceinline__ void out_range(int lo, int hi, int S, int P, int off, int O, int& o_lo,
@@ -358,14 +360,19 @@ __device__ __forceinline__ DcnRec dcn_record(const DcnArgs& a, const TileCtx& t,
     return r;
 }
 
-// grad_out[i .. i + VEC): GOV -- 16-byte aligned rows and VEC a multiple of 4 --
-// takes 8- or 16-byte vector loads of any grad_out type (the type test is
-// wave-uniform); otherwise element loads of the run-time type go_dtype.
-template <int VEC, bool GOV>
+// How the backward kernels read grad_out: element loads of the run-time type
+// go_dtype, or (16-byte aligned rows, VEC a multiple of 4) vector loads of a width
+// fixed at compile time -- binary32, or 16-bit (bfloat16 or binary16 by a
+// wave-uniform test after the load) -- so that the binary32 loads of a sample issue
+// with its corner loads, no branch on the type between them.
+constexpr int kGoElem = 0, kGoVecF32 = 1, kGoVec16 = 2;
+
+// grad_out[i .. i + VEC) in binary32
+template <int VEC, int GOV>
 __device__ __forceinline__ void load_go(const DcnArgs& a, uint32_t i, float (&go)[VEC]) {
-    if constexpr (GOV) {
+    if constexpr (GOV != kGoElem) {
         static_assert(VEC % 4 == 0, "vector grad_out loads cover 4 channels or more");
-        if (a.go_dtype == kF32) {
+        if constexpr (GOV == kGoVecF32) {
             const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.grad_out) + i);
 #pragma unroll
             for (int h = 0; h < VEC / 4; ++h) {
@@ -654,8 +661,9 @@ struct TileShape<1> {
     __device__ explicit TileShape(const DcnArgs&) {}
 };
 
-template <typename T, int VEC, int NVL, bool GOV, int FIXED>
-__global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a) {
+template <typename T, int VEC, int NVL, int GOV, int FIXED>
+__global__ void __launch_bounds__(kDcnTileThreads) __attribute__((amdgpu_waves_per_eu(6)))
+dcn_bwd_tile_kernel(DcnArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const TileShape<FIXED> sh(a);
     const int TY = sh.TY, TX = sh.TX;
@@ -680,8 +688,23 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     t.Iy1 = min(t.Iy0 + TY, a.H);
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
+    // (fixed shape) each tap's home range: h0, w0, nw, nh, oy, ox, 1 / nw
+    int* taps = reinterpret_cast<int*>(cnt + TY * TX * 4 + kDcnBwdWaves * kDcnListWords * kWave);
     for (int i = tid; i < TY * TX * sh.Dp; i += kDcnTileThreads) acc[i] = 0ull;
     for (int i = tid; i < TY * TX * 4; i += kDcnTileThreads) cnt[i] = 0u;
+    if (FIXED == 1 && tid < a.K) {
+        const int k = tid, ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+        int h0, h1, w0, w1;
+        out_range(t.Iy0 == 0 ? -(1 << 28) : t.Iy0, t.Iy1 == a.H ? (1 << 28) : t.Iy1 - 1, a.SH, a.PH,
+                  ki * a.DH, a.Ho, h0, h1);
+        out_range(t.Ix0 == 0 ? -(1 << 28) : t.Ix0, t.Ix1 == a.W ? (1 << 28) : t.Ix1 - 1, a.SW, a.PW,
+                  kj * a.DW, a.Wo, w0, w1);
+        const int nw = w1 - w0 + 1;
+        const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+        *reinterpret_cast<int4*>(taps + 8 * k) = int4{h0, w0, nw, nh};
+        *reinterpret_cast<int4*>(taps + 8 * k + 4) =
+            int4{ki * a.DH - a.PH, kj * a.DW - a.PW, __float_as_int(nw > 0 ? 1.0f / (float)nw : 0.0f), 0};
+    }
     __syncthreads();
 
     const int jj = tid & (sh.Lg - 1), slot = tid >> sh.log2Lg, spp = kDcnTileThreads >> sh.log2Lg;
@@ -735,78 +758,150 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
     };
 
     // ---- home samples: offset / scalar gradients, corners in this tile ----
-    for (int k = 0; k < a.K; ++k) {
-        const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
-        const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
-        int h0, h1, w0, w1;
-        out_range(t.Iy0 == 0 ? -(1 << 28) : t.Iy0, t.Iy1 == a.H ? (1 << 28) : t.Iy1 - 1, a.SH, a.PH,
-                  ki * a.DH, a.Ho, h0, h1);
-        out_range(t.Ix0 == 0 ? -(1 << 28) : t.Ix0, t.Ix1 == a.W ? (1 << 28) : t.Ix1 - 1, a.SW, a.PW,
-                  kj * a.DW, a.Wo, w0, w1);
-        const int nw = w1 - w0 + 1;
-        const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
-        const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
-        for (int idx = slot; idx < nh; idx += spp) {
-            int oh, ow;
-            divmod_small(idx, nw, inv_nw, oh, ow);
-            const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
-            const DcnRec R = dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox,
-                                        load_om(a, pix, t.g, k), true, TY, TX, sh.M);
-            if (jj == 0 && (R.flags >> 9)) {          // far corners (rare): listed
-                const uint32_t sid = ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
-                                         (uint32_t)a.K + (uint32_t)k;
+    // One home sample R of tap k: the group's loads, its offset and scalar
+    // gradients, and its corners in this tile.
+    auto home_sample = [&](const DcnRec& R, int k) {
+        if (jj == 0 && (R.flags >> 9 & 0xfu)) {       // far corners (rare): listed
+            const uint32_t sid = ((uint32_t)R.pix * (uint32_t)a.G + (uint32_t)t.g) *
+                                     (uint32_t)a.K + (uint32_t)k;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (R.flags >> (9 + q) & 1u) a.fb[atomicAdd(a.ctrl + kDcnCtrlFar, 1u)] = sid * 4u + q;
+            for (int q = 0; q < 4; ++q)
+                if (R.flags >> (9 + q) & 1u) a.fb[atomicAdd(a.ctrl + kDcnCtrlFar, 1u)] = sid * 4u + q;
+        }
+        // byte offset of corner 0's group channels (modulo 2^32: a corner outside
+        // the image is never addressed, and the others come out in range)
+        const uint32_t ib0 =
+            (((uint32_t)(t.n * a.H + R.y0) * (uint32_t)a.W + (uint32_t)R.x0) * (uint32_t)a.C + gD) *
+            (uint32_t)kElem;
+        float go[NVL][VEC];
+        float v[NVL][4][VEC];
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            load_go<VEC, GOV>(a, (uint32_t)R.pix * (uint32_t)a.C + gD + cl[u], go[u]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // all ones when the corner is in the image and the vector exists
+                const uint32_t m = (0u - (R.flags >> (1 + q) & 1u)) & vvm[u];
+                const uint32_t off = ((ib0 + cq[q] + clb[u]) & m) | (a.in_bytes & ~m);
+                VecLoad<T, VEC>::run(r_in, off, 0u, v[u][q]);
             }
-            // byte offset of corner 0's group channels (modulo 2^32: a corner outside
-            // the image is never addressed, and the others come out in range)
-            const uint32_t ib0 =
-                (((uint32_t)(t.n * a.H + R.y0) * (uint32_t)a.W + (uint32_t)R.x0) * (uint32_t)a.C + gD) *
-                (uint32_t)kElem;
-            float go[NVL][VEC];
-            float v[NVL][4][VEC];
+        }
+        // S_q = sum over the group's channels of grad_out * corner q: the value,
+        // x- and y-derivative sums are fixed combinations of the four
+        float cw[4];
+        corner_weights(R, cw);
+        float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        double gd[NVL][VEC];
 #pragma unroll
-            for (int u = 0; u < NVL; ++u) {
-                load_go<VEC, GOV>(a, (uint32_t)pix * (uint32_t)a.C + gD + cl[u], go[u]);
+        for (int u = 0; u < NVL; ++u) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // all ones when the corner is in the image and the vector exists
-                    const uint32_t m = (0u - (R.flags >> (1 + q) & 1u)) & vvm[u];
-                    const uint32_t off = ((ib0 + cq[q] + clb[u]) & m) | (a.in_bytes & ~m);
-                    VecLoad<T, VEC>::run(r_in, off, 0u, v[u][q]);
+            for (int e = 0; e < VEC; ++e) {
+                const float g = vv[u] ? go[u][e] : 0.0f;
+                gd[u][e] = (double)g;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) S[q] += g * v[u][q][e];
+            }
+        }
+        group_sum4(S, sh.Lg);
+        if (last) {
+            const bool live = R.flags & 1u;
+            const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
+            const float px = hy * (S[1] - S[0]) + R.ly * (S[3] - S[2]);
+            const float py = hx * (S[2] - S[0]) + R.lx * (S[3] - S[1]);
+            const float pm = cw[0] * S[0] + cw[1] * S[1] + cw[2] * S[2] + cw[3] * S[3];
+            float* gom = a.grad_om + ((uint32_t)R.pix * (uint32_t)a.G + (uint32_t)t.g) *
+                                         (uint32_t)(3 * a.K);
+            gom[2 * k] = live ? R.m * px : 0.0f;
+            gom[2 * k + 1] = live ? R.m * py : 0.0f;
+            gom[2 * a.K + k] = live ? pm : 0.0f;
+        }
+        add_tile(R, cw, gd);
+    };
+    if constexpr (FIXED == 1) {
+        // A lane group is one quad.  Lane jj of a quad forms the record of tap
+        // k0 + jj at the quad's slot and puts it in the wave's list area (pixel,
+        // scalar, position, flags); the quad then takes the (up to) four samples one
+        // at a time, every lane reading the record back: each stencil is formed
+        // once instead of once per lane of its group.  The list area is written and
+        // read by this wave only (as in the ring pass below).
+        static_assert(TileShape<1>::Lg == 4, "lane groups of four lanes");
+        for (int k0 = 0; k0 < a.K; k0 += 4) {
+            const int kk = k0 + jj;
+            // the largest of the four taps' counts (every quad holds the same taps)
+            int nmax = kk < a.K ? taps[8 * kk + 3] : 0;
+            nmax = max(nmax, __builtin_amdgcn_update_dpp(0, nmax, 0xB1, 0xF, 0xF, false));
+            nmax = max(nmax, __builtin_amdgcn_update_dpp(0, nmax, 0x4E, 0xF, 0xF, false));
+            nmax = __builtin_amdgcn_readfirstlane(nmax);
+            for (int idx = slot; idx < nmax; idx += spp) {
+                uint32_t pix = 0u, flags = 0u;
+                float m = 0.0f, y = 0.0f, x = 0.0f;
+                if (kk < a.K) {
+                    const int4 tr = *reinterpret_cast<const int4*>(taps + 8 * kk);   // h0 w0 nw nh
+                    if (idx < tr.w) {
+                        const int4 to = *reinterpret_cast<const int4*>(taps + 8 * kk + 4);
+                        int oh, ow;
+                        divmod_small(idx, tr.z, __int_as_float(to.z), oh, ow);
+                        const int gy = (tr.x + oh) * a.SH + to.x, gx = (tr.y + ow) * a.SW + to.y;
+                        pix = (uint32_t)((t.n * a.Ho + tr.x + oh) * a.Wo + tr.y + ow);
+                        const DcnOm o = load_om(a, (int)pix, t.g, kk);
+                        const DcnRec R = dcn_record(a, t, (int)pix, gy, gx, o, true, TY, TX, sh.M);
+                        m = o.m;
+                        y = (float)gy + o.dy;
+                        x = (float)gx + o.dx;
+                        flags = R.flags | kRecHome;
+                    }
                 }
-            }
-            // S_q = sum over the group's channels of grad_out * corner q: the value,
-            // x- and y-derivative sums are fixed combinations of the four
-            float cw[4];
-            corner_weights(R, cw);
-            float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            double gd[NVL][VEC];
-#pragma unroll
-            for (int u = 0; u < NVL; ++u) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float g = vv[u] ? go[u][e] : 0.0f;
-                    gd[u][e] = (double)g;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) S[q] += g * v[u][q][e];
+                __builtin_amdgcn_wave_barrier();
+                wl[lane] = pix;
+                wl[kWave + lane] = __float_as_uint(m);
+                wl[2 * kWave + lane] = __float_as_uint(y);
+                wl[3 * kWave + lane] = __float_as_uint(x);
+                wl[4 * kWave + lane] = flags;
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+                for (int j = 0; j < 4; ++j) {
+                    if (k0 + j >= a.K) break;
+                    const int src = (lane & ~3) | j;
+                    DcnRec Q;
+                    Q.flags = wl[4 * kWave + src];
+                    if (Q.flags & kRecHome) {
+                        // corner 0 and fractions from the position, as the record has them
+                        const float qy = __uint_as_float(wl[2 * kWave + src]);
+                        const float qx = __uint_as_float(wl[3 * kWave + src]);
+                        const bool inside = Q.flags & 1u;
+                        const float yf = inside ? floorf(qy) : 0.0f, xf = inside ? floorf(qx) : 0.0f;
+                        Q.pix = (int)wl[src];
+                        Q.m = __uint_as_float(wl[kWave + src]);
+                        Q.ly = inside ? qy - yf : 0.0f;
+                        Q.lx = inside ? qx - xf : 0.0f;
+                        Q.y0 = (int)yf;
+                        Q.x0 = (int)xf;
+                        home_sample(Q, k0 + j);
+                    }
                 }
+                __builtin_amdgcn_wave_barrier();     // the list is rewritten next
             }
-            group_sum4(S, sh.Lg);
-            if (last) {
-                const bool live = R.flags & 1u;
-                const float hy = 1.0f - R.ly, hx = 1.0f - R.lx;
-                const float px = hy * (S[1] - S[0]) + R.ly * (S[3] - S[2]);
-                const float py = hx * (S[2] - S[0]) + R.lx * (S[3] - S[1]);
-                const float pm = cw[0] * S[0] + cw[1] * S[1] + cw[2] * S[2] + cw[3] * S[3];
-                float* gom = a.grad_om + ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
-                                             (uint32_t)(3 * a.K);
-                gom[2 * k] = live ? R.m * px : 0.0f;
-                gom[2 * k + 1] = live ? R.m * py : 0.0f;
-                gom[2 * a.K + k] = live ? pm : 0.0f;
+        }
+    } else {
+        for (int k = 0; k < a.K; ++k) {
+            const int ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
+            const int oy = ki * a.DH - a.PH, ox = kj * a.DW - a.PW;
+            int h0, h1, w0, w1;
+            out_range(t.Iy0 == 0 ? -(1 << 28) : t.Iy0, t.Iy1 == a.H ? (1 << 28) : t.Iy1 - 1, a.SH,
+                      a.PH, ki * a.DH, a.Ho, h0, h1);
+            out_range(t.Ix0 == 0 ? -(1 << 28) : t.Ix0, t.Ix1 == a.W ? (1 << 28) : t.Ix1 - 1, a.SW,
+                      a.PW, kj * a.DW, a.Wo, w0, w1);
+            const int nw = w1 - w0 + 1;
+            const int nh = (h1 >= h0 && nw > 0) ? (h1 - h0 + 1) * nw : 0;
+            const float inv_nw = nw > 0 ? 1.0f / (float)nw : 0.0f;
+            for (int idx = slot; idx < nh; idx += spp) {
+                int oh, ow;
+                divmod_small(idx, nw, inv_nw, oh, ow);
+                const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
+                home_sample(dcn_record(a, t, pix, (h0 + oh) * a.SH + oy, (w0 + ow) * a.SW + ox,
+                                       load_om(a, pix, t.g, k), true, TY, TX, sh.M),
+                            k);
             }
-            add_tile(R, cw, gd);
         }
     }
 
@@ -911,7 +1006,7 @@ __global__ void __launch_bounds__(kDcnTileThreads) dcn_bwd_tile_kernel(DcnArgs a
 
 // The far list: corner q of sample s gets cw_q * m * grad_out by atomics (after every
 // tile has been stored).  Lg lanes per entry, a grid-stride loop over the entries.
-template <typename T, int VEC, int NVL, bool GOV>
+template <typename T, int VEC, int NVL, int GOV>
 __global__ void __launch_bounds__(kDcnThreads) dcn_far_kernel(DcnArgs a) {
 #pragma clang fp contract(off)
     const uint32_t count = a.ctrl[kDcnCtrlFar];
@@ -972,14 +1067,15 @@ hipError_t dcn_fwd_dispatch_nv(const DcnArgs& a, int nv, hipStream_t st) {
     }
 }
 
-template <typename T, int VEC, int NVL, bool GOV>
+template <typename T, int VEC, int NVL, int GOV>
 hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
     const unsigned blocks = (unsigned)((int64_t)a.N * a.tiles_y * a.tiles_x * a.G);
     hipLaunchKernelGGL(dcn_bound_kernel, dim3(kBoundGrid), dim3(kBoundThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.TY == TileShape<1>::TY && a.TX == TileShape<1>::TX && a.Dp == TileShape<1>::Dp &&
-        a.bLg == TileShape<1>::Lg && a.blog2Lg == TileShape<1>::log2Lg && a.M == TileShape<1>::M)
+        a.bLg == TileShape<1>::Lg && a.blog2Lg == TileShape<1>::log2Lg && a.M == TileShape<1>::M &&
+        a.K <= kDcnShareTaps)
         hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV, 1>), dim3(blocks),
                            dim3(kDcnTileThreads), lds, st, a);
     else
@@ -1013,7 +1109,7 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
     auto by_nvl = [&](auto tv, auto vv, auto gv) -> hipError_t {
         using T = decltype(tv);
         constexpr int V = decltype(vv)::value;
-        constexpr bool G = decltype(gv)::value;
+        constexpr int G = decltype(gv)::value;
         switch (a.bNVL) {
             case 1: return dcn_bwd_launch<T, V, 1, G>(a, lds_bytes, stream);
             case 2:       // two vectors per lane only where a vector holds 4 channels or fewer
@@ -1023,12 +1119,16 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
         }
     };
     using I1 = std::integral_constant<int, 1>;
+    using GoE = std::integral_constant<int, kGoElem>;
+    using GoF = std::integral_constant<int, kGoVecF32>;
+    using GoH = std::integral_constant<int, kGoVec16>;
     return with_elem(in_dtype, [&](auto t) {
         using T = decltype(t);
         using V = std::integral_constant<int, sizeof(T) == 2 ? 8 : 4>;
-        if (vec == V::value && a.go_vec4) return by_nvl(t, V{}, std::true_type{});
-        if (vec == V::value) return by_nvl(t, V{}, std::false_type{});
-        return by_nvl(t, I1{}, std::false_type{});
+        if (vec == V::value && a.go_vec4)
+            return a.go_dtype == kF32 ? by_nvl(t, V{}, GoF{}) : by_nvl(t, V{}, GoH{});
+        if (vec == V::value) return by_nvl(t, V{}, GoE{});
+        return by_nvl(t, I1{}, GoE{});
     });
 }
 

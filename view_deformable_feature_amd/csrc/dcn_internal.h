@@ -64,9 +64,12 @@ hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t l
 constexpr int kDcnTileThreads = 512;   // backward tile kernel workgroup
 constexpr int kDcnBwdWaves = kDcnTileThreads / 64;
 constexpr int kDcnListWords = 5;
+// taps whose home ranges the fixed-shape tile kernel keeps in an LDS table (8 words
+// each); kernels with more taps take the general form
+constexpr int kDcnShareTaps = 16;
 inline size_t dcn_tile_lds_bytes(int ty, int tx, int dp) {
     return (size_t)ty * tx * dp * 8 + (size_t)ty * tx * 16 +
-           (size_t)kDcnBwdWaves * 64 * kDcnListWords * 4;
+           (size_t)kDcnBwdWaves * 64 * kDcnListWords * 4 + (size_t)kDcnShareTaps * 32;
 }
 
 }  // namespace da
