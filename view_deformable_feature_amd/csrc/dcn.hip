@@ -917,6 +917,32 @@ dcn_bwd_tile_kernel(DcnArgs a) {
     int n_list = 0;                                  // wave-uniform
     auto drain = [&]() {
         __builtin_amdgcn_wave_barrier();
+        // lane r forms the record of entry r in place (the test pass keeps only the
+        // pixel, the tap and the position): scalar, fractions, low corner relative
+        // to the tile and the in-tile corner bits -- an accepted sample lies inside
+        // the image, and every corner in the tile is in the image
+        if (lane < n_list) {
+            const uint32_t pix = wl[lane];
+            const int k = (int)wl[kWave + lane];
+            const float y = __uint_as_float(wl[2 * kWave + lane]);
+            const float x = __uint_as_float(wl[3 * kWave + lane]);
+            const float m = a.om[(pix * (uint32_t)a.G + (uint32_t)t.g) * (uint32_t)(3 * a.K) +
+                                 (uint32_t)(2 * a.K + k)];
+            const float yf = floorf(y), xf = floorf(x);
+            const int y0 = (int)yf, x0 = (int)xf;
+            uint32_t f = 1u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int cy = y0 + (q >> 1), cx = x0 + (q & 1);
+                const bool own = cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1;
+                f |= (own ? 1u : 0u) << (5 + q);
+            }
+            wl[kWave + lane] = __float_as_uint(m);
+            wl[2 * kWave + lane] = __float_as_uint(y - yf);
+            wl[3 * kWave + lane] = __float_as_uint(x - xf);
+            wl[4 * kWave + lane] = (uint32_t)(y0 - t.Iy0 + 1) | (uint32_t)(x0 - t.Ix0 + 1) << 8 | f << 16;
+        }
+        __builtin_amdgcn_wave_barrier();
         for (int r = grp; r < n_list; r += gpw) {
             DcnRec L;
             L.pix = (int)wl[r];
@@ -964,9 +990,21 @@ dcn_bwd_tile_kernel(DcnArgs a) {
             const int pix = (t.n * a.Ho + h0 + oh) * a.Wo + w0 + ow;
             const int cy = min(max(gy, 0), a.H - 1), cx = min(max(gx, 0), a.W - 1);
             const bool cand = idx < nh && !(cy >= t.Iy0 && cy < t.Iy1 && cx >= t.Ix0 && cx < t.Ix1);
-            const DcnOm o = cand ? load_om(a, pix, t.g, k) : DcnOm{0.0f, 0.0f, 0.0f};
-            const DcnRec R = dcn_record(a, t, pix, gy, gx, o, false, TY, TX, sh.M);
-            const bool take = cand && (R.flags >> 5) != 0u;
+            // A candidate has a corner in this tile exactly when it lies inside the
+            // image (as the record defines it) with its low corner in rows
+            // [Iy0 - 1, Iy1 - 1] and columns [Ix0 - 1, Ix1 - 1]: only the offsets
+            // are read here, the record is formed when the list is drained.
+            float y = 0.0f, x = 0.0f;
+            bool take = false;
+            if (cand) {
+                const float* om = a.om + ((uint32_t)pix * (uint32_t)a.G + (uint32_t)t.g) *
+                                             (uint32_t)(3 * a.K);
+                y = (float)gy + om[2 * k + 1];
+                x = (float)gx + om[2 * k];
+                take = y > -1.0f && x > -1.0f && y < (float)a.H && x < (float)a.W &&
+                       y >= (float)(t.Iy0 - 1) && y < (float)t.Iy1 && x >= (float)(t.Ix0 - 1) &&
+                       x < (float)t.Ix1;
+            }
             const unsigned long long mask = __ballot(take);
             const int n_take = __popcll(mask);
             if (n_list + n_take > kWave) drain();
@@ -974,13 +1012,9 @@ dcn_bwd_tile_kernel(DcnArgs a) {
                 const int r = n_list + (int)__builtin_amdgcn_mbcnt_hi(
                     (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
                 wl[r] = (uint32_t)pix;
-                wl[kWave + r] = __float_as_uint(R.m);
-                wl[2 * kWave + r] = __float_as_uint(R.ly);
-                wl[3 * kWave + r] = __float_as_uint(R.lx);
-                // low corner relative to the tile (in [-1, TY] x [-1, TX] for an
-                // accepted sample), the inside bit and the in-tile corner bits
-                wl[4 * kWave + r] = (uint32_t)(R.y0 - t.Iy0 + 1) | (uint32_t)(R.x0 - t.Ix0 + 1) << 8 |
-                                    (R.flags & 0x1e1u) << 16;
+                wl[kWave + r] = (uint32_t)k;
+                wl[2 * kWave + r] = __float_as_uint(y);
+                wl[3 * kWave + r] = __float_as_uint(x);
             }
             n_list += n_take;
         }
