@@ -640,9 +640,8 @@ __device__ __forceinline__ void group_sum4(float (&v)[4], int n) {
 // Tile sums: a term t is added as the binary64 encoding of RNE(t 2^E) + 1.5 * 2^52,
 // an integer in [2^52, 2^53) whose encoding is kFixMagicBits + RNE(t 2^E), and each
 // tile pixel counts the terms it takes (the same count for every channel of the
-// group; each lane of the group adds 1 to its own of the pixel's four counters, so
-// their sum is bLg times that).  The store subtracts count * kFixMagicBits modulo
-// 2^64, which leaves the exact sum of the rounded terms.
+// group: the group's first lane adds 1 per term).  The store subtracts
+// count * kFixMagicBits modulo 2^64, which leaves the exact sum of the rounded terms.
 constexpr unsigned long long kFixMagicBits = 0x4338000000000000ull;   // encoding of 1.5 * 2^52
 
 // Tile shape and lane layout of the tile kernel: from the arguments, or (FIXED = 1)
@@ -668,9 +667,9 @@ dcn_bwd_tile_kernel(DcnArgs a) {
     const TileShape<FIXED> sh(a);
     const int TY = sh.TY, TX = sh.TX;
     unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);    // [TY*TX][Dp]
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * sh.Dp);        // [TY*TX][4]
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(acc + TY * TX * sh.Dp);        // [TY*TX]
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    uint32_t* wl = cnt + TY * TX * 4 + wave * (kDcnListWords * kWave);
+    uint32_t* wl = cnt + TY * TX + wave * (kDcnListWords * kWave);
     const int E = dcn_fixed_exponent(a);
     const double scale = ldexp(1.0, E);
 
@@ -689,9 +688,9 @@ dcn_bwd_tile_kernel(DcnArgs a) {
     t.Ix1 = min(t.Ix0 + TX, a.W);
 
     // (fixed shape) each tap's home range: h0, w0, nw, nh, oy, ox, 1 / nw
-    int* taps = reinterpret_cast<int*>(cnt + TY * TX * 4 + kDcnBwdWaves * kDcnListWords * kWave);
+    int* taps = reinterpret_cast<int*>(cnt + TY * TX + kDcnBwdWaves * kDcnListWords * kWave);
     for (int i = tid; i < TY * TX * sh.Dp; i += kDcnTileThreads) acc[i] = 0ull;
-    for (int i = tid; i < TY * TX * 4; i += kDcnTileThreads) cnt[i] = 0u;
+    for (int i = tid; i < TY * TX; i += kDcnTileThreads) cnt[i] = 0u;
     if (FIXED == 1 && tid < a.K) {
         const int k = tid, ki = k / a.KW, kj = k - (k / a.KW) * a.KW;
         int h0, h1, w0, w1;
@@ -713,7 +712,7 @@ dcn_bwd_tile_kernel(DcnArgs a) {
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
         const int vi = jj + sh.Lg * u;
-        vv[u] = vi < a.Dv;
+        vv[u] = FIXED == 1 || vi < a.Dv;   // (the fixed shape's vectors fill the group)
         cl[u] = vv[u] ? vi * VEC : 0;
     }
     const uint32_t gD = (uint32_t)(t.g * a.D);
@@ -741,9 +740,7 @@ dcn_bwd_tile_kernel(DcnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (!(R.flags >> (5 + q) & 1u)) continue;
-            // once per lane of the group (bLg per term), each lane on its own of the
-            // pixel's 4 counters so that no two lanes of a group add to one address
-            atomicAdd(&cnt[(pb + dpq[q]) * 4 + (jj & 3)], 1u);
+            if (jj == 0) atomicAdd(&cnt[pb + dpq[q]], 1u);   // once per term
             const double ws = (double)(cw[q] * R.m) * scale;
             unsigned long long* row = acc + (rb + dpr[q]);
 #pragma unroll
@@ -1031,8 +1028,7 @@ dcn_bwd_tile_kernel(DcnArgs a) {
         const int tp = py * TX + px;
         const long long code =
             (long long)(acc[tp * sh.Dp + c] -
-                        (unsigned long long)((cnt[4 * tp] + cnt[4 * tp + 1] + cnt[4 * tp + 2] +
-                                              cnt[4 * tp + 3]) >> sh.log2Lg) * kFixMagicBits);
+                        (unsigned long long)cnt[tp] * kFixMagicBits);
         a.grad_input[(((int64_t)t.n * a.H + t.Iy0 + py) * a.W + t.Ix0 + px) * a.C + gD + c] =
             (float)((double)code * inv);
     }
@@ -1109,7 +1105,7 @@ hipError_t dcn_bwd_launch(const DcnArgs& a, size_t lds, hipStream_t st) {
     if (e != hipSuccess) return e;
     if (a.TY == TileShape<1>::TY && a.TX == TileShape<1>::TX && a.Dp == TileShape<1>::Dp &&
         a.bLg == TileShape<1>::Lg && a.blog2Lg == TileShape<1>::log2Lg && a.M == TileShape<1>::M &&
-        a.K <= kDcnShareTaps)
+        a.K <= kDcnShareTaps && a.Dv == TileShape<1>::Lg * NVL)
         hipLaunchKernelGGL((dcn_bwd_tile_kernel<T, VEC, NVL, GOV, 1>), dim3(blocks),
                            dim3(kDcnTileThreads), lds, st, a);
     else

@@ -68,7 +68,7 @@ constexpr int kDcnListWords = 5;
 // each); kernels with more taps take the general form
 constexpr int kDcnShareTaps = 16;
 inline size_t dcn_tile_lds_bytes(int ty, int tx, int dp) {
-    return (size_t)ty * tx * dp * 8 + (size_t)ty * tx * 16 +
+    return (size_t)ty * tx * dp * 8 + (size_t)ty * tx * 4 +
            (size_t)kDcnBwdWaves * 64 * kDcnListWords * 4 + (size_t)kDcnShareTaps * 32;
 }
 
