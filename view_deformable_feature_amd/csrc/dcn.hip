@@ -433,11 +433,9 @@ __device__ __forceinline__ void corner_weights(const DcnRec& r, float (&cw)[4]) 
 constexpr int kBoundThreads = 1024;
 constexpr int kBoundWaves = kBoundThreads / kWave;
 constexpr int kBoundGrid = 256;
-static_assert(kBoundGrid <= kDcnBoundBlocks, "partials fit the workspace");
 
 __global__ void __launch_bounds__(kBoundThreads) dcn_bound_kernel(DcnArgs a) {
     __shared__ uint32_t red[2][kBoundWaves];
-    __shared__ uint32_t is_last;
     constexpr int U = 4;                    // loads in flight per thread
     // element counts are below 2^30 (every tensor is under 4 GiB)
     const uint32_t stride = gridDim.x * kBoundThreads;
@@ -541,42 +539,16 @@ __global__ void __launch_bounds__(kBoundThreads) dcn_bound_kernel(DcnArgs a) {
         red[1][threadIdx.x / kWave] = mm;
     }
     __syncthreads();
+    // the block's maxima into the (zeroed) control words: device-scope atomics, no
+    // fence (the tile kernel reads them after this kernel ends); a maximum over
+    // binary32 magnitudes is the maximum over their bit patterns
     if (threadIdx.x == 0) {
         for (int w = 1; w < kBoundWaves; ++w) {
             mg = max(mg, red[0][w]);
             mm = max(mm, red[1][w]);
         }
-        a.part[2 * blockIdx.x] = mg;
-        a.part[2 * blockIdx.x + 1] = mm;
-        __threadfence();
-        is_last = atomicAdd(a.ctrl + kDcnCtrlTicket, 1u) == gridDim.x - 1 ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    mg = 0;
-    mm = 0;
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBoundThreads) {
-        mg = max(mg, a.part[2 * b]);
-        mm = max(mm, a.part[2 * b + 1]);
-    }
-    for (int d = 1; d < kWave; d <<= 1) {
-        mg = max(mg, (uint32_t)__shfl_xor((int)mg, d, kWave));
-        mm = max(mm, (uint32_t)__shfl_xor((int)mm, d, kWave));
-    }
-    __syncthreads();
-    if (threadIdx.x % kWave == 0) {
-        red[0][threadIdx.x / kWave] = mg;
-        red[1][threadIdx.x / kWave] = mm;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < kBoundWaves; ++w) {
-            mg = max(mg, red[0][w]);
-            mm = max(mm, red[1][w]);
-        }
-        a.ctrl[kDcnCtrlMaxGo] = mg;
-        a.ctrl[kDcnCtrlMaxM] = mm;
+        atomicMax(a.ctrl + kDcnCtrlMaxGo, mg);
+        atomicMax(a.ctrl + kDcnCtrlMaxM, mm);
     }
 }
 

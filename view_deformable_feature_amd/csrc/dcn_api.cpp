@@ -41,10 +41,8 @@ struct DcnPlan {
 constexpr int kDcnMargin = 4;                 // offsets up to 4 px reach a tile through its ring
 constexpr size_t kDcnTileLds = 48 * 1024;     // LDS for one tile's gradient sums
 
-// Workspace: control words, the bound kernel's block maxima, then the far list
-// (one 32-bit entry per (sample, corner)).
-constexpr uint64_t kDcnPartOffset = 256;
-constexpr uint64_t kDcnFarOffset = kDcnPartOffset + 8 * da::kDcnBoundBlocks;
+// Workspace: control words, then the far list (one 32-bit entry per (sample, corner)).
+constexpr uint64_t kDcnFarOffset = 256;
 uint64_t dcn_workspace_bytes(int64_t n_samples) {
     return n_samples == 0 ? 0 : kDcnFarOffset + (uint64_t)n_samples * 16;
 }
@@ -256,7 +254,6 @@ da_status dcn_backward(const dcn_problem* p, const void* input, const float* off
                                 workspace_bytes, (unsigned long long)need);
         unsigned char* base = static_cast<unsigned char*>(workspace);
         a.ctrl = reinterpret_cast<uint32_t*>(base);
-        a.part = reinterpret_cast<uint32_t*>(base + kDcnPartOffset);
         a.fb = reinterpret_cast<uint32_t*>(base + kDcnFarOffset);
     }
     return da::report_hip(da::launch_dcn_backward(a, p->in_dtype, plan.vec, plan.lds_bytes,

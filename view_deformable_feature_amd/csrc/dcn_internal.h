@@ -39,7 +39,6 @@ struct DcnArgs {
     int32_t TY, TX, M, tiles_y, tiles_x, Dp;
     int32_t bLg, blog2Lg, bNVL;   // backward lanes: bLg lanes per sample, bNVL vectors per lane
     uint32_t* ctrl;          // workspace control words (zeroed first): kDcnCtrl*
-    uint32_t* part;          // workspace: [kDcnBoundBlocks][2] block maxima
     uint32_t* fb;            // workspace: [4 * N * Ho * Wo * G * K]
     int32_t log2_terms;      // ceil(log2(most terms one tile sum can take))
 };
@@ -48,8 +47,6 @@ struct DcnArgs {
 constexpr int kDcnCtrlFar = 0;      // entries in fb
 constexpr int kDcnCtrlMaxGo = 1;    // max |grad_out| (binary32 bits)
 constexpr int kDcnCtrlMaxM = 2;     // max |m|
-constexpr int kDcnCtrlTicket = 3;   // bound blocks done
-constexpr int kDcnBoundBlocks = 1024;
 
 // vec: channels per lane vector (1, 4 or 8); nv: groups per lane (1, 2, 4 or 8)
 hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, hipStream_t stream);
