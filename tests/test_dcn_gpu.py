@@ -37,11 +37,20 @@ CASES = {
     "k5_d2": dict(N=1, H=29, W=35, C=32, groups=2, kernel=(5, 5), pad=(4, 4), dilation=(2, 2)),
     # offsets of sigma 15 px: most corners leave the image or go to the far list
     "far_all": dict(N=1, H=40, W=40, C=16, groups=2, offset_sigma=15.0),
+    # 32 channels per group (the fixed tile shape): 12 taps (three groups of four
+    # taps per shared record pass), 25 taps (more than the shared form takes: the
+    # general tap loop at the fixed shape), and stride 2 across several tiles
+    "k34_d32": dict(N=1, H=19, W=23, C=64, groups=2, kernel=(3, 4), pad=(1, 2), seed=3100),
+    "k55_d32": dict(N=1, H=17, W=21, C=32, groups=1, kernel=(5, 5), pad=(2, 2), seed=3101),
+    "s2_d32": dict(N=2, H=20, W=34, C=128, groups=4, stride=(2, 2), seed=3102),
 }
+_SEEDED = [n for n in sorted(CASES) if "seed" not in CASES[n]]
 
 
 def _wl(name, **over):
-    kw = dict(CASES[name], seed=3000 + sorted(CASES).index(name))
+    kw = dict(CASES[name])
+    if "seed" not in kw:
+        kw["seed"] = 3000 + _SEEDED.index(name)
     kw.update(over)
     return W.dcn_custom(name, **kw)
 
@@ -87,7 +96,7 @@ def test_dcn_full(name):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("name", ["tiny", "c96_g3", "c512_g16", "k35_dil"])
+@pytest.mark.parametrize("name", ["tiny", "c96_g3", "c512_g16", "k35_dil", "k34_d32"])
 def test_dcn_16bit_input(name, dtype):
     _check(_wl(name, dtype=dtype))
 
