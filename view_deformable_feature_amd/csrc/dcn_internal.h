@@ -56,8 +56,9 @@ hipError_t launch_dcn_forward(const DcnArgs& a, int in_dtype, int vec, int nv, h
 hipError_t launch_dcn_backward(const DcnArgs& a, int in_dtype, int vec, size_t lds_bytes,
                                hipStream_t stream);
 // Dynamic LDS of the backward tile kernel: the [TY*TX][Dp] 64-bit sums, the number of
-// terms each tile pixel took (four 32-bit counters per pixel), and per wave a list of
-// up to 64 accepted ring candidates (kDcnListWords words each).
+// terms each tile pixel took (one 32-bit counter per pixel), per wave a list of up to
+// 64 records (kDcnListWords words each: the shared home records, then the accepted
+// ring candidates), and the fixed shape's tap table.
 constexpr int kDcnTileThreads = 512;   // backward tile kernel workgroup
 constexpr int kDcnBwdWaves = kDcnTileThreads / 64;
 constexpr int kDcnListWords = 5;
