@@ -210,6 +210,34 @@ def test_dcn_grad_input_repeatable_without_far_corners():
     assert_close("repeatable grad_input", runs[0].numpy(), r_gi, TOL_BWD)
 
 
+@pytest.mark.parametrize("C, G", [(64, 2), (64, 4)], ids=["d32_fixed_tiles", "d16_general"])
+def test_dcn_offsets_at_the_ring_margin(C, G):
+    """Offsets at and around the 4-pixel ring margin of the tile backward (and whole
+    pixels, where a corner falls exactly on a tile edge): a sample with
+    |offset| <= 4 reaches every tile that owns one of its corners through that
+    tile's ring, a larger one lists its far corners.  Every element against the
+    oracle, across ragged 8 x 16 tiles."""
+    import view_deformable_feature_amd as vdf
+    wl = W.dcn_custom("margin", N=1, H=24, W=40, C=C, groups=G, seed=3200)
+    inp = W.make_dcn_inputs(wl)
+    om = inp["offset_mask"].copy()
+    K = wl.K
+    vals = np.array([-5.0, -4.5, -4.0001, -4.0, -3.9999, -1.0, -0.5, 0.0, 0.5, 1.0,
+                     3.9999, 4.0, 4.0001, 4.5, 5.0], dtype=np.float32)
+    rng = np.random.default_rng(3201)
+    om[..., :2 * K] = rng.choice(vals, size=om[..., :2 * K].shape)
+    x, omt = _dev(dict(inp, offset_mask=om))
+    go = torch.from_numpy(inp["grad_out"]).cuda()
+    out = vdf.dcn_forward(x, omt, **_conf(wl))
+    gi, gom = vdf.dcn_backward(x, omt, go, **_conf(wl))
+    torch.cuda.synchronize()
+    ref = oracle.dcn_forward(inp["input"], om, **_conf(wl))
+    r_gi, r_gom = oracle.dcn_backward(inp["input"], om, inp["grad_out"], **_conf(wl))
+    assert_close("margin out", out.cpu().numpy(), ref, TOL_FWD)
+    assert_close("margin grad_input", gi.cpu().numpy(), r_gi, TOL_BWD)
+    assert_close("margin grad_offset_mask", gom.cpu().numpy(), r_gom, TOL_BWD)
+
+
 def test_dcn_unaligned_views():
     """input, offset_mask and grad_out as views one element into larger buffers: one
     channel per lane vector, the bound kernel's element-wise scans and element-wise
