@@ -60,7 +60,8 @@ constexpr int kGatherThreads = 256;
 // the next long row starts at least kSlotStride entries later.
 constexpr int kSlotStride = kGatherLong + 1;
 // Words of the control block at the start of the backward workspace.
-constexpr int kCtrlScanDone = 0;   // (unused: the scan's tile totals are added by a second launch)
+constexpr int kCtrlScanDone = 0;   // (reserved: the bucket kernel, or above 256 tiles a second
+                                   // launch, adds the scan's tile totals; no completion count)
 constexpr int kCtrlMaxGo = 1;      // max |grad_out| (float bits)
 constexpr int kCtrlMaxW = 2;       // max |weight| (float bits)
 constexpr int kCtrlMaxCnt = 3;     // max entries of one row
