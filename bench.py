@@ -11,7 +11,9 @@ forward + backward (bs*A*P*K*S*C per step / step time); the step time is the
 wall time of K replays of one HIP graph holding a captured step (the library
 launches kernels only, so the graph replays exactly the calls' kernels), between
 device synchronisations; --launch eager times K eager steps instead, and
-eager_ms_per_step always reports that figure.
+eager_ms_per_step always reports that figure.  forward / backward avg_us are
+eager calls (HIP events on the call's stream); their graph_us (graph launch only)
+is the same call's time with eight calls back to back in one captured graph.
 
 The roofline entries divide the compulsory bytes of each direction (every input
 tensor read once, every output tensor written once) by the HIP-event time of
@@ -380,6 +382,35 @@ def graph_step_seconds(step, warmup, steps):
     return t
 
 
+def graph_call_seconds(fn, calls, replays):
+    """Time per call of `calls` back-to-back calls of fn captured in one HIP graph
+    and replayed `replays` times (HIP events on the replaying stream): the calls'
+    kernels alone, without the host's launch gaps of eager calls."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (calls * replays)
+    del graph
+    return t
+
+
 def bench_dcn(args):
     """Deformable convolution (DCNv3 / DCNv4 operator): forward + backward on the
     shape the DCNv4 notes time (56x56x128, batch 64, 4 groups by default)."""
@@ -474,6 +505,14 @@ def bench_dcn(args):
                                                  "dcn_far_kernel"),
            "roofline_forward": roof(b_fwd, e_fwd, t_fwd, "dcn_forward_kernel"),
            "vector_memory_reference": vref}
+    if args.launch == "graph":
+        # the same calls' kernels back to back in one captured graph
+        reps = max(2, args.steps // 8)
+        rec["forward"]["graph_us"] = graph_call_seconds(
+            lambda: vdf.dcn_forward(x, om, **conf, out=out), 8, reps) * 1e6
+        rec["backward"]["graph_us"] = graph_call_seconds(
+            lambda: vdf.dcn_backward(x, om, go, **conf, grad_input=gi, grad_offset_mask=gom,
+                                     workspace=ws), 8, reps) * 1e6
     cref = copy_reference()
     rec["copy_reference"] = cref
     for key in ("roofline", "roofline_forward"):
@@ -686,6 +725,12 @@ def main():
     }
     rec["forward"]["median_us"] = float(np.median(t_fwd)) * 1e6
     rec["backward"]["median_us"] = float(np.median(t_bwd)) * 1e6
+    if args.launch == "graph":
+        # the same calls' kernels back to back in one captured graph
+        reps = max(2, args.steps // 8)
+        rec["forward"]["graph_us"] = graph_call_seconds(
+            lambda: vdf.da_forward(feat, shape, start, loc, w, out=out, workspace=fws), 8, reps) * 1e6
+        rec["backward"]["graph_us"] = graph_call_seconds(backward, 8, reps) * 1e6
     if args.cold:
         # a 512 MiB write between calls evicts the inputs from L2 and the MALL
         flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
