@@ -43,6 +43,9 @@ CASES = {
     "k34_d32": dict(N=1, H=19, W=23, C=64, groups=2, kernel=(3, 4), pad=(1, 2), seed=3100),
     "k55_d32": dict(N=1, H=17, W=21, C=32, groups=1, kernel=(5, 5), pad=(2, 2), seed=3101),
     "s2_d32": dict(N=2, H=20, W=34, C=128, groups=4, stride=(2, 2), seed=3102),
+    # fewer taps than the lanes of a group (one and three: lanes without a tap)
+    "k1_d32": dict(N=1, H=13, W=30, C=64, groups=2, kernel=(1, 1), pad=(0, 0), seed=3103),
+    "k13_d32": dict(N=1, H=11, W=21, C=32, groups=1, kernel=(1, 3), pad=(0, 1), seed=3104),
 }
 _SEEDED = [n for n in sorted(CASES) if "seed" not in CASES[n]]
 
